@@ -1,0 +1,191 @@
+"""Python binding of libgemm_a8w8.so, the a8w8 block-scale GEMM for MI355X (gfx950).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels of
+the library.  torch supplies device memory and the stream.  The names mirror
+the C ABI in ``include/gemm_a8w8_blockscale.h``.
+
+    Y[m,n] = bf16( sum_kb (A_fp8 . W_fp8^T)_kb * a_scale[m,kb] * w_scale[n//128,kb] )
+
+A ``float8_e4m3fn`` (or uint8 bytes) [M,K]; a_scale float32 [M,K/128];
+W ``float8_e4m3fn`` (or uint8) [N,K]; w_scale float32 [ceil(N/128),K/128];
+Y bfloat16 [M,N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemm_a8w8.so")
+
+A8W8_OK = 0
+A8W8_ERR_NULL = 1
+A8W8_ERR_SHAPE = 2
+A8W8_ERR_ALIGN = 3
+A8W8_ERR_ARCH = 4
+A8W8_ERR_HIP = 5
+A8W8_ERR_PLAN = 6
+KERNEL_NAMES = {1: "skinny", 2: "tile"}
+
+EXPORTED = (
+    "gemm_a8w8_blockscale",
+    "gemm_a8w8_blockscale_plan",
+    "gemm_a8w8_num_variants",
+    "gemm_a8w8_describe_variant",
+    "gemm_a8w8_blockscale_run_variant",
+    "gemm_a8w8_variant_name",
+    "gemm_a8w8_status_string",
+    "gemm_a8w8_table_hash",
+)
+
+
+class A8W8Error(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {gemm_a8w8_status_string(status)} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("key_m", ctypes.c_int64),
+                ("fallback", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
+        return d
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it was not built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m fp8_block_scaled_a8w8_amd.build or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.gemm_a8w8_blockscale.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale.argtypes = [vp] * 5 + [i64] * 3 + [vp]
+        L.gemm_a8w8_blockscale_plan.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        L.gemm_a8w8_num_variants.restype = ctypes.c_int
+        L.gemm_a8w8_num_variants.argtypes = []
+        L.gemm_a8w8_describe_variant.restype = ctypes.c_int
+        L.gemm_a8w8_describe_variant.argtypes = [i32, i64, i64, i64, ctypes.POINTER(Plan)]
+        L.gemm_a8w8_blockscale_run_variant.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_run_variant.argtypes = [i32] + [vp] * 5 + [i64] * 3 + [vp]
+        L.gemm_a8w8_variant_name.restype = ctypes.c_char_p
+        L.gemm_a8w8_variant_name.argtypes = [i32]
+        L.gemm_a8w8_status_string.restype = ctypes.c_char_p
+        L.gemm_a8w8_status_string.argtypes = [ctypes.c_int]
+        L.gemm_a8w8_table_hash.restype = ctypes.c_uint64
+        L.gemm_a8w8_table_hash.argtypes = []
+        _lib = L
+    return _lib
+
+
+def gemm_a8w8_status_string(status: int) -> str:
+    return lib().gemm_a8w8_status_string(int(status)).decode()
+
+
+def gemm_a8w8_variant_name(variant: int) -> str | None:
+    r = lib().gemm_a8w8_variant_name(int(variant))
+    return r.decode() if r is not None else None
+
+
+def gemm_a8w8_table_hash() -> int:
+    return int(lib().gemm_a8w8_table_hash())
+
+
+def gemm_a8w8_num_variants() -> int:
+    return int(lib().gemm_a8w8_num_variants())
+
+
+def gemm_a8w8_blockscale_plan(M: int, N: int, K: int, cu_count: int = 0) -> dict:
+    p = Plan()
+    rc = lib().gemm_a8w8_blockscale_plan(M, N, K, cu_count, ctypes.byref(p))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_blockscale_plan")
+    d = p.as_dict()
+    d["name"] = gemm_a8w8_variant_name(d["variant"])
+    return d
+
+
+def gemm_a8w8_describe_variant(variant: int, M: int = 0, N: int = 1, K: int = 128) -> dict:
+    p = Plan()
+    rc = lib().gemm_a8w8_describe_variant(variant, M, N, K, ctypes.byref(p))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_describe_variant")
+    d = p.as_dict()
+    d["name"] = gemm_a8w8_variant_name(variant)
+    return d
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(A, a_scale, W, w_scale, out):
+    if A.dtype not in (torch.float8_e4m3fn, torch.uint8) or W.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError("A and W must be float8_e4m3fn (or raw uint8 bytes)")
+    if a_scale.dtype != torch.float32 or w_scale.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    if A.dim() != 2 or W.dim() != 2:
+        raise ValueError("A and W must be 2-D")
+    M, K = A.shape
+    N, K2 = W.shape
+    if K2 != K:
+        raise ValueError(f"A is [M,{K}] but W is [N,{K2}]")
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    KB, NB = K // 128, (N + 127) // 128
+    if tuple(a_scale.shape) != (M, KB) or tuple(w_scale.shape) != (NB, KB):
+        raise ValueError(f"scale shapes must be [{M},{KB}] and [{NB},{KB}], got "
+                         f"{tuple(a_scale.shape)} and {tuple(w_scale.shape)}")
+    for name, t in (("A", A), ("a_scale", a_scale), ("W", W), ("w_scale", w_scale)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [M,N] tensor")
+    return M, N, K, out
+
+
+def gemm_a8w8_blockscale(A: torch.Tensor, a_scale: torch.Tensor, W: torch.Tensor,
+                         w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """Y = A . W^T with 1x128 activation / 128x128 weight fp32 block scales; returns bf16 [M,N]."""
+    M, N, K, out = _check(A, a_scale, W, w_scale, out)
+    rc = lib().gemm_a8w8_blockscale(A.data_ptr(), a_scale.data_ptr(), W.data_ptr(),
+                                    w_scale.data_ptr(), out.data_ptr(), M, N, K,
+                                    _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_blockscale")
+    return out
+
+
+def gemm_a8w8_blockscale_run_variant(variant: int, A, a_scale, W, w_scale, out=None, stream=None):
+    """Same as gemm_a8w8_blockscale with a fixed kernel instance (tuning and tests)."""
+    M, N, K, out = _check(A, a_scale, W, w_scale, out)
+    rc = lib().gemm_a8w8_blockscale_run_variant(variant, A.data_ptr(), a_scale.data_ptr(),
+                                                W.data_ptr(), w_scale.data_ptr(), out.data_ptr(),
+                                                M, N, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, f"gemm_a8w8_blockscale_run_variant({variant})")
+    return out
+
+
+def variants() -> list[dict]:
+    """Descriptions of every compiled kernel instance."""
+    return [gemm_a8w8_describe_variant(i) for i in range(gemm_a8w8_num_variants())]

@@ -1,0 +1,316 @@
+// a8w8_api.hip -- C ABI of libgemm_a8w8.so: argument checks, the exact-M
+// selector, per-device set-up and the launch on the caller's stream.
+//
+// Selection.  For each registered (N, K) the tuned table holds ascending keys
+// key_m[0] < key_m[1] < ... and the instance picked for each key.  A request
+// M is served by the instance of the smallest key >= M.  The generator that
+// writes the table keeps consecutive keys close enough that the key is never
+// above 1.25 M (and equals M for M <= 16), so no M runs an instance that was
+// tuned for a much larger problem -- unlike a lookup that pads M to the next
+// power of two and makes M = 6016 use the row tuned for 8192, the failure the
+// "Why aiter#5069's measured -25% kernel win moved serving throughput by 0.0%"
+// page describes (its "Two amplifiers" section).  An (N, K) with no table gets
+// a heuristic plan of the same kernels and is flagged, never refused: a lookup
+// gap falls back to a default kernel, as the "CK int8 GEMM ... gfx90a" page
+// recommends after its build-time lookup raised instead (its Gate 1).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <tuple>
+
+#include "a8w8_internal.h"
+#include "a8w8_selector_table.h"
+#include "gemm_a8w8_blockscale.h"
+
+using a8w8::Args;
+using a8w8::Variant;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Per-device state: 0 = not yet checked, 1 = gfx950 ready, 2 = unsupported.
+std::atomic<int> g_dev_state[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+std::mutex g_init_mutex;
+
+int device_ready(int *cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return A8W8_ERR_HIP;
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        std::lock_guard<std::mutex> lock(g_init_mutex);
+        st = g_dev_state[dev].load(std::memory_order_acquire);
+        if (st == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+                return A8W8_ERR_HIP;
+            if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+                st = 2;
+            } else {
+                if (a8w8::set_kernel_attributes() != hipSuccess)
+                    return A8W8_ERR_HIP;
+                g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+                st = 1;
+            }
+            g_dev_state[dev].store(st, std::memory_order_release);
+        }
+    }
+    if (st != 1)
+        return A8W8_ERR_ARCH;
+    *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    return A8W8_OK;
+}
+
+int check_shape(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 1 || K < 1 || (K % 128) != 0)
+        return A8W8_ERR_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return A8W8_ERR_SHAPE;
+    // Row offsets into the scale arrays are 32-bit inside the kernels.
+    if (M * (K / 128) >= ((int64_t)1 << 31) || ((N + 127) / 128) * (K / 128) >= ((int64_t)1 << 31))
+        return A8W8_ERR_SHAPE;
+    return A8W8_OK;
+}
+
+int check_pointers(const void *A, const float *a_scale, const void *W, const float *w_scale, const void *Y)
+{
+    if (!A || !a_scale || !W || !w_scale || !Y)
+        return A8W8_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(W) & 15))
+        return A8W8_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(a_scale) & 3) || (reinterpret_cast<uintptr_t>(w_scale) & 3))
+        return A8W8_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(Y) & 1)
+        return A8W8_ERR_ALIGN;
+    return A8W8_OK;
+}
+
+bool variant_accepts(int id, int64_t M)
+{
+    const Variant &v = a8w8::variant(id);
+    return v.max_m == 0 || M <= v.max_m;
+}
+
+int find_variant(int kernel, int bm, int bn, int waves)
+{
+    for (int i = 0; i < a8w8::num_variants(); ++i) {
+        const Variant &v = a8w8::variant(i);
+        if (v.kernel == kernel && v.bm == bm && v.bn == bn && (waves == 0 || v.waves == waves))
+            return i;
+    }
+    return -1;
+}
+
+// Plan for shapes with no tuned table: the skinny kernel up to M = 16 (waves
+// chosen so each keeps about four K blocks), else the largest tile that still
+// gives every compute unit at least two workgroups, else the smallest tile.
+int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
+{
+    if (M <= 16) {
+        const int64_t kb = K / 128;
+        const int waves = kb >= 64 ? 16 : (kb >= 24 ? 8 : 4);
+        return find_variant(A8W8_KERNEL_SKINNY, 16, 16, waves);
+    }
+    static const int kTiles[][2] = {{256, 128}, {128, 128}, {128, 64}, {64, 64}, {32, 64}, {32, 32}};
+    const int nt = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
+    for (int i = 0; i < nt; ++i) {
+        const int bm = kTiles[i][0], bn = kTiles[i][1];
+        if (N <= 32 && bn > 32)
+            continue;
+        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        if (tiles >= 2 * (int64_t)cus)
+            return find_variant(A8W8_KERNEL_TILE, bm, bn, 0);
+    }
+    return find_variant(A8W8_KERNEL_TILE, 32, 32, 0);
+}
+
+struct Choice {
+    int variant;
+    int64_t key_m;
+    int fallback;
+};
+
+Choice select_variant(int64_t M, int64_t N, int64_t K, int cus)
+{
+    using namespace a8w8_table;
+    for (int t = 0; t < kNumShapes; ++t) {
+        const ShapeTable &s = kShapes[t];
+        if (s.n != N || s.k != K)
+            continue;
+        // smallest key >= M (binary search over the ascending keys)
+        int lo = 0, hi = s.count;
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (s.key_m[mid] < M)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        if (lo < s.count) {
+            const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo]);
+            if (v >= 0 && variant_accepts(v, M))
+                return {v, s.key_m[lo], 0};
+        }
+        break;
+    }
+    return {heuristic_variant(M, N, K, cus), M, 1};
+}
+
+void fill_plan(int id, int64_t M, int64_t N, int64_t key_m, int fallback, a8w8_plan *out)
+{
+    const Variant &v = a8w8::variant(id);
+    std::memset(out, 0, sizeof(*out));
+    out->kernel = v.kernel;
+    out->variant = id;
+    out->bm = v.bm;
+    out->bn = v.bn;
+    out->waves = v.waves;
+    out->ksplit = v.ksplit;
+    out->grid = M > 0 ? a8w8::variant_grid(id, M, N) : 0;
+    out->key_m = key_m;
+    out->fallback = fallback;
+}
+
+// GEMM_A8W8_LOG=1: one stderr line per distinct (M, N, K) with the plan used.
+void log_plan(int64_t M, int64_t N, int64_t K, int id, int64_t key_m, int fallback)
+{
+    static const bool enabled = [] {
+        const char *e = std::getenv("GEMM_A8W8_LOG");
+        return e && e[0] && std::strcmp(e, "0") != 0;
+    }();
+    if (!enabled)
+        return;
+    static std::mutex mu;
+    static std::set<std::tuple<int64_t, int64_t, int64_t>> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!seen.insert(std::make_tuple(M, N, K)).second)
+        return;
+    std::fprintf(stderr, "gemm_a8w8: M=%lld N=%lld K=%lld -> %s key_m=%lld%s\n", (long long)M, (long long)N,
+                 (long long)K, a8w8::variant(id).name, (long long)key_m, fallback ? " fallback" : "");
+}
+
+int launch(int id, const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
+           int64_t M, int64_t N, int64_t K, void *stream)
+{
+    Args a;
+    a.A = static_cast<const uint8_t *>(A);
+    a.a_scale = a_scale;
+    a.W = static_cast<const uint8_t *>(W);
+    a.w_scale = w_scale;
+    a.Y = static_cast<uint16_t *>(Y);
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    if (a8w8::launch_variant(id, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return A8W8_ERR_HIP;
+    return A8W8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
+                         int64_t M, int64_t N, int64_t K, void *stream)
+{
+    int rc = check_shape(M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M == 0)
+        return A8W8_OK;
+    rc = check_pointers(A, a_scale, W, w_scale, Y);
+    if (rc != A8W8_OK)
+        return rc;
+    int cus = 0;
+    rc = device_ready(&cus);
+    if (rc != A8W8_OK)
+        return rc;
+    const Choice c = select_variant(M, N, K, cus);
+    log_plan(M, N, K, c.variant, c.key_m, c.fallback);
+    return launch(c.variant, A, a_scale, W, w_scale, Y, M, N, K, stream);
+}
+
+int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
+{
+    if (!out)
+        return A8W8_ERR_NULL;
+    const int rc = check_shape(M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    const int cus = cu_count > 0 ? cu_count : 256;
+    const Choice c = select_variant(M > 0 ? M : 1, N, K, cus);
+    fill_plan(c.variant, M, N, c.key_m, c.fallback, out);
+    return A8W8_OK;
+}
+
+int gemm_a8w8_num_variants(void) { return a8w8::num_variants(); }
+
+int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K, a8w8_plan *out)
+{
+    if (!out)
+        return A8W8_ERR_NULL;
+    if (variant < 0 || variant >= a8w8::num_variants())
+        return A8W8_ERR_PLAN;
+    if (M < 0 || N < 1 || K < 1)
+        return A8W8_ERR_SHAPE;
+    fill_plan(variant, M, N, M, 0, out);
+    return A8W8_OK;
+}
+
+int gemm_a8w8_blockscale_run_variant(int32_t variant, const void *A, const float *a_scale, const void *W,
+                                     const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
+                                     void *stream)
+{
+    if (variant < 0 || variant >= a8w8::num_variants())
+        return A8W8_ERR_PLAN;
+    int rc = check_shape(M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M == 0)
+        return A8W8_OK;
+    if (!variant_accepts(variant, M))
+        return A8W8_ERR_PLAN;
+    rc = check_pointers(A, a_scale, W, w_scale, Y);
+    if (rc != A8W8_OK)
+        return rc;
+    int cus = 0;
+    rc = device_ready(&cus);
+    if (rc != A8W8_OK)
+        return rc;
+    return launch(variant, A, a_scale, W, w_scale, Y, M, N, K, stream);
+}
+
+const char *gemm_a8w8_variant_name(int32_t variant)
+{
+    if (variant < 0 || variant >= a8w8::num_variants())
+        return nullptr;
+    return a8w8::variant(variant).name;
+}
+
+const char *gemm_a8w8_status_string(int status)
+{
+    switch (status) {
+    case A8W8_OK: return "ok";
+    case A8W8_ERR_NULL: return "a required pointer is NULL";
+    case A8W8_ERR_SHAPE: return "invalid shape (need M >= 0, N >= 1, K >= 1, K % 128 == 0, dims <= 2^30)";
+    case A8W8_ERR_ALIGN: return "misaligned buffer (A and W need 16 bytes, scales 4, Y 2)";
+    case A8W8_ERR_ARCH: return "the current device is not gfx950 (MI355X)";
+    case A8W8_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case A8W8_ERR_PLAN: return "invalid kernel instance for this shape";
+    default: return "unknown status";
+    }
+}
+
+uint64_t gemm_a8w8_table_hash(void) { return a8w8_table::kTableHash; }
+
+}  // extern "C"

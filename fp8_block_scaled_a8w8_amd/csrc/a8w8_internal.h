@@ -1,0 +1,38 @@
+// a8w8_internal.h -- declarations shared by the host API and the kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace a8w8 {
+
+// One compiled kernel instance.
+struct Variant {
+    int32_t kernel;    // A8W8_KERNEL_SKINNY or A8W8_KERNEL_TILE
+    int32_t bm, bn;    // output tile per workgroup (skinny: 16 x 16)
+    int32_t waves;     // waves per workgroup
+    int32_t ksplit;    // ways one tile's K loop is split (skinny: over the waves)
+    int32_t max_m;     // largest M the instance accepts (skinny: 16), 0 = any
+    const char *name;
+};
+
+struct Args {
+    const uint8_t *A;
+    const float *a_scale;
+    const uint8_t *W;
+    const float *w_scale;
+    uint16_t *Y;
+    int32_t M, N, K;
+};
+
+int num_variants();
+const Variant &variant(int id);
+// Workgroups the instance launches for (M, N).
+int64_t variant_grid(int id, int64_t M, int64_t N);
+// Raise the dynamic-LDS limit of the instances that need more than 64 KB
+// (once per device, with that device current).
+hipError_t set_kernel_attributes();
+// Enqueue the instance; returns hipSuccess or the launch error.
+hipError_t launch_variant(int id, const Args &a, hipStream_t stream);
+
+}  // namespace a8w8

@@ -1,0 +1,123 @@
+/*
+ * gemm_a8w8_blockscale.h -- C ABI of libgemm_a8w8.so, the a8w8 block-scale
+ * GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("gemm_a8w8_blockscale", the op that the "[Perf] Retune gfx942
+ * Qwen3.8-27B a8w8 blockscale decode rows for cold weights" page retunes in its
+ * Kernel section, and that dense projections of a checkpoint quantised with
+ * "weight_block_size: [128,128]" take, per "Why aiter#5069's measured -25%
+ * kernel win moved serving throughput by 0.0%"):
+ *
+ *   Y[m,n] = bf16( sum over 128-wide K blocks kb of
+ *                  (sum_{k in kb} e4m3(A[m,k]) * e4m3(W[n,k]))
+ *                  * a_scale[m,kb] * w_scale[n/128,kb] )
+ *
+ * i.e. Y = A . W^T with fp8 e4m3 operands, fp32 scales per 1x128 activation
+ * group and per 128x128 weight block, fp32 accumulation, and one
+ * round-to-nearest-even to bf16 at the end.  The pages name the op but print no
+ * formula; this scale granularity and the e4m3 variant (OCP "e4m3fn", largest
+ * finite 448, no infinities) are this library's reading.
+ *
+ * Buffers (all device memory, row-major, owned by the caller; the library
+ * never frees or keeps a pointer after the call returns):
+ *   A        uint8 e4m3fn [M, K]                         16-byte aligned
+ *   a_scale  float32      [M, K/128]                      4-byte aligned
+ *   W        uint8 e4m3fn [N, K]                         16-byte aligned
+ *   w_scale  float32      [ceil(N/128), K/128]            4-byte aligned
+ *   Y        bf16 (uint16 bit patterns) [M, N]            2-byte aligned; overwritten
+ * Y must not overlap any input.
+ *
+ * Threading / asynchrony: calls only enqueue kernels on `stream` (a
+ * hipStream_t; NULL = the null stream) and return; they never synchronise the
+ * host, allocate, or issue memsets, so they may be captured into a HIP graph.
+ * Calls are re-entrant; the selector table is immutable.
+ */
+#ifndef GEMM_A8W8_BLOCKSCALE_H
+#define GEMM_A8W8_BLOCKSCALE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Nothing is thrown across this ABI. */
+enum {
+    A8W8_OK = 0,
+    A8W8_ERR_NULL = 1,    /* a required pointer is NULL                          */
+    A8W8_ERR_SHAPE = 2,   /* M < 0, N < 1, K < 1, K % 128 != 0, or a dimension too large */
+    A8W8_ERR_ALIGN = 3,   /* A or W not 16-byte aligned, a scale or Y not 4-byte aligned */
+    A8W8_ERR_ARCH = 4,    /* the current device is not gfx950                    */
+    A8W8_ERR_HIP = 5,     /* a HIP runtime call or kernel launch failed          */
+    A8W8_ERR_PLAN = 6     /* a plan passed to gemm_a8w8_blockscale_run_plan is invalid for the shape */
+};
+
+/* Kernels behind the selector. */
+enum {
+    A8W8_KERNEL_SKINNY = 1,  /* M <= 16: streams W once, K split over the waves of a workgroup */
+    A8W8_KERNEL_TILE = 2     /* LDS double-buffered fp8-MFMA output tiles                     */
+};
+
+/*
+ * A launch plan.  `variant` identifies a compiled kernel instance; the other
+ * fields describe it (and the launch for the given shape) for logging and tests.
+ */
+typedef struct {
+    int32_t kernel;     /* A8W8_KERNEL_*                                                */
+    int32_t variant;    /* index in [0, gemm_a8w8_num_variants())                       */
+    int32_t bm, bn;     /* output tile of one workgroup: rows of Y (M) x columns (N)    */
+    int32_t waves;      /* waves (64 lanes) per workgroup                               */
+    int32_t ksplit;     /* ways the K loop of one tile is split (across waves)          */
+    int64_t grid;       /* workgroups launched for this shape                           */
+    int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
+    int32_t fallback;   /* 1: (N,K) has no tuned table, a heuristic plan was chosen     */
+    int32_t reserved;
+} a8w8_plan;
+
+/*
+ * Y = A . W^T with block scales (see top of file).  M == 0 is a no-op
+ * returning A8W8_OK.  Errors are reported before anything is enqueued.
+ */
+int gemm_a8w8_blockscale(const void *A, const float *a_scale,
+                         const void *W, const float *w_scale,
+                         void *Y, int64_t M, int64_t N, int64_t K,
+                         void *stream);
+
+/*
+ * The plan gemm_a8w8_blockscale would launch for (M, N, K) on a gfx950
+ * device with `cu_count` compute units (0 = 256).  Host only; needs no GPU.
+ */
+int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count,
+                              a8w8_plan *out);
+
+/* Number of compiled kernel instances, and the description of one of them
+   (grid and key_m are filled for (M, N, K); M may be 0 for a bare description). */
+int gemm_a8w8_num_variants(void);
+int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
+                               a8w8_plan *out);
+
+/*
+ * Run a specific instance (for tuning).  Same contract as gemm_a8w8_blockscale;
+ * returns A8W8_ERR_PLAN if the instance cannot handle M (the skinny kernel
+ * needs M <= 16).
+ */
+int gemm_a8w8_blockscale_run_variant(int32_t variant,
+                                     const void *A, const float *a_scale,
+                                     const void *W, const float *w_scale,
+                                     void *Y, int64_t M, int64_t N, int64_t K,
+                                     void *stream);
+
+/* Static name of a compiled instance, e.g. "tile_256x128" (NULL if out of range). */
+const char *gemm_a8w8_variant_name(int32_t variant);
+
+/* Static, human-readable text for a status code. */
+const char *gemm_a8w8_status_string(int status);
+
+/* Hash of the compiled selector table (identifies the tuning that is deployed). */
+uint64_t gemm_a8w8_table_hash(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_A8W8_BLOCKSCALE_H */

@@ -1,0 +1,144 @@
+"""Host-side checks of libgemm_a8w8.so: exports, argument errors, selector table.
+
+Nothing here launches a kernel: argument errors are reported before the
+library touches the HIP runtime, and planning is host-only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_block_scaled_a8w8_amd as g
+from fp8_block_scaled_a8w8_amd import gen_selector_table as gst
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_a8w8_blockscale.h")
+
+# the (N, K) pairs the tuned table must cover, M = 1..8192
+REGISTERED = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6144), (32, 6144), (512, 1024)]
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_a8w8_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(g.LIB_PATH)
+    declared = _declared_functions()
+    assert len(declared) >= 8
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(g.EXPORTED) == declared
+
+
+def _call(A=16, a_s=16, W=16, w_s=16, Y=16, M=4, N=512, K=1024):
+    return g.lib().gemm_a8w8_blockscale(A, a_s, W, w_s, Y, M, N, K, None)
+
+
+@pytest.mark.parametrize("M,N,K", [(-1, 512, 1024), (4, 0, 1024), (4, 512, 0), (4, 512, 1000),
+                                   (4, 512, 127), (1 << 31, 512, 1024)])
+def test_bad_shapes(M, N, K):
+    assert _call(M=M, N=N, K=K) == g.A8W8_ERR_SHAPE
+    p = g.Plan()
+    assert g.lib().gemm_a8w8_blockscale_plan(M, N, K, 0, ctypes.byref(p)) == g.A8W8_ERR_SHAPE
+
+
+def test_m_zero_is_a_no_op_even_with_null_pointers():
+    assert g.lib().gemm_a8w8_blockscale(None, None, None, None, None, 0, 512, 1024, None) == g.A8W8_OK
+
+
+@pytest.mark.parametrize("which", ["A", "a_s", "W", "w_s", "Y"])
+def test_null_pointers(which):
+    assert _call(**{which: None}) == g.A8W8_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [{"A": 24}, {"W": 8}, {"a_s": 18}, {"w_s": 2}, {"Y": 17}])
+def test_misaligned_pointers(kw):
+    assert _call(**kw) == g.A8W8_ERR_ALIGN
+
+
+def test_status_strings_and_variant_names():
+    for s in range(7):
+        assert g.gemm_a8w8_status_string(s)
+    assert g.gemm_a8w8_status_string(99) == "unknown status"
+    n = g.gemm_a8w8_num_variants()
+    names = [g.gemm_a8w8_variant_name(i) for i in range(n)]
+    assert len(set(names)) == n and all(names)
+    assert g.gemm_a8w8_variant_name(n) is None
+    assert g.lib().gemm_a8w8_describe_variant(n, 1, 1, 128, ctypes.byref(g.Plan())) == g.A8W8_ERR_PLAN
+
+
+def test_run_variant_rejects_skinny_above_16_rows():
+    skinny = [v["variant"] for v in g.variants() if v["kernel_name"] == "skinny"]
+    assert skinny
+    rc = g.lib().gemm_a8w8_blockscale_run_variant(skinny[0], 16, 16, 16, 16, 16, 17, 512, 1024, None)
+    assert rc == g.A8W8_ERR_PLAN
+
+
+def test_variant_shapes_are_launchable():
+    for v in g.variants():
+        if v["kernel_name"] == "tile":
+            assert v["bm"] % 32 == 0 and v["bn"] % 32 == 0 and v["bn"] // 2 <= 128
+            assert 128 % (v["bn"] // 2) == 0, v          # a wave's columns stay in one weight block
+            assert 2 * (v["bm"] + v["bn"]) * 128 <= 160 * 1024
+        else:
+            assert v["bm"] == 16 and v["bn"] == 16
+
+
+# ---------------------------------------------------------------- selector table
+
+def test_generated_header_matches_table():
+    assert gst.main(["--check"]) == 0
+
+
+def test_table_validation_rejects_bad_tables():
+    good = {"shapes": [{"n": 64, "k": 128, "rows":
+                        [{"key_m": m, "kernel": "skinny", "bm": 16, "bn": 16, "waves": 4} for m in range(1, 17)] +
+                        [{"key_m": 20, "kernel": "tile", "bm": 32, "bn": 32, "waves": 4},
+                         {"key_m": 8192, "kernel": "tile", "bm": 32, "bn": 32, "waves": 4}]}]}
+    with pytest.raises(ValueError):
+        gst.validate(good)                                   # 8192 serves M = 21 (> 1.25x)
+    rows = good["shapes"][0]["rows"][:-1]
+    m = 20
+    while m < 8192:
+        m = min(8192, int(m * 1.25))
+        rows.append({"key_m": m, "kernel": "tile", "bm": 32, "bn": 32, "waves": 4})
+    ok = {"shapes": [{"n": 64, "k": 128, "rows": rows}]}
+    gst.validate(ok)
+    dup = {"shapes": ok["shapes"] * 2}
+    with pytest.raises(ValueError):
+        gst.validate(dup)
+    bad = {"shapes": [{"n": 64, "k": 128, "rows": rows[:3] + [dict(rows[3], key_m=3)] + rows[4:]}]}
+    with pytest.raises(ValueError):
+        gst.validate(bad)
+
+
+def _table_shapes():
+    return [(int(s["n"]), int(s["k"])) for s in gst.load()["shapes"]]
+
+
+@pytest.mark.parametrize("N,K", REGISTERED)
+def test_every_m_has_a_tuned_plan_within_125_percent(N, K):
+    if (N, K) not in _table_shapes():
+        pytest.skip(f"({N},{K}) has no tuned table yet")
+    for M in range(1, 8193):
+        p = g.gemm_a8w8_blockscale_plan(M, N, K)
+        assert p["fallback"] == 0, (M, p)
+        assert M <= p["key_m"] <= 1.25 * M, (M, p)
+        if M <= 16:
+            assert p["key_m"] == M
+        if p["kernel_name"] == "skinny":
+            assert M <= 16
+
+
+def test_unregistered_shape_falls_back_not_fails():
+    p = g.gemm_a8w8_blockscale_plan(3, 1000, 384)
+    assert p["fallback"] == 1 and p["kernel_name"] == "skinny"
+    p = g.gemm_a8w8_blockscale_plan(5000, 1000, 384)
+    assert p["fallback"] == 1 and p["kernel_name"] == "tile"
+    assert p["grid"] == ((5000 + p["bm"] - 1) // p["bm"]) * ((1000 + p["bn"] - 1) // p["bn"])

@@ -1,0 +1,230 @@
+"""GPU parity: libgemm_a8w8.so (through its C ABI) against the fp64 CPU oracle.
+
+Bar: rel-L2 <= 3e-3 and per-element |err| <= 2e-2 rms(ref) unless the value is
+one of the two bf16 neighbours of the exact result (tests/parity_util.py).
+Workloads use the seeded recipe of inputgen (A ~ N(0,1) with 1x128 scales,
+W ~ N(0,0.02) with 128x128 scales) at the shapes the pages time: decode
+(N,K) in {(14336,5120), (5120,6144), (34816,5120)} at every M <= 16, prefill
+M in {512, 2048, 6016, 8192}, and a dense sweep of 256 random M over six
+(N,K).  Large outputs are checked on sampled rows (each row of Y depends only
+on its row of A, so a sampled row is checked in full).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_a8w8_amd as g
+import inputgen
+import oracle
+from tests.gpu_util import DEV, run, say, to_dev, y_bits, y_host
+from tests.parity_util import assert_parity, bf16_round
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, N, K, a_seed=0, w_seed=1):
+    A, a_s = inputgen.make_activations(M, K, seed=a_seed)
+    W, w_s = inputgen.make_weights(N, K, seed=w_seed)
+    return A, a_s, W, w_s
+
+
+def test_device_is_gfx950():
+    assert torch.cuda.is_available()
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+
+
+def test_tiny_config_full():
+    M, N, K = 4, 512, 1024
+    A, a_s, W, w_s = _inputs(M, N, K)
+    y = run(*to_dev(A, a_s, W, w_s))
+    st = assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), "tiny")
+    say("tiny", st)
+
+
+@pytest.mark.parametrize("N,K", [(14336, 5120), (5120, 6144), (34816, 5120)])
+def test_decode_every_m_up_to_16(N, K):
+    A, a_s, W, w_s = _inputs(16, N, K)
+    ref = oracle.gemm(A, a_s, W, w_s)                 # row m of Y depends only on row m of A
+    dA, da, dW, dw = to_dev(A, a_s, W, w_s)
+    for M in range(1, 17):
+        y = run(dA[:M], da[:M], dW, dw)
+        st = assert_parity(y_host(y), ref[:M], f"decode M={M} N={N} K={K}")
+        say(f"decode M={M} N={N} K={K} plan={g.gemm_a8w8_blockscale_plan(M, N, K)['name']} "
+            f"rel_l2={st['rel_l2']:.3e} err_ratio={st['error_ratio']:.2e}")
+
+
+def _sample_rows(M, rng, extra=()):
+    rows = {0, M - 1, M // 2, *[r for r in extra if 0 <= r < M]}
+    for b in (32, 64, 128, 256):
+        last = ((M - 1) // b) * b
+        rows.update({last, max(0, last - 1)})
+    rows.update(int(r) for r in rng.integers(0, M, size=6))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("N,K", [(14336, 5120), (16384, 5120)])
+def test_prefill_sampled_rows(N, K):
+    W, w_s = inputgen.make_weights(N, K, seed=1)
+    dW = torch.from_numpy(W).to(DEV)
+    dw = torch.from_numpy(w_s).to(DEV)
+    A_all, a_all = inputgen.make_activations(8192, K, seed=0)
+    rng = np.random.default_rng(5)
+    for M in (512, 2048, 6016, 8192):
+        A, a_s = A_all[:M], a_all[:M]
+        y = run(torch.from_numpy(A).to(DEV), torch.from_numpy(a_s).to(DEV), dW, dw)
+        rows = _sample_rows(M, rng)
+        yh = y_host(y)[rows]
+        st = assert_parity(yh, oracle.gemm(A, a_s, W, w_s, rows=rows), f"prefill M={M} N={N}")
+        say(f"prefill M={M} N={N} K={K} plan={g.gemm_a8w8_blockscale_plan(M, N, K)['name']} "
+            f"rows={len(rows)} rel_l2={st['rel_l2']:.3e}")
+        del y
+
+
+SWEEP_NK = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6144), (32, 6144)]
+
+
+@pytest.mark.parametrize("N,K", SWEEP_NK)
+def test_dense_m_sweep_sampled_rows(N, K):
+    Ms = inputgen.random_m_values(256, seed=2)
+    A_all, a_all = inputgen.make_activations(8192, K, seed=0)
+    W, w_s = inputgen.make_weights(N, K, seed=1)
+    dA, da, dW, dw = to_dev(A_all, a_all, W, w_s)
+    rng = np.random.default_rng(6)
+    picked = []          # (M, rows, gpu values of those rows)
+    for M in Ms:
+        y = run(dA[:M], da[:M], dW, dw)
+        rows = sorted({M - 1, int(rng.integers(0, M))})
+        picked.append((M, rows, y[rows].to(torch.float32).cpu().numpy().astype(np.float64)))
+    union = sorted({r for _, rows, _ in picked for r in rows})
+    ref = oracle.gemm(A_all, a_all, W, w_s, rows=union)
+    pos = {r: i for i, r in enumerate(union)}
+    ys = np.concatenate([v for _, _, v in picked])
+    refs = np.concatenate([ref[[pos[r] for r in rows]] for _, rows, _ in picked])
+    st = assert_parity(ys, refs, f"sweep N={N} K={K}")
+    say(f"sweep N={N} K={K}: {len(Ms)} M values, {ys.shape[0]} rows, rel_l2={st['rel_l2']:.3e} "
+        f"err_ratio={st['error_ratio']:.2e}")
+
+
+# ---------------------------------------------------------------- every compiled instance
+
+@pytest.mark.parametrize("variant", range(14))
+def test_every_instance_on_ragged_shape(variant):
+    if variant >= g.gemm_a8w8_num_variants():
+        pytest.skip("no such instance")
+    info = g.gemm_a8w8_describe_variant(variant)
+    K = 640
+    for (M, N) in ([(1, 300), (7, 130), (16, 64)] if info["kernel_name"] == "skinny"
+                   else [(77, 300), (200, 520), (33, 32)]):
+        A, a_s, W, w_s = _inputs(M, N, K, a_seed=10 + M, w_seed=20 + N)
+        y = run(*to_dev(A, a_s, W, w_s), variant=variant)
+        assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{info['name']} M={M} N={N}")
+    say(f"instance {info['name']} ok")
+
+
+# ---------------------------------------------------------------- bitwise invariants
+
+def test_identity_weights_power_of_two_scales_exact():
+    M, K, N = 21, 384, 300
+    A, _ = inputgen.make_activations(M, K, seed=3)
+    a_s = np.ldexp(np.ones((M, K // 128), np.float32),
+                   np.random.default_rng(4).integers(-6, 3, size=(M, K // 128))).astype(np.float32)
+    W = np.zeros((N, K), np.uint8)
+    W[np.arange(N), np.arange(N)] = 0x38
+    w_s = np.ones(((N + 127) // 128, K // 128), np.float32)
+    ref = oracle.gemm(A, a_s, W, w_s)
+    assert np.array_equal(bf16_round(ref), ref)          # every value is a bf16
+    for Mx in (M, 5):
+        y = run(*to_dev(A[:Mx], a_s[:Mx], W, w_s))
+        assert np.array_equal(y_host(y), ref[:Mx])
+
+
+def test_integer_valued_inputs_exact():
+    rng = np.random.default_rng(8)
+    for M, N, K in ((9, 200, 256), (70, 96, 128)):
+        A = rng.choice(np.array([0xB8, 0x00, 0x38], np.uint8), size=(M, K))
+        W = rng.choice(np.array([0xB8, 0x00, 0x38], np.uint8), size=(N, K))
+        a_s = np.ones((M, K // 128), np.float32)
+        w_s = np.ones(((N + 127) // 128, K // 128), np.float32)
+        ref = oracle.gemm(A, a_s, W, w_s)
+        y = run(*to_dev(A, a_s, W, w_s))
+        assert np.array_equal(y_host(y), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 5120, 6144), (300, 1000, 1024)])
+def test_doubling_activation_scales_doubles_output(M, N, K):
+    A, a_s, W, w_s = _inputs(M, N, K)
+    dA, da, dW, dw = to_dev(A, a_s, W, w_s)
+    y1 = y_host(run(dA, da, dW, dw))
+    y2 = y_host(run(dA, da * 2, dW, dw))
+    assert np.array_equal(y2, 2 * y1)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 14336, 5120), (1000, 2048, 1024)])
+def test_repeat_calls_bitwise_identical(M, N, K):
+    A, a_s, W, w_s = _inputs(M, N, K)
+    d = to_dev(A, a_s, W, w_s)
+    a = y_bits(run(*d))
+    for _ in range(3):
+        assert np.array_equal(y_bits(run(*d)), a)
+
+
+def test_graph_replay_matches_eager():
+    cases = []
+    for (M, N, K) in ((2, 14336, 5120), (600, 1536, 1024)):
+        A, a_s, W, w_s = _inputs(M, N, K)
+        d = to_dev(A, a_s, W, w_s)
+        eager = y_bits(run(*d))
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        cases.append((d, out, eager))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        run(*cases[0][0], out=cases[0][1])      # warm-up on the capture stream
+        run(*cases[1][0], out=cases[1][1])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        for d, out, _ in cases:
+            g.gemm_a8w8_blockscale(*d, out=out, stream=s)
+    for rep in range(4):
+        for _, out, _ in cases:
+            out.fill_(0)                         # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for _, out, eager in cases:
+            assert np.array_equal(y_bits(out), eager), f"replay {rep}"
+
+
+# ---------------------------------------------------------------- bounds
+
+@pytest.mark.parametrize("M,N,K", [(1, 32, 6144), (5, 130, 256), (17, 32, 6144), (33, 300, 384),
+                                   (255, 256, 6144), (257, 520, 640), (6016, 96, 256)])
+def test_output_guard_bands_untouched(M, N, K):
+    A, a_s, W, w_s = _inputs(M, N, K, a_seed=M, w_seed=N)
+    pad = 64
+    sentinel = torch.tensor([-12345.0], dtype=torch.bfloat16).view(torch.int16).item()
+    buf = torch.full((pad + M * N + pad,), sentinel, dtype=torch.int16, device=DEV)
+    out = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    run(*to_dev(A, a_s, W, w_s), out=out)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:pad] == sentinel) and np.all(b[-pad:] == sentinel)
+    assert_parity(y_host(out), oracle.gemm(A, a_s, W, w_s), f"guard M={M} N={N}")
+
+
+def test_error_paths_on_device():
+    A, a_s, W, w_s = _inputs(17, 64, 256)
+    d = to_dev(A, a_s, W, w_s)
+    skinny = [v["variant"] for v in g.variants() if v["kernel_name"] == "skinny"][0]
+    with pytest.raises(g.A8W8Error) as e:
+        g.gemm_a8w8_blockscale_run_variant(skinny, *d)
+    assert e.value.status == g.A8W8_ERR_PLAN
+    out = torch.empty((17, 64), dtype=torch.bfloat16, device=DEV)
+    rc = g.lib().gemm_a8w8_blockscale(d[0].data_ptr() + 1, d[1].data_ptr(), d[2].data_ptr(),
+                                      d[3].data_ptr(), out.data_ptr(), 17, 64, 256, None)
+    assert rc == g.A8W8_ERR_ALIGN
