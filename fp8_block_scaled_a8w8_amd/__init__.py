@@ -50,12 +50,12 @@ class A8W8Error(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("ksplit", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("key_m", ctypes.c_int64),
-                ("fallback", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("kblocks", ctypes.c_int32),
+                ("kpasses", ctypes.c_int32), ("fallback", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("key_m", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
-        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d = {f: getattr(self, f) for f, _ in self._fields_}
         d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
         return d
 

@@ -95,31 +95,57 @@ int check_pointers(const void *A, const float *a_scale, const void *W, const flo
     return A8W8_OK;
 }
 
-bool variant_accepts(int id, int64_t M)
+// The skinny kernel addresses A and W with 32-bit per-lane offsets.
+bool skinny_fits(int64_t N, int64_t K)
 {
-    const Variant &v = a8w8::variant(id);
-    return v.max_m == 0 || M <= v.max_m;
+    return N * K < ((int64_t)1 << 32) && 16 * K < ((int64_t)1 << 32);
 }
 
-int find_variant(int kernel, int bm, int bn, int waves)
+bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
+{
+    const Variant &v = a8w8::variant(id);
+    if (v.kernel == A8W8_KERNEL_SKINNY)
+        return M <= v.max_m && skinny_fits(N, K);
+    return true;
+}
+
+int find_variant(int kernel, int bm, int bn, int waves, int kblocks)
 {
     for (int i = 0; i < a8w8::num_variants(); ++i) {
         const Variant &v = a8w8::variant(i);
-        if (v.kernel == kernel && v.bm == bm && v.bn == bn && (waves == 0 || v.waves == waves))
+        if (v.kernel == kernel && v.bm == bm && v.bn == bn && (waves == 0 || v.waves == waves) &&
+            (kblocks == 0 || v.kblocks == kblocks))
             return i;
     }
     return -1;
 }
 
-// Plan for shapes with no tuned table: the skinny kernel up to M = 16 (waves
-// chosen so each keeps about four K blocks), else the largest tile that still
-// gives every compute unit at least two workgroups, else the smallest tile.
+// Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
+// with the widest row group that still yields at least ~200 workgroups (wider
+// groups share each activation fragment across more weight tiles), covering
+// K in one pass with the fewest blocks per wave.  Above: the largest tile that
+// still gives every compute unit at least two workgroups, else the smallest.
 int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
 {
-    if (M <= 16) {
-        const int64_t kb = K / 128;
-        const int waves = kb >= 64 ? 16 : (kb >= 24 ? 8 : 4);
-        return find_variant(A8W8_KERNEL_SKINNY, 16, 16, waves);
+    if (M <= 16 && skinny_fits(N, K)) {
+        int best = -1;
+        int64_t best_key = 0;
+        for (int i = 0; i < a8w8::num_variants(); ++i) {
+            const Variant &v = a8w8::variant(i);
+            if (v.kernel != A8W8_KERNEL_SKINNY)
+                continue;
+            const int64_t groups = (N + v.bn - 1) / v.bn;
+            const int64_t passes = a8w8::variant_passes(i, K);
+            // rank: enough workgroups, then one pass, then wider rows, then fewer blocks per pass
+            const int64_t key = (groups >= 200 || v.bn == 16 ? 1 : 0) * 1000000 + (passes == 1 ? 1 : 0) * 100000 +
+                                v.bn * 100 - v.waves * v.kblocks;
+            if (best < 0 || key > best_key) {
+                best = i;
+                best_key = key;
+            }
+        }
+        if (best >= 0)
+            return best;
     }
     static const int kTiles[][2] = {{256, 128}, {128, 128}, {128, 64}, {64, 64}, {32, 64}, {32, 32}};
     const int nt = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
@@ -129,9 +155,9 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
             continue;
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
         if (tiles >= 2 * (int64_t)cus)
-            return find_variant(A8W8_KERNEL_TILE, bm, bn, 0);
+            return find_variant(A8W8_KERNEL_TILE, bm, bn, 0, 0);
     }
-    return find_variant(A8W8_KERNEL_TILE, 32, 32, 0);
+    return find_variant(A8W8_KERNEL_TILE, 32, 32, 0, 0);
 }
 
 struct Choice {
@@ -157,8 +183,8 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus)
                 hi = mid;
         }
         if (lo < s.count) {
-            const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo]);
-            if (v >= 0 && variant_accepts(v, M))
+            const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo], s.kblocks[lo]);
+            if (v >= 0 && variant_accepts(v, M, N, K))
                 return {v, s.key_m[lo], 0};
         }
         break;
@@ -166,7 +192,7 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus)
     return {heuristic_variant(M, N, K, cus), M, 1};
 }
 
-void fill_plan(int id, int64_t M, int64_t N, int64_t key_m, int fallback, a8w8_plan *out)
+void fill_plan(int id, int64_t M, int64_t N, int64_t K, int64_t key_m, int fallback, a8w8_plan *out)
 {
     const Variant &v = a8w8::variant(id);
     std::memset(out, 0, sizeof(*out));
@@ -175,8 +201,9 @@ void fill_plan(int id, int64_t M, int64_t N, int64_t key_m, int fallback, a8w8_p
     out->bm = v.bm;
     out->bn = v.bn;
     out->waves = v.waves;
-    out->ksplit = v.ksplit;
-    out->grid = M > 0 ? a8w8::variant_grid(id, M, N) : 0;
+    out->kblocks = v.kblocks;
+    out->kpasses = (int32_t)a8w8::variant_passes(id, K);
+    out->grid = M > 0 ? a8w8::variant_grid(id, M, N, K) : 0;
     out->key_m = key_m;
     out->fallback = fallback;
 }
@@ -249,7 +276,7 @@ int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count,
         return rc;
     const int cus = cu_count > 0 ? cu_count : 256;
     const Choice c = select_variant(M > 0 ? M : 1, N, K, cus);
-    fill_plan(c.variant, M, N, c.key_m, c.fallback, out);
+    fill_plan(c.variant, M, N, K, c.key_m, c.fallback, out);
     return A8W8_OK;
 }
 
@@ -263,7 +290,7 @@ int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
         return A8W8_ERR_PLAN;
     if (M < 0 || N < 1 || K < 1)
         return A8W8_ERR_SHAPE;
-    fill_plan(variant, M, N, M, 0, out);
+    fill_plan(variant, M, N, K, M, 0, out);
     return A8W8_OK;
 }
 
@@ -278,7 +305,7 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant, const void *A, const float
         return rc;
     if (M == 0)
         return A8W8_OK;
-    if (!variant_accepts(variant, M))
+    if (!variant_accepts(variant, M, N, K))
         return A8W8_ERR_PLAN;
     rc = check_pointers(A, a_scale, W, w_scale, Y);
     if (rc != A8W8_OK)

@@ -9,12 +9,13 @@ namespace a8w8 {
 // One compiled kernel instance.
 struct Variant {
     int32_t kernel;    // A8W8_KERNEL_SKINNY or A8W8_KERNEL_TILE
-    int32_t bm, bn;    // output tile per workgroup (skinny: 16 x 16)
+    int32_t bm, bn;    // output tile per workgroup (skinny: 16 x 16 * tiles per wave)
     int32_t waves;     // waves per workgroup
-    int32_t ksplit;    // ways one tile's K loop is split (skinny: over the waves)
+    int32_t kblocks;   // K blocks each wave loads (skinny), 1 for the tile kernel
     int32_t max_m;     // largest M the instance accepts (skinny: 16), 0 = any
     const char *name;
 };
+
 
 struct Args {
     const uint8_t *A;
@@ -27,8 +28,10 @@ struct Args {
 
 int num_variants();
 const Variant &variant(int id);
-// Workgroups the instance launches for (M, N).
-int64_t variant_grid(int id, int64_t M, int64_t N);
+// Workgroups the instance launches for (M, N, K), and the passes over K one
+// wave makes (skinny: ceil(K/128 / (waves * kblocks)); tile: K/128 blocks).
+int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K);
+int64_t variant_passes(int id, int64_t K);
 // Raise the dynamic-LDS limit of the instances that need more than 64 KB
 // (once per device, with that device current).
 hipError_t set_kernel_attributes();

@@ -39,6 +39,13 @@ __device__ __forceinline__ v4f mfma_block(v8i w, v8i a)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, z, 0, 0, 0, 0, 0, 0);
 }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, 32-bit data
+// format word of the CDNA buffer resource).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ v8i cat(v4i lo, v4i hi)
 {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -83,78 +90,136 @@ __device__ __forceinline__ void store4(uint16_t *Y, int64_t row_off, int n, int 
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel, M <= 16.  One workgroup owns 16 rows of W (16 output
-// columns) and NW waves split its K blocks into contiguous ranges.  Each wave
-// keeps DEPTH blocks of loads in flight (2 x 16-byte loads of W per lane per
-// block, every W byte read exactly once), takes one MFMA per block and one
-// FMA per output with a_scale * w_scale; the NW partial 16 x 16 tiles are then
-// summed through LDS in wave order (fixed order: deterministic) and rounded
-// once to bf16.
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
+// Skinny kernel, M <= 16 (decode): stream every byte of W from HBM exactly
+// once with as many bytes in flight as possible.
+//
+// A workgroup owns RG = 16*TPW rows of W (TPW 16-row tiles) and all of K; its
+// NW waves split the K blocks into contiguous runs of D blocks (more passes
+// if NW*D < K/128).  A wave issues all loads of a pass at once -- per block one
+// activation fragment and TPW weight fragments -- and one activation fragment
+// feeds TPW MFMAs.  Per block: one MFMA per tile, then one FMA per output with
+// a_scale * w_scale.  The NW wave partials of each tile are summed through LDS
+// in wave order (fixed order: bitwise deterministic), rounded once to bf16.
+//
+// Weight loads cover whole 128-byte lines: load 0 of a block takes rows 0-7 of
+// the 16-row tile and load 1 rows 8-15, lane (rho = l/16, p = l%16) reading
+// chunk 2 rho + (p >= 8) of row (p & 7) (+8).  A row_ror:8 DPP exchange between
+// lanes p and p+8 of each 16-lane row then leaves lane l with row l%16, bytes
+// [32 rho, 32 rho + 32) of the block -- the MFMA operand layout.  Streaming
+// whole lines per instruction is what lets the loads run at the HBM ceiling;
+// the half-line pattern of a direct MFMA-layout load measured ~35% slower.
+__device__ __forceinline__ v8i fix_row_layout(v4i v0, v4i v1)
 {
-    constexpr int DEPTH = NW >= 16 ? 4 : 8;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
-    const int n0 = blockIdx.x * 16;
-    const int r = lane & 15, g = lane >> 4;
-
-    const int wrow = min(n0 + r, N - 1);                 // clamp the N tail inside W
-    const uint8_t *wp = p.W + (size_t)wrow * K + g * 32;
-    const bool mval = r < M;
-    const int arow = mval ? r : 0;                       // padded rows read row 0, then zeroed
-    const uint8_t *ap = p.A + (size_t)arow * K + g * 32;
-    const float *asp = p.a_scale + (size_t)arow * KB;
-    const float *wsp = p.w_scale + (size_t)(n0 >> 7) * KB;
-
-    const int per = (KB + NW - 1) / NW;
-    const int kb_lo = min(KB, wave * per);
-    const int kb_hi = min(KB, kb_lo + per);
-
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int kb0 = kb_lo; kb0 < kb_hi; kb0 += DEPTH) {
-        v8i wf[DEPTH], af[DEPTH];
-        float s[DEPTH];
+    // lanes 8-15 of each row take v1 from lane p-8; lanes 0-7 take v0 from lane p+8
+    v4i a, b;
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            const int kb = kb0 + j;
-            if (kb < kb_hi) {
-                const v4i *w4 = reinterpret_cast<const v4i *>(wp + (size_t)kb * 128);
-                const v4i *a4 = reinterpret_cast<const v4i *>(ap + (size_t)kb * 128);
-                wf[j] = cat(__builtin_nontemporal_load(w4), __builtin_nontemporal_load(w4 + 1));
-                const v8i a8 = cat(a4[0], a4[1]);
-                af[j] = mval ? a8 : zero8;
-                s[j] = asp[kb] * wsp[kb];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            if (kb0 + j < kb_hi)
-                acc = fma4(mfma_block(wf[j], af[j]), s[j], acc);
-        }
+    for (int i = 0; i < 4; ++i) {
+        a[i] = __builtin_amdgcn_update_dpp(v0[i], v1[i], 0x128, 0xF, 0xC, false);
+        b[i] = __builtin_amdgcn_update_dpp(v1[i], v0[i], 0x128, 0xF, 0x3, false);
     }
-
-    if constexpr (NW > 1) {
-        __shared__ v4f red[NW][64];
-        red[wave][lane] = acc;
-        __syncthreads();
-        if (wave != 0)
-            return;
-#pragma unroll
-        for (int w = 1; w < NW; ++w) {
-            const v4f o = red[w][lane];
-            acc[0] += o[0];
-            acc[1] += o[1];
-            acc[2] += o[2];
-            acc[3] += o[3];
-        }
-    }
-    if (mval)
-        store4(p.Y, (int64_t)r * N, n0 + 4 * g, N, vec_store != 0, acc);
+    return cat(a, b);
 }
 
+template <int TPW, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
+    const int n0 = (int)blockIdx.x * (16 * TPW);
+    const int r16 = lane & 15, g = lane >> 4;
+    const bool mval = r16 < M;
+
+    // Whole-line load addressing (see fix_row_layout): load h of a block takes
+    // row 8h + (r16 & 7), 16-byte chunk 2g + (r16 >> 3).  Loads go through
+    // buffer descriptors: a 32-bit per-lane offset (the host keeps N*K and
+    // M*K below 2^32) plus the wave-uniform block offset kb*128.
+    const int lrow = r16 & 7;
+    const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, (uint32_t)N * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
+    uint32_t woff[TPW][2];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            woff[t][h] = (uint32_t)min(n0 + 16 * t + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
+    // Activation rows past M load row 0: they only feed output columns that are never stored.
+    uint32_t aoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int m = 8 * h + lrow;
+        aoff[h] = (uint32_t)(m < M ? m : 0) * (uint32_t)K + lcol;
+    }
+    const float *asp = p.a_scale + (size_t)(mval ? r16 : 0) * KB;
+    // RG divides 128, so the row group lies in one 128-row weight block.
+    const float *wsp = p.w_scale + (size_t)(n0 >> 7) * KB;
+
+    v4f acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
+        v4i ar[D][2];
+        v4i wr[D][TPW][2];
+        float sa[D], sw[D];
+        // Issue every load of the pass before consuming any of them.
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int kb = min(kb_begin + j, KB - 1);   // blocks past the end load a valid block, skipped below
+            const int koff = kb * 128;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[t][h], koff, 2 /* nt */);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[h], koff, 0);
+            sa[j] = asp[kb];
+            sw[j] = wsp[kb];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            if (kb_begin + j < KB) {
+                const v8i af = fix_row_layout(ar[j][0], ar[j][1]);
+                const float sc = sa[j] * sw[j];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    acc[t] = fma4(mfma_block(fix_row_layout(wr[j][t][0], wr[j][t][1]), af), sc, acc[t]);
+            }
+        }
+    }
+
+    const bool vec = vec_store != 0;
+    if constexpr (NW > 1) {
+        __shared__ v4f red[NW][TPW][64];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            red[wave][t][lane] = acc[t];
+        __syncthreads();
+        for (int t = wave; t < TPW; t += NW) {
+            v4f v = red[0][t][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                const v4f o = red[w][t][lane];
+                v[0] += o[0];
+                v[1] += o[1];
+                v[2] += o[2];
+                v[3] += o[3];
+            }
+            if (mval)
+                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, v);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            if (mval)
+                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, acc[t]);
+    }
+}
 
 // Copy block kb of the A and W tiles into LDS stage `base` with direct-to-LDS
 // 16-byte loads: each wave instruction writes 1 KB (8 rows x 128 bytes) at
@@ -346,13 +411,14 @@ struct Entry {
     int lds_bytes;
 };
 
-#define SKINNY(NW) {{A8W8_KERNEL_SKINNY, 16, 16, NW, NW, 16, "skinny_w" #NW}, \
-                    reinterpret_cast<const void *>(&skinny_kernel<NW>), 0}
+#define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, "skinny_r" #TPW "_d" #D "_w" #NW}, \
+                            reinterpret_cast<const void *>(&skinny_kernel<TPW, D, NW>), 0}
 #define TILE(BM, BN) {{A8W8_KERNEL_TILE, BM, BN, 4, 1, 0, "tile_" #BM "x" #BN}, \
                        reinterpret_cast<const void *>(&tile_kernel<BM, BN>), 2 * (BM + BN) * 128}
 
 const Entry kEntries[] = {
-    SKINNY(4), SKINNY(8), SKINNY(16),
+    SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
+    SKINNY(1, 3, 16), SKINNY(2, 3, 16), SKINNY(1, 10, 4), SKINNY(1, 12, 4), SKINNY(1, 2, 4),
     TILE(256, 128), TILE(128, 128), TILE(128, 64), TILE(64, 128), TILE(64, 64),
     TILE(256, 32), TILE(128, 32), TILE(32, 128), TILE(32, 64), TILE(64, 32), TILE(32, 32),
 };
@@ -364,12 +430,22 @@ int num_variants() { return kNumEntries; }
 
 const Variant &variant(int id) { return kEntries[id].v; }
 
-int64_t variant_grid(int id, int64_t M, int64_t N)
+int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K)
 {
+    (void)K;
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_SKINNY)
-        return (N + 15) / 16;
+        return (N + v.bn - 1) / v.bn;
     return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+}
+
+int64_t variant_passes(int id, int64_t K)
+{
+    const Variant &v = kEntries[id].v;
+    if (v.kernel != A8W8_KERNEL_SKINNY)
+        return K / 128;
+    const int64_t per_pass = (int64_t)v.waves * v.kblocks;
+    return (K / 128 + per_pass - 1) / per_pass;
 }
 
 hipError_t set_kernel_attributes()
@@ -388,7 +464,7 @@ hipError_t set_kernel_attributes()
 hipError_t launch_variant(int id, const Args &a, hipStream_t stream)
 {
     const Entry &e = kEntries[id];
-    const int64_t grid = variant_grid(id, a.M, a.N);
+    const int64_t grid = variant_grid(id, a.M, a.N, a.K);
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;
     void *params[] = {&args, &vec};

@@ -27,9 +27,12 @@
  *   Y        bf16 (uint16 bit patterns) [M, N]            2-byte aligned; overwritten
  * Y must not overlap any input.
  *
- * Threading / asynchrony: calls only enqueue kernels on `stream` (a
- * hipStream_t; NULL = the null stream) and return; they never synchronise the
- * host, allocate, or issue memsets, so they may be captured into a HIP graph.
+ * Threading / asynchrony: calls only enqueue one kernel on `stream` (a
+ * hipStream_t of the current device; NULL = the null stream) and return; they
+ * never synchronise the host, allocate device memory or issue memsets, so they
+ * may be captured into a HIP graph.  Each output element is reduced in a fixed
+ * order inside one workgroup, so results are bitwise reproducible.  The first
+ * call on a device reads its properties (architecture, compute units) once.
  * Calls are re-entrant; the selector table is immutable.
  */
 #ifndef GEMM_A8W8_BLOCKSCALE_H
@@ -63,15 +66,15 @@ enum {
  * fields describe it (and the launch for the given shape) for logging and tests.
  */
 typedef struct {
-    int32_t kernel;     /* A8W8_KERNEL_*                                                */
-    int32_t variant;    /* index in [0, gemm_a8w8_num_variants())                       */
-    int32_t bm, bn;     /* output tile of one workgroup: rows of Y (M) x columns (N)    */
-    int32_t waves;      /* waves (64 lanes) per workgroup                               */
-    int32_t ksplit;     /* ways the K loop of one tile is split (across waves)          */
-    int64_t grid;       /* workgroups launched for this shape                           */
+    int32_t kernel;     /* A8W8_KERNEL_*                                                  */
+    int32_t variant;    /* index in [0, gemm_a8w8_num_variants())                         */
+    int32_t bm, bn;     /* output tile of one workgroup: rows of Y (M) x columns (N)      */
+    int32_t waves;      /* waves (64 lanes) per workgroup                                 */
+    int32_t kblocks;    /* 128-wide K blocks one wave loads at once (skinny); 1 for tile  */
+    int32_t kpasses;    /* passes over K per wave (skinny), K/128 steps (tile)            */
+    int32_t fallback;   /* 1: (N,K) has no tuned table, a heuristic plan was chosen       */
+    int64_t grid;       /* workgroups launched for this shape                             */
     int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
-    int32_t fallback;   /* 1: (N,K) has no tuned table, a heuristic plan was chosen     */
-    int32_t reserved;
 } a8w8_plan;
 
 /*

@@ -102,7 +102,7 @@ def sign_flip_copy(W: np.ndarray, seed: int) -> np.ndarray:
     memory.  Used to rotate weights so that each call reads them from HBM.
     """
     rng = np.random.default_rng(seed)
-    mask = rng.integers(0, 256, size=W.shape, dtype=np.uint8) & np.uint8(0x80)
+    mask = np.frombuffer(rng.bytes(W.size), dtype=np.uint8).reshape(W.shape) & np.uint8(0x80)
     return W ^ mask
 
 

@@ -87,7 +87,8 @@ def test_variant_shapes_are_launchable():
             assert 128 % (v["bn"] // 2) == 0, v          # a wave's columns stay in one weight block
             assert 2 * (v["bm"] + v["bn"]) * 128 <= 160 * 1024
         else:
-            assert v["bm"] == 16 and v["bn"] == 16
+            assert v["bm"] == 16 and v["bn"] in (16, 32, 64, 128), v   # row group inside one weight block
+            assert v["waves"] >= 1 and v["kblocks"] >= 1
 
 
 # ---------------------------------------------------------------- selector table
