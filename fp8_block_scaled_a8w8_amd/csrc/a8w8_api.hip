@@ -147,7 +147,7 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
         if (best >= 0)
             return best;
     }
-    static const int kTiles[][2] = {{256, 128}, {128, 128}, {128, 64}, {64, 64}, {32, 64}, {32, 32}};
+    static const int kTiles[][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}, {32, 64}, {32, 32}};
     const int nt = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
     for (int i = 0; i < nt; ++i) {
         const int bm = kTiles[i][0], bn = kTiles[i][1];

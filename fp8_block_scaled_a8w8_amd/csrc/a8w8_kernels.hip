@@ -30,6 +30,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+// Read-only global data read through the constant address space: wave-uniform
+// loads from it become scalar loads.
+typedef const __attribute__((address_space(4))) float const_f32;
 
 __device__ __forceinline__ v4f mfma_block(v8i w, v8i a)
 {
@@ -221,92 +224,154 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     }
 }
 
-// Copy block kb of the A and W tiles into LDS stage `base` with direct-to-LDS
-// 16-byte loads: each wave instruction writes 1 KB (8 rows x 128 bytes) at
-// consecutive LDS addresses, lane i at byte 16 i.
+// Copy block kb into one LDS stage with direct-to-LDS loads: A_LOADS + W_LOADS
+// 16-byte loads (each wave instruction writes 1 KB = 8 rows x 128 bytes at
+// consecutive LDS addresses, lane i at byte 16 i), then one 4-byte load of 64
+// activation-scale values (lane i -> float i).  Every wave issues exactly
+// A_LOADS + W_LOADS + 1 vector-memory instructions per block, which is what the
+// counted waits in the main loop rely on.
+//
+// The copies are written as inline asm on purpose: the compiler treats every
+// LDS read as possibly aliasing every copy still in flight and would wait for
+// all of them before the first fragment read, collapsing the ring to depth 1.
+// The asm has no register outputs (only the address and the LDS base, which
+// the hardware reads at issue), and the kernel's own counted waits below are
+// what order the copies against the reads.
+__device__ __forceinline__ void lds_copy16(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_copy4(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+}
+
 template <int A_LOADS, int W_LOADS>
 __device__ __forceinline__ void issue_tile_loads(const uint8_t *const (&a_src)[A_LOADS],
-                                                 const uint8_t *const (&w_src)[W_LOADS], int kb,
-                                                 uint8_t *base, int a_bytes, int wave)
+                                                 const uint8_t *const (&w_src)[W_LOADS], const float *as_src,
+                                                 int kb, uint8_t *stage, int a_bytes, int w_bytes, int wave)
 {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds(a_src[i] + (size_t)kb * 128,
-                                         (lds_ptr_t)(base + (wave * A_LOADS + i) * 1024), 16, 0, 0);
+        lds_copy16(a_src[i] + (size_t)kb * 128, stage + (wave * A_LOADS + i) * 1024);
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds(w_src[i] + (size_t)kb * 128,
-                                         (lds_ptr_t)(base + a_bytes + (wave * W_LOADS + i) * 1024), 16, 0, 0);
+        lds_copy16(w_src[i] + (size_t)kb * 128, stage + a_bytes + (wave * W_LOADS + i) * 1024);
+    lds_copy4(as_src + kb, stage + a_bytes + w_bytes + wave * 256);
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    // s_waitcnt immediate (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS tiles are row-major 128-byte rows whose 16-byte chunk c sits at chunk
+// position c ^ chunk_swizzle(row).  A fragment read has lane (g = l/16,
+// p = l%16) read chunk 2g (then 2g+1) of row r0 + p; with this swizzle those
+// 16-byte reads are free of LDS bank conflicts (measured with the LDS bank
+// conflict counter over candidate placements: plain r & 7 still costs 1.33
+// extra cycles per read).  Rows are 16-aligned in every read, so the pattern
+// only needs to be a bijection on each row.
+__device__ __forceinline__ int chunk_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 // MFMA operand of this lane: logical chunks 2g and 2g+1 (K bytes 32g..32g+31)
-// of tile row `row`, undoing the chunk ^ (row & 7) placement.
+// of tile row `row`.
 __device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
 {
     const uint8_t *rp = tile + row * 128;
-    const int x = row & 7;
+    const int x = chunk_swizzle(row);
     const v4i lo = *reinterpret_cast<const v4i *>(rp + (((2 * g) ^ x) << 4));
     const v4i hi = *reinterpret_cast<const v4i *>(rp + (((2 * g + 1) ^ x) << 4));
     return cat(lo, hi);
 }
 
-// ---------------------------------------------------------------------------
-// Tile kernel.  A workgroup of 4 waves (2 x 2) owns a BM x BN output tile and
-// walks K one 128-wide block at a time.  The A [BM x 128] and W [BN x 128]
-// fp8 tiles of block kb+1 are copied global -> LDS with direct-to-LDS 16-byte
-// loads (no VGPR staging) while block kb is multiplied from the other LDS
-// buffer.  Each wave owns a (BM/2) x (BN/2) sub-tile: per block it reads its W
-// and A fragments from LDS, takes one MFMA per 16 x 16 output, and folds the
-// result into the fp32 accumulator with the block's a_scale * w_scale.
-//
-// LDS layout of one tile: row-major 128-byte rows; the 16-byte chunk c of row
-// r is stored at chunk position c ^ (r & 7), so the 8 rows that a direct load
-// writes, and the 16 rows a fragment read touches, spread over the banks.
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void tile_kernel(Args p, int vec_store)
+// Tile index of workgroup `b` among T tiles: workgroups are dispatched to the
+// 8 XCDs round-robin (b % 8), so each XCD is given a contiguous range of tile
+// ids; inside it, tiles run in groups of G tile-rows, column by column, so the
+// workgroups that are resident together on one XCD share A rows and W rows in
+// that XCD's L2.  A bijection on [0, T): results do not depend on it.
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int G, int &tm, int &tn)
 {
-    constexpr int WM = BM / 2, WN = BN / 2;
+    const int T = tiles_m * tiles_n;
+    const int xcd = b & 7, local = b >> 3;
+    const int q = T >> 3, r = T & 7;
+    const int t = xcd * q + min(xcd, r) + local;
+    const int per_group = G * tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * G;
+    const int gsize = min(tiles_m - first_m, G);
+    const int in_group = t - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel.  A workgroup of WGM x WGN waves owns a BM x BN output tile and
+// walks K one 128-wide scale block at a time through a STAGES-deep ring of LDS
+// buffers: block kb+STAGES-1 is copied global -> LDS (direct-to-LDS loads, no
+// VGPR staging) while block kb is multiplied.  Each wave owns a
+// (BM/WGM) x (BN/WGN) sub-tile: per block it reads its W and A fragments from
+// LDS, takes one MFMA per 16 x 16 output, and folds the result into the fp32
+// accumulator with the block's a_scale * w_scale.  The MFMAs of 16-row slice
+// t+1 are issued before the scale FMAs of slice t consume slice t's results,
+// so the matrix core and the VALU work overlap.
+//
+// LDS stage: A tile [BM][128] | W tile [BN][128] | activation scales
+// [64 * waves] floats, tiles swizzled as described at chunk_swizzle().
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+__global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
+{
+    constexpr int NWAVES = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128, STAGE = A_BYTES + W_BYTES;
-    constexpr int A_LOADS = BM / 32, W_LOADS = BN / 32;   // 1 KB direct loads per wave per stage
-    static_assert(BM % 32 == 0 && BN % 32 == 0, "tile dims must be multiples of 32");
-    static_assert(WN <= 128, "a wave's columns must lie in one 128-row weight block");
+    constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
+    constexpr int STAGE = A_BYTES + W_BYTES + NWAVES * 256;
+    constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB loads per wave per block
+    constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
+    static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
+                  "each wave copies whole 8-row groups of both tiles");
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
+    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-row weight block");
+    static_assert(STAGES >= 2 && (STAGES - 2) * PER_BLOCK < 64, "ring depth");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int m0 = (int)(blockIdx.x / tiles_n) * BM;
-    const int n0 = (int)(blockIdx.x % tiles_n) * BN;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tmi, tni;
+    tile_coords((int)blockIdx.x, tiles_m, tiles_n, 4, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
     const int r16 = lane & 15, g = lane >> 4;
 
     // Direct-load sources: lane covers row (lane >> 3) of an 8-row group and
-    // physical chunk (lane & 7), which holds logical chunk (lane & 7) ^ row.
+    // physical chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row).
     const int lrow = lane >> 3, pch = lane & 7;
     const uint8_t *a_src[A_LOADS];
     const uint8_t *w_src[W_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
         const int row = (wave * A_LOADS + i) * 8 + lrow;
-        const int grow = min(m0 + row, M - 1);
-        a_src[i] = p.A + (size_t)grow * K + ((pch ^ lrow) << 4);
+        a_src[i] = p.A + (size_t)min(m0 + row, M - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i) {
         const int row = (wave * W_LOADS + i) * 8 + lrow;
-        const int grow = min(n0 + row, N - 1);
-        w_src[i] = p.W + (size_t)grow * K + ((pch ^ lrow) << 4);
+        w_src[i] = p.W + (size_t)min(n0 + row, N - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
     }
-
-    // Scales: one activation row per lane per 16-row slice; one weight block per wave.
-    int a_off[TM];
-#pragma unroll
-    for (int t = 0; t < TM; ++t)
-        a_off[t] = min(m0 + wm * WM + 16 * t + r16, M - 1) * KB;
+    // Activation scales: wave w copies tile rows 64w + lane (rows past the tile
+    // or past M repeat a valid row and are never read).
+    const float *as_src = p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB;
     const int NB = (N + 127) >> 7;
-    const float *wsp = p.w_scale + (size_t)min((n0 + wn * WN) >> 7, NB - 1) * KB;
+    const_f32 *wsp = (const_f32 *)(p.w_scale + (size_t)min((n0 + wn * WN) >> 7, NB - 1) * KB);
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -315,39 +380,33 @@ __global__ __launch_bounds__(256) void tile_kernel(Args p, int vec_store)
         for (int u = 0; u < TN; ++u)
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    float sa[TM];
-    float ws;
-    issue_tile_loads<A_LOADS, W_LOADS>(a_src, w_src, 0, smem, A_BYTES, wave);
+    // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat the last block).
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
-        sa[t] = p.a_scale[a_off[t]];
-    ws = wsp[0];
+    for (int s = 0; s < STAGES - 1; ++s)
+        issue_tile_loads<A_LOADS, W_LOADS>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
+                                           W_BYTES, wave);
+    float ws_next = wsp[0];
 
     for (int kb = 0; kb < KB; ++kb) {
+        const float ws = ws_next;
+        wait_vmcnt<(STAGES - 2) * PER_BLOCK>();   // this wave's copies of block kb have landed
+        __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
+        const int kn = min(kb + STAGES - 1, KB - 1);
+        issue_tile_loads<A_LOADS, W_LOADS>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
+                                           A_BYTES, W_BYTES, wave);
+        ws_next = wsp[min(kb + 1, KB - 1)];
+
+        const uint8_t *sA = smem + (kb % STAGES) * STAGE;
+        const uint8_t *sW = sA + A_BYTES;
+        const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
         float sc[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t)
-            sc[t] = sa[t] * ws;
-        __builtin_amdgcn_s_waitcnt(0);    // this wave's copies of block kb have landed
-        __syncthreads();                  // ... and every wave's; buffer (kb+1)&1 is free
-        // Prefetch block kb+1 (the last iteration re-fetches block KB-1 into the
-        // idle buffer, which keeps the loop body branch-free).
-        const int kn = min(kb + 1, KB - 1);
-        issue_tile_loads<A_LOADS, W_LOADS>(a_src, w_src, kn, smem + ((kb + 1) & 1) * STAGE, A_BYTES, wave);
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-            sa[t] = p.a_scale[a_off[t] + kn];
-        ws = wsp[kn];
-
-        const uint8_t *sA = smem + (kb & 1) * STAGE;
-        const uint8_t *sW = sA + A_BYTES;
+            sc[t] = sS[wm * WM + 16 * t + r16] * ws;
         v8i wf[TN];
 #pragma unroll
         for (int u = 0; u < TN; ++u)
             wf[u] = lds_fragment(sW, wn * WN + 16 * u + r16, g);
-        // Software pipeline over the 16-row activation slices: the MFMAs of
-        // slice t+1 are issued before the scale FMAs of slice t consume the
-        // results of slice t, so the matrix core never waits on the VALU.
         v4f d[2][TN];
         {
             const v8i af = lds_fragment(sA, wm * WM + r16, g);
@@ -368,7 +427,7 @@ __global__ __launch_bounds__(256) void tile_kernel(Args p, int vec_store)
                 acc[t][u] = fma4(d[t & 1][u], sc[t], acc[t][u]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);        // no copy into LDS may outlive the workgroup
+    wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
 
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
@@ -382,18 +441,21 @@ __global__ __launch_bounds__(256) void tile_kernel(Args p, int vec_store)
 }
 
 // Explicit instantiations (emit the host-side launch stubs).
-#define A8W8_TILE_INST(BM, BN) template __global__ void tile_kernel<BM, BN>(Args, int);
-A8W8_TILE_INST(256, 128)
-A8W8_TILE_INST(128, 128)
-A8W8_TILE_INST(128, 64)
-A8W8_TILE_INST(64, 128)
-A8W8_TILE_INST(64, 64)
-A8W8_TILE_INST(256, 32)
-A8W8_TILE_INST(128, 32)
-A8W8_TILE_INST(32, 128)
-A8W8_TILE_INST(32, 64)
-A8W8_TILE_INST(64, 32)
-A8W8_TILE_INST(32, 32)
+#define A8W8_TILE_INST(BM, BN, WGM, WGN, S) template __global__ void tile_kernel<BM, BN, WGM, WGN, S>(Args, int);
+A8W8_TILE_INST(256, 256, 2, 4, 2)
+A8W8_TILE_INST(256, 128, 2, 4, 3)
+A8W8_TILE_INST(128, 256, 2, 4, 3)
+A8W8_TILE_INST(128, 128, 2, 2, 2)
+A8W8_TILE_INST(128, 128, 2, 2, 4)
+A8W8_TILE_INST(128, 64, 2, 2, 3)
+A8W8_TILE_INST(64, 128, 2, 2, 3)
+A8W8_TILE_INST(64, 64, 2, 2, 3)
+A8W8_TILE_INST(256, 32, 4, 1, 3)
+A8W8_TILE_INST(128, 32, 4, 1, 3)
+A8W8_TILE_INST(32, 128, 1, 4, 3)
+A8W8_TILE_INST(32, 64, 2, 2, 3)
+A8W8_TILE_INST(64, 32, 2, 2, 3)
+A8W8_TILE_INST(32, 32, 2, 2, 3)
 #undef A8W8_TILE_INST
 
 }  // namespace kern
@@ -413,14 +475,18 @@ struct Entry {
 
 #define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, "skinny_r" #TPW "_d" #D "_w" #NW}, \
                             reinterpret_cast<const void *>(&skinny_kernel<TPW, D, NW>), 0}
-#define TILE(BM, BN) {{A8W8_KERNEL_TILE, BM, BN, 4, 1, 0, "tile_" #BM "x" #BN}, \
-                       reinterpret_cast<const void *>(&tile_kernel<BM, BN>), 2 * (BM + BN) * 128}
+#define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, \
+                                    "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
+                                   reinterpret_cast<const void *>(&tile_kernel<BM, BN, WGM, WGN, S>), \
+                                   S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
     SKINNY(1, 3, 16), SKINNY(2, 3, 16), SKINNY(1, 10, 4), SKINNY(1, 12, 4), SKINNY(1, 2, 4),
-    TILE(256, 128), TILE(128, 128), TILE(128, 64), TILE(64, 128), TILE(64, 64),
-    TILE(256, 32), TILE(128, 32), TILE(32, 128), TILE(32, 64), TILE(64, 32), TILE(32, 32),
+    TILE(256, 256, 2, 4, 2), TILE(256, 128, 2, 4, 3), TILE(128, 256, 2, 4, 3), TILE(128, 128, 2, 2, 2),
+    TILE(128, 128, 2, 2, 4), TILE(128, 64, 2, 2, 3), TILE(64, 128, 2, 2, 3), TILE(64, 64, 2, 2, 3),
+    TILE(256, 32, 4, 1, 3), TILE(128, 32, 4, 1, 3), TILE(32, 128, 1, 4, 3), TILE(32, 64, 2, 2, 3),
+    TILE(64, 32, 2, 2, 3), TILE(32, 32, 2, 2, 3),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 

@@ -110,7 +110,7 @@ def test_dense_m_sweep_sampled_rows(N, K):
 
 # ---------------------------------------------------------------- every compiled instance
 
-@pytest.mark.parametrize("variant", range(14))
+@pytest.mark.parametrize("variant", range(24))
 def test_every_instance_on_ragged_shape(variant):
     if variant >= g.gemm_a8w8_num_variants():
         pytest.skip("no such instance")
