@@ -348,7 +348,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tmi, tni;
-    tile_coords((int)blockIdx.x, tiles_m, tiles_n, 4, tmi, tni);
+    tile_coords((int)blockIdx.x, tiles_m, tiles_n, BM >= 256 ? 2 : 4, tmi, tni);
     const int m0 = tmi * BM, n0 = tni * BN;
     const int r16 = lane & 15, g = lane >> 4;
 
