@@ -49,6 +49,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def recorded_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "skinny_decode_qkv_traffic.md")
+    src = os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "csrc", "a8w8_kernels.hip")
+    try:
+        text = open(prof).read()
+        rec = json.loads(re.findall(r"```json\n(.*?)\n```", text, re.S)[-1])
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, IndexError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if rec.get("kernel_source_sha256_16") == cur else None
+
+
 def parity_gate(g, oracle, A, a_s, W_host, w_s, dA, da, dW, dw, Ms, what):
     """Compare GPU rows with the oracle; raise on mismatch (no perf without parity)."""
     import torch
@@ -118,6 +134,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", choices=["decode", "sweep"], default="decode",
+                    help="decode: the headline decode workload (default); sweep: dense-M sweep report")
+    ap.add_argument("--sweep-out", default=None, help="where the sweep writes its per-point table (markdown)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the run, copy 256 MiB device-to-device three times (traffic calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; the build runs on exactly one "
@@ -135,6 +156,9 @@ def main():
     props = torch.cuda.get_device_properties(0)
     if not props.gcnArchName.startswith("gfx950"):
         raise SystemExit(f"bench.py targets gfx950, found {props.gcnArchName}")
+
+    if args.workload == "sweep":
+        return sweep(args, torch, g, inputgen, oracle)
 
     # ------------------------------------------------------------ decode, cold W
     N, K = 14336, 5120
@@ -257,7 +281,7 @@ def main():
                    "calls_per_step": R, "rotate_bytes": R * w_bytes,
                    "table_hash": f"0x{g.gemm_a8w8_table_hash():016x}"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "skinny (M<=16) weight-streaming kernel",
                      "bytes_per_launch": round(bytes_mean)},
         "per_m": per_m,
@@ -266,7 +290,109 @@ def main():
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": cpu,
     }
+    if args.calib_copy:
+        calib_copy(torch)
     print(json.dumps(res), flush=True)
+
+
+def calib_copy(torch):
+    """A plain device copy of known size (reads and writes 256 MiB), for counter calibration."""
+    n = 256 * 2**20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: 3 x {n} bytes read and written")
+
+
+SWEEP_NK = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6144), (32, 6144)]
+
+
+def sweep(args, torch, g, inputgen, oracle):
+    """Dense arbitrary-M sweep: 256 seeded M in 1..8192 for each (N, K)."""
+    dev = "cuda:0"
+    Ms = inputgen.random_m_values(256, seed=2)
+    rng = np.random.default_rng(6)
+    points = []
+    fallbacks = 0
+    worst_ratio = 0.0
+    worst_rel = 0.0
+    t_start = time.time()
+    for (N, K) in SWEEP_NK:
+        A, a_s = inputgen.make_activations(8192, K, seed=0)
+        W0, w_s = inputgen.make_weights(N, K, seed=1)
+        dA = torch.from_numpy(A).to(dev)
+        da = torch.from_numpy(a_s).to(dev)
+        dw = torch.from_numpy(w_s).to(dev)
+        R = max(2, math.ceil(2**30 / (W0.nbytes + w_s.nbytes)))
+        copies = [torch.from_numpy(W0).to(dev)] + \
+            [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
+        picked = []
+        for M in Ms:
+            plan = g.gemm_a8w8_blockscale_plan(M, N, K)
+            fallbacks += plan["fallback"]
+            worst_ratio = max(worst_ratio, plan["key_m"] / M)
+            # long calls need no rotation to be cold: cap the graph at ~20 ms of work
+            fl = flops(M, N, K)
+            est_us = max(algorithmic_bytes(M, N, K) / 6e3, fl / 2e9)
+            Rp = max(2, min(R, int(20000 / max(est_us, 1.0))))
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            gr = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw, out=out))
+                                    for r in range(Rp)], 0, 1)
+            reps = max(2, int(5000 / (est_us * Rp)))
+            us = timed_replays(torch, gr, reps) * 1000.0 / Rp
+            del gr
+            # the graph's last call used a rotated copy: recompute with copy 0 for the parity check
+            g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[0], dw, out=out)
+            rows = sorted({M - 1, int(rng.integers(0, M))})
+            picked.append((M, rows, out[rows].float().cpu().numpy().astype(np.float64)))
+            by = algorithmic_bytes(M, N, K)
+            t_hbm = by / (HBM_PEAK_GBS * 1e3)          # us
+            t_mfma = fl / (FP8_PEAK_TFLOPS * 1e6)      # us
+            bound = "hbm" if t_hbm >= t_mfma else "mfma"
+            frac = max(t_hbm, t_mfma) / us
+            points.append({"N": N, "K": K, "M": M, "us": round(us, 3), "bound": bound,
+                           "frac": round(frac, 4), "plan": plan["name"], "key_m": plan["key_m"],
+                           "fallback": plan["fallback"]})
+        union = sorted({r for _, rows, _ in picked for r in rows})
+        ref = oracle.gemm(A, a_s, W0, w_s, rows=union)
+        pos = {r: i for i, r in enumerate(union)}
+        ys = np.concatenate([v for _, _, v in picked])
+        refs = np.concatenate([ref[[pos[r] for r in rows]] for _, rows, _ in picked])
+        rel = float(np.linalg.norm(ys - refs) / np.linalg.norm(refs))
+        worst_rel = max(worst_rel, rel)
+        if rel > 3e-3:
+            raise SystemExit(f"parity gate failed (sweep N={N} K={K}): rel_l2={rel:.3e}")
+        log(f"sweep N={N} K={K}: {len(Ms)} points, parity rel_l2 {rel:.3e}, "
+            f"median {np.median([p['frac'] for p in points if p['N'] == N]):.3f} of roofline")
+        del copies, dA
+        torch.cuda.empty_cache()
+    fr = np.array([p["frac"] for p in points])
+    summary = {
+        "metric": "dense-M sweep: fraction of the binding roofline per call (median over points)",
+        "value": round(float(np.median(fr)), 4), "unit": "fraction of roofline", "n_gpus": 1,
+        "higher_is_better": True, "data": "synthetic", "dtype": "fp8e4m3 x fp8e4m3 -> fp32 accumulate -> bf16",
+        "config": {"workload": "256 M values uniform in 1..8192 (seed 2) x (N,K) in " + str(SWEEP_NK),
+                   "table_hash": f"0x{g.gemm_a8w8_table_hash():016x}"},
+        "points": len(points), "fallbacks": fallbacks, "max_key_over_m": round(worst_ratio, 4),
+        "frac_p10": round(float(np.percentile(fr, 10)), 4), "frac_p90": round(float(np.percentile(fr, 90)), 4),
+        "parity_worst_rel_l2": round(worst_rel, 6), "seconds": round(time.time() - t_start, 1),
+    }
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write("# Dense-M sweep on one MI355X\n\n")
+            f.write("Command: `python bench.py --workload sweep --sweep-out <file>`\n\n")
+            f.write("```\n" + json.dumps(summary) + "\n```\n\n")
+            for (N, K) in SWEEP_NK:
+                sub = [p for p in points if p["N"] == N and p["K"] == K]
+                f.write(f"## N={N}, K={K}\n\n| M | key M | plan | µs/call | bound | % of roofline |\n"
+                        "|---:|---:|---|---:|---|---:|\n")
+                for p in sorted(sub, key=lambda p: p["M"]):
+                    f.write(f"| {p['M']} | {p['key_m']} | {p['plan']} | {p['us']} | {p['bound']} | "
+                            f"{100 * p['frac']:.1f} |\n")
+                f.write("\n")
+    print(json.dumps(summary), flush=True)
 
 
 if __name__ == "__main__":
