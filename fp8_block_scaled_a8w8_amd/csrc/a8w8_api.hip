@@ -34,6 +34,8 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// The tile kernel addresses a tile's rows with 32-bit offsets: 256 * K < 2^31.
+constexpr int64_t kMaxK = (int64_t)1 << 22;
 
 // Per-device state: 0 = not yet checked, 1 = gfx950 ready, 2 = unsupported.
 std::atomic<int> g_dev_state[kMaxDevices];
@@ -74,7 +76,7 @@ int check_shape(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 1 || K < 1 || (K % 128) != 0)
         return A8W8_ERR_SHAPE;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    if (M > kMaxDim || N > kMaxDim || K > kMaxK)
         return A8W8_ERR_SHAPE;
     // Row offsets into the scale arrays are 32-bit inside the kernels.
     if (M * (K / 128) >= ((int64_t)1 << 31) || ((N + 127) / 128) * (K / 128) >= ((int64_t)1 << 31))
@@ -329,7 +331,7 @@ const char *gemm_a8w8_status_string(int status)
     switch (status) {
     case A8W8_OK: return "ok";
     case A8W8_ERR_NULL: return "a required pointer is NULL";
-    case A8W8_ERR_SHAPE: return "invalid shape (need M >= 0, N >= 1, K >= 1, K % 128 == 0, dims <= 2^30)";
+    case A8W8_ERR_SHAPE: return "invalid shape (need M >= 0, N >= 1, K >= 1, K % 128 == 0, M, N <= 2^30, K <= 2^22)";
     case A8W8_ERR_ALIGN: return "misaligned buffer (A and W need 16 bytes, scales 4, Y 2)";
     case A8W8_ERR_ARCH: return "the current device is not gfx950 (MI355X)";
     case A8W8_ERR_HIP: return "HIP runtime call or kernel launch failed";

@@ -224,43 +224,74 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     }
 }
 
-// Copy block kb into one LDS stage with direct-to-LDS loads: A_LOADS + W_LOADS
-// 16-byte loads (each wave instruction writes 1 KB = 8 rows x 128 bytes at
-// consecutive LDS addresses, lane i at byte 16 i), then one 4-byte load of 64
-// activation-scale values (lane i -> float i).  Every wave issues exactly
-// A_LOADS + W_LOADS + 1 vector-memory instructions per block, which is what the
-// counted waits in the main loop rely on.
+// Direct global -> LDS copies.  Each wave instruction moves one value per lane
+// and writes them to consecutive LDS addresses starting at the wave-uniform
+// address in m0 (lane i at byte 16 i for the 16-byte form, 4 i for the 4-byte
+// form), so one 16-byte copy fills 1 KB of LDS = 8 tile rows of 128 bytes.
 //
 // The copies are written as inline asm on purpose: the compiler treats every
 // LDS read as possibly aliasing every copy still in flight and would wait for
 // all of them before the first fragment read, collapsing the ring to depth 1.
-// The asm has no register outputs (only the address and the LDS base, which
-// the hardware reads at issue), and the kernel's own counted waits below are
-// what order the copies against the reads.
-__device__ __forceinline__ void lds_copy16(const void *src, const void *lds_dst)
+// The asm has no register outputs (only the addresses, which the hardware reads
+// at issue), and the kernel's own counted waits order the copies against the
+// reads.  The 16-byte form addresses global memory as a wave-uniform 64-bit
+// base (SGPR pair) plus a 32-bit per-lane offset.
+__device__ __forceinline__ void lds_copy16(const uint8_t *sbase, uint32_t voff, uint32_t lds_addr)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 
-__device__ __forceinline__ void lds_copy4(const void *src, const void *lds_dst)
+__device__ __forceinline__ void lds_copy4(const float *src, uint32_t lds_addr)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(src) : "memory", "m0");
 }
 
-template <int A_LOADS, int W_LOADS>
-__device__ __forceinline__ void issue_tile_loads(const uint8_t *const (&a_src)[A_LOADS],
-                                                 const uint8_t *const (&w_src)[W_LOADS], const float *as_src,
-                                                 int kb, uint8_t *stage, int a_bytes, int w_bytes, int wave)
+// Wave-uniform 64-bit pointer forced into scalar registers.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
 {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t *>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+// Issue the copies of K block kb into the LDS stage at byte address `stage`:
+// A_LOADS 16-byte copies of activation rows, W_LOADS of weight rows, and one
+// 4-byte copy of scale values (see tile_kernel for the stage layout).  Every
+// wave issues exactly A_LOADS + W_LOADS + 1 vector-memory instructions per
+// block, which is what the counted waits in the main loop rely on.
+template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES>
+__device__ __forceinline__ void issue_tile_loads(const uint8_t *a_tile, const uint8_t *w_tile,
+                                                 const uint32_t (&a_off)[A_LOADS], const uint32_t (&w_off)[W_LOADS],
+                                                 const float *s_src, int kb, uint32_t stage, int wave)
+{
+    const uint8_t *ab = uniform_ptr(a_tile + (size_t)kb * 128);
+    const uint8_t *wb = uniform_ptr(w_tile + (size_t)kb * 128);
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-        lds_copy16(a_src[i] + (size_t)kb * 128, stage + (wave * A_LOADS + i) * 1024);
+        lds_copy16(ab, a_off[i], stage + (uint32_t)(wave * A_LOADS + i) * 1024u);
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i)
-        lds_copy16(w_src[i] + (size_t)kb * 128, stage + a_bytes + (wave * W_LOADS + i) * 1024);
-    lds_copy4(as_src + kb, stage + a_bytes + w_bytes + wave * 256);
+        lds_copy16(wb, w_off[i], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + i) * 1024));
+    lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
+}
+
+// Copy number j (0 <= j < A_LOADS + W_LOADS + 1) of one block, in the order
+// issue_tile_loads uses; ab and wb already include the block's K offset.
+template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES>
+__device__ __forceinline__ void issue_one(int j, const uint8_t *ab, const uint8_t *wb,
+                                          const uint32_t (&a_off)[A_LOADS], const uint32_t (&w_off)[W_LOADS],
+                                          const float *s_src, int kb, uint32_t stage, int wave)
+{
+    if (j < A_LOADS)
+        lds_copy16(ab, a_off[j], stage + (uint32_t)(wave * A_LOADS + j) * 1024u);
+    else if (j < A_LOADS + W_LOADS)
+        lds_copy16(wb, w_off[j - A_LOADS], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + j - A_LOADS) * 1024));
+    else
+        lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -315,16 +346,32 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 // ---------------------------------------------------------------------------
 // Tile kernel.  A workgroup of WGM x WGN waves owns a BM x BN output tile and
 // walks K one 128-wide scale block at a time through a STAGES-deep ring of LDS
-// buffers: block kb+STAGES-1 is copied global -> LDS (direct-to-LDS loads, no
-// VGPR staging) while block kb is multiplied.  Each wave owns a
-// (BM/WGM) x (BN/WGN) sub-tile: per block it reads its W and A fragments from
-// LDS, takes one MFMA per 16 x 16 output, and folds the result into the fp32
-// accumulator with the block's a_scale * w_scale.  The MFMAs of 16-row slice
-// t+1 are issued before the scale FMAs of slice t consume slice t's results,
-// so the matrix core and the VALU work overlap.
+// buffers filled by direct global -> LDS copies (no VGPR staging).  Each wave
+// owns a (BM/WGM) x (BN/WGN) sub-tile: TM 16-row activation slices times TN
+// 16-row weight fragments, one MFMA each per block.
 //
-// LDS stage: A tile [BM][128] | W tile [BN][128] | activation scales
-// [64 * waves] floats, tiles swizzled as described at chunk_swizzle().
+// Per block and wave, slice t does: issue a share of the copies of block
+// kb+STAGES-1 (spread over the first slices so that no wave stalls behind a
+// burst of copies), read the activation fragment of slice t+1, issue the TN
+// MFMAs of slice t, and apply a_scale * w_scale to the results of slice t-1
+// with one FMA per output.  The results of a block's last slice are scaled at
+// the start of the next block.
+//
+// The one workgroup barrier per block sits at the start of the last slice.
+// Before it every wave waits for its own copies of block kb+1; after it those
+// copies are visible to all waves, and every wave has finished reading the
+// stage of block kb (its last fragment read happens before the barrier), so
+// the stage is free for the copies the next block issues.  Right after the
+// barrier each wave issues the last slice's MFMAs from registers and then
+// reads block kb+1's weight fragments, first activation fragment and scales,
+// so the LDS latency at a block boundary hides under that slice's work.
+//
+// LDS stage: A tile [BM][128] | W tile [BN][128] | scales [64 * waves] floats.
+// Scale slot s < BM holds a_scale of tile row s; slot BM + j holds w_scale of
+// the tile's j-th 128-row weight block.  Tiles are swizzled as described at
+// chunk_swizzle().
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
 template <int BM, int BN, int WGM, int WGN, int STAGES>
 __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
 {
@@ -333,13 +380,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     constexpr int TM = WM / 16, TN = WN / 16;
     constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
     constexpr int STAGE = A_BYTES + W_BYTES + NWAVES * 256;
-    constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB loads per wave per block
+    constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB copies per wave per block
     constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
+    constexpr int NBW = (BN + 127) / 128;                                    // weight blocks a tile spans
+    // Copies of a block go out CPS per slice over its first SPREAD slices.
+    // With two stages they fetch the next block and must all be issued before
+    // the last slice's barrier.
+    constexpr int SPREAD = STAGES == 2 ? cmin(TM - 1, 6) : cmin(TM, 6);
+    constexpr int CPS = SPREAD > 0 ? (PER_BLOCK + SPREAD - 1) / SPREAD : PER_BLOCK;
+    constexpr int C_BEFORE = cmin(PER_BLOCK, cmin(SPREAD, TM - 1) * CPS);   // issued before the barrier
+    // Copies a wave may still have in flight at the barrier of block kb: all
+    // of those issued after block kb+1's.
+    constexpr int VM_AT_BARRIER = (STAGES - 3) * PER_BLOCK + C_BEFORE;
     static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
                   "each wave copies whole 8-row groups of both tiles");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-row weight block");
-    static_assert(STAGES >= 2 && (STAGES - 2) * PER_BLOCK < 64, "ring depth");
+    static_assert(BN <= 128 ? 128 % BN == 0 : BN % 128 == 0, "tiles start on weight-block boundaries");
+    static_assert(BM + NBW <= NWAVES * 64, "scale slots");
+    static_assert(STAGES >= 2 && SPREAD >= 1 && SPREAD * CPS >= PER_BLOCK, "copy schedule");
+    static_assert(STAGES > 2 || C_BEFORE == PER_BLOCK, "two stages: next block's copies precede the barrier");
+    static_assert(VM_AT_BARRIER >= 0 && VM_AT_BARRIER < 64 && (STAGES - 2) * PER_BLOCK < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
@@ -352,26 +413,32 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     const int m0 = tmi * BM, n0 = tni * BN;
     const int r16 = lane & 15, g = lane >> 4;
 
-    // Direct-load sources: lane covers row (lane >> 3) of an 8-row group and
-    // physical chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row).
+    // Copy sources: lane covers row (lane >> 3) of an 8-row group and physical
+    // chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row).
+    // Offsets are relative to the tile's first row (rows past M or N repeat the
+    // last valid row; their outputs are never stored) and fit in 32 bits
+    // because the host keeps 256 * K below 2^31.
     const int lrow = lane >> 3, pch = lane & 7;
-    const uint8_t *a_src[A_LOADS];
-    const uint8_t *w_src[W_LOADS];
+    const uint8_t *a_tile = p.A + (size_t)m0 * K;
+    const uint8_t *w_tile = p.W + (size_t)n0 * K;
+    uint32_t a_off[A_LOADS], w_off[W_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
         const int row = (wave * A_LOADS + i) * 8 + lrow;
-        a_src[i] = p.A + (size_t)min(m0 + row, M - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
+        a_off[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i) {
         const int row = (wave * W_LOADS + i) * 8 + lrow;
-        w_src[i] = p.W + (size_t)min(n0 + row, N - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
+        w_off[i] = (uint32_t)(min(n0 + row, N - 1) - n0) * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
     }
-    // Activation scales: wave w copies tile rows 64w + lane (rows past the tile
-    // or past M repeat a valid row and are never read).
-    const float *as_src = p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB;
-    const int NB = (N + 127) >> 7;
-    const_f32 *wsp = (const_f32 *)(p.w_scale + (size_t)min((n0 + wn * WN) >> 7, NB - 1) * KB);
+    const int NB = (N + 127) >> 7, nb0 = n0 >> 7;
+    const int slot = wave * 64 + lane;
+    const float *s_src = slot < BM ? p.a_scale + (size_t)min(m0 + slot, M - 1) * KB
+                                   : p.w_scale + (size_t)min(nb0 + slot - BM, NB - 1) * KB;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    const int ws_slot = BM + ((n0 + wn * WN) >> 7) - nb0;
+    const int arow = wm * WM + r16, wrow = wn * WN + r16;
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -380,53 +447,107 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         for (int u = 0; u < TN; ++u)
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat the last block).
+    // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat
+    // the last block), then the fragments of block 0.
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-        issue_tile_loads<A_LOADS, W_LOADS>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
-                                           W_BYTES, wave);
-    float ws_next = wsp[0];
+        issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(a_tile, w_tile, a_off, w_off, s_src, min(s, KB - 1),
+                                                            lds0 + (uint32_t)(s * STAGE), wave);
+    wait_vmcnt<(STAGES - 2) * PER_BLOCK>();
+    __syncthreads();
+    v8i wf[TN], af;
+    float sa[TM], ws;
+    {
+        const uint8_t *sA = smem, *sW = smem + A_BYTES;
+        const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
+        wf[0] = lds_fragment(sW, wrow, g);
+        af = lds_fragment(sA, arow, g);
+#pragma unroll
+        for (int u = 1; u < TN; ++u)
+            wf[u] = lds_fragment(sW, wrow + 16 * u, g);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            sa[t] = sS[arow + 16 * t];
+        ws = sS[ws_slot];
+    }
+
+    // Last slice of the previous block, scaled at the start of the next one
+    // (zero before the first block: adds exactly +0).
+    v4f d_last[TN];
+#pragma unroll
+    for (int u = 0; u < TN; ++u)
+        d_last[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+    float s_last = 0.f;
 
     for (int kb = 0; kb < KB; ++kb) {
-        const float ws = ws_next;
-        wait_vmcnt<(STAGES - 2) * PER_BLOCK>();   // this wave's copies of block kb have landed
-        __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
-        const int kn = min(kb + STAGES - 1, KB - 1);
-        issue_tile_loads<A_LOADS, W_LOADS>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
-                                           A_BYTES, W_BYTES, wave);
-        ws_next = wsp[min(kb + 1, KB - 1)];
-
         const uint8_t *sA = smem + (kb % STAGES) * STAGE;
-        const uint8_t *sW = sA + A_BYTES;
-        const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
+        const int kc = min(kb + STAGES - 1, KB - 1);   // block fetched by this block's copies
+        const uint32_t cstage = lds0 + (uint32_t)(((kb + STAGES - 1) % STAGES) * STAGE);
+        const uint8_t *ab = uniform_ptr(a_tile + (size_t)kc * 128);
+        const uint8_t *wb = uniform_ptr(w_tile + (size_t)kc * 128);
         float sc[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t)
-            sc[t] = sS[wm * WM + 16 * t + r16] * ws;
-        v8i wf[TN];
+            sc[t] = sa[t] * ws;
 #pragma unroll
         for (int u = 0; u < TN; ++u)
-            wf[u] = lds_fragment(sW, wn * WN + 16 * u + r16, g);
-        v4f d[2][TN];
-        {
-            const v8i af = lds_fragment(sA, wm * WM + r16, g);
-#pragma unroll
-            for (int u = 0; u < TN; ++u)
-                d[0][u] = mfma_block(wf[u], af);
-        }
+            acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
+
+        v4f d[TN];
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            if (t + 1 < TM) {
-                const v8i af = lds_fragment(sA, wm * WM + 16 * (t + 1) + r16, g);
+            if (t == TM - 1) {
+                wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of block kb+1 have landed
+                __syncthreads();               // ... every wave's; stage kb % STAGES is read out
+            }
+            if (t < SPREAD) {
+#pragma unroll
+                for (int j = t * CPS; j < (t + 1) * CPS && j < PER_BLOCK; ++j)
+                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ab, wb, a_off, w_off, s_src, kc, cstage, wave);
+            }
+            v8i af_next = af;
+            if (t + 1 < TM)
+                af_next = lds_fragment(sA, arow + 16 * (t + 1), g);
+            v4f dn[TN];
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                dn[u] = mfma_block(wf[u], af);
+            if (t == TM - 1) {
+                // Block kb+1: its stage is complete (barrier above); these reads
+                // overwrite fragments the MFMAs just issued have already read.
+                // After the last block they read a stale stage and are unused.
+                __builtin_amdgcn_sched_barrier(0);
+                const uint8_t *nA = smem + ((kb + 1) % STAGES) * STAGE, *nW = nA + A_BYTES;
+                const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
+                wf[0] = lds_fragment(nW, wrow, g);
+                af_next = lds_fragment(nA, arow, g);
+#pragma unroll
+                for (int u = 1; u < TN; ++u)
+                    wf[u] = lds_fragment(nW, wrow + 16 * u, g);
+#pragma unroll
+                for (int s = 0; s < TM; ++s)
+                    sa[s] = nS[arow + 16 * s];
+                ws = nS[ws_slot];
+            }
+            if (t > 0) {
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    d[(t + 1) & 1][u] = mfma_block(wf[u], af);
+                    acc[t - 1][u] = fma4(d[u], sc[t - 1], acc[t - 1][u]);
             }
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                acc[t][u] = fma4(d[t & 1][u], sc[t], acc[t][u]);
+                d[u] = dn[u];
+            af = af_next;
+            __builtin_amdgcn_sched_barrier(0);   // keep each slice's work together
         }
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+            d_last[u] = d[u];
+        s_last = sc[TM - 1];
     }
+#pragma unroll
+    for (int u = 0; u < TN; ++u)
+        acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
     wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
 
 #pragma unroll
@@ -450,7 +571,6 @@ A8W8_TILE_INST(128, 128, 2, 2, 4)
 A8W8_TILE_INST(128, 64, 2, 2, 3)
 A8W8_TILE_INST(64, 128, 2, 2, 3)
 A8W8_TILE_INST(64, 64, 2, 2, 3)
-A8W8_TILE_INST(256, 32, 4, 1, 3)
 A8W8_TILE_INST(128, 32, 4, 1, 3)
 A8W8_TILE_INST(32, 128, 1, 4, 3)
 A8W8_TILE_INST(32, 64, 2, 2, 3)
@@ -485,7 +605,7 @@ const Entry kEntries[] = {
     SKINNY(1, 3, 16), SKINNY(2, 3, 16), SKINNY(1, 10, 4), SKINNY(1, 12, 4), SKINNY(1, 2, 4),
     TILE(256, 256, 2, 4, 2), TILE(256, 128, 2, 4, 3), TILE(128, 256, 2, 4, 3), TILE(128, 128, 2, 2, 2),
     TILE(128, 128, 2, 2, 4), TILE(128, 64, 2, 2, 3), TILE(64, 128, 2, 2, 3), TILE(64, 64, 2, 2, 3),
-    TILE(256, 32, 4, 1, 3), TILE(128, 32, 4, 1, 3), TILE(32, 128, 1, 4, 3), TILE(32, 64, 2, 2, 3),
+    TILE(128, 32, 4, 1, 3), TILE(32, 128, 1, 4, 3), TILE(32, 64, 2, 2, 3),
     TILE(64, 32, 2, 2, 3), TILE(32, 32, 2, 2, 3),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);

@@ -48,7 +48,7 @@ extern "C" {
 enum {
     A8W8_OK = 0,
     A8W8_ERR_NULL = 1,    /* a required pointer is NULL                          */
-    A8W8_ERR_SHAPE = 2,   /* M < 0, N < 1, K < 1, K % 128 != 0, or a dimension too large */
+    A8W8_ERR_SHAPE = 2,   /* M < 0, N < 1, K < 1, K % 128 != 0, M or N > 2^30, K > 2^22 */
     A8W8_ERR_ALIGN = 3,   /* A or W not 16-byte aligned, a scale or Y not 4-byte aligned */
     A8W8_ERR_ARCH = 4,    /* the current device is not gfx950                    */
     A8W8_ERR_HIP = 5,     /* a HIP runtime call or kernel launch failed          */

@@ -41,7 +41,7 @@ def _call(A=16, a_s=16, W=16, w_s=16, Y=16, M=4, N=512, K=1024):
 
 
 @pytest.mark.parametrize("M,N,K", [(-1, 512, 1024), (4, 0, 1024), (4, 512, 0), (4, 512, 1000),
-                                   (4, 512, 127), (1 << 31, 512, 1024)])
+                                   (4, 512, 127), (1 << 31, 512, 1024), (4, 512, (1 << 22) + 128)])
 def test_bad_shapes(M, N, K):
     assert _call(M=M, N=N, K=K) == g.A8W8_ERR_SHAPE
     p = g.Plan()
