@@ -194,7 +194,7 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus)
     return {heuristic_variant(M, N, K, cus), M, 1};
 }
 
-void fill_plan(int id, int64_t M, int64_t N, int64_t K, int64_t key_m, int fallback, a8w8_plan *out)
+void fill_plan(int id, int64_t M, int64_t N, int64_t K, int cus, int64_t key_m, int fallback, a8w8_plan *out)
 {
     const Variant &v = a8w8::variant(id);
     std::memset(out, 0, sizeof(*out));
@@ -205,7 +205,7 @@ void fill_plan(int id, int64_t M, int64_t N, int64_t K, int64_t key_m, int fallb
     out->waves = v.waves;
     out->kblocks = v.kblocks;
     out->kpasses = (int32_t)a8w8::variant_passes(id, K);
-    out->grid = M > 0 ? a8w8::variant_grid(id, M, N, K) : 0;
+    out->grid = M > 0 ? a8w8::variant_grid(id, M, N, K, cus) : 0;
     out->key_m = key_m;
     out->fallback = fallback;
 }
@@ -229,7 +229,7 @@ void log_plan(int64_t M, int64_t N, int64_t K, int id, int64_t key_m, int fallba
 }
 
 int launch(int id, const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
-           int64_t M, int64_t N, int64_t K, void *stream)
+           int64_t M, int64_t N, int64_t K, int cus, void *stream)
 {
     Args a;
     a.A = static_cast<const uint8_t *>(A);
@@ -240,7 +240,7 @@ int launch(int id, const void *A, const float *a_scale, const void *W, const flo
     a.M = (int32_t)M;
     a.N = (int32_t)N;
     a.K = (int32_t)K;
-    if (a8w8::launch_variant(id, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (a8w8::launch_variant(id, a, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
         return A8W8_ERR_HIP;
     return A8W8_OK;
 }
@@ -266,7 +266,7 @@ int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, con
         return rc;
     const Choice c = select_variant(M, N, K, cus);
     log_plan(M, N, K, c.variant, c.key_m, c.fallback);
-    return launch(c.variant, A, a_scale, W, w_scale, Y, M, N, K, stream);
+    return launch(c.variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream);
 }
 
 int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
@@ -278,7 +278,7 @@ int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count,
         return rc;
     const int cus = cu_count > 0 ? cu_count : 256;
     const Choice c = select_variant(M > 0 ? M : 1, N, K, cus);
-    fill_plan(c.variant, M, N, K, c.key_m, c.fallback, out);
+    fill_plan(c.variant, M, N, K, cus, c.key_m, c.fallback, out);
     return A8W8_OK;
 }
 
@@ -292,7 +292,7 @@ int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
         return A8W8_ERR_PLAN;
     if (M < 0 || N < 1 || K < 1)
         return A8W8_ERR_SHAPE;
-    fill_plan(variant, M, N, K, M, 0, out);
+    fill_plan(variant, M, N, K, 256, M, 0, out);
     return A8W8_OK;
 }
 
@@ -316,7 +316,7 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant, const void *A, const float
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    return launch(variant, A, a_scale, W, w_scale, Y, M, N, K, stream);
+    return launch(variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream);
 }
 
 const char *gemm_a8w8_variant_name(int32_t variant)

@@ -11,8 +11,9 @@ struct Variant {
     int32_t kernel;    // A8W8_KERNEL_SKINNY or A8W8_KERNEL_TILE
     int32_t bm, bn;    // output tile per workgroup (skinny: 16 x 16 * tiles per wave)
     int32_t waves;     // waves per workgroup
-    int32_t kblocks;   // K blocks each wave loads (skinny), 1 for the tile kernel
+    int32_t kblocks;   // K blocks each wave loads (skinny), LDS ring depth (tile)
     int32_t max_m;     // largest M the instance accepts (skinny: 16), 0 = any
+    int32_t per_cu;    // tile: workgroups per CU the persistent grid is sized for
     const char *name;
 };
 
@@ -28,14 +29,16 @@ struct Args {
 
 int num_variants();
 const Variant &variant(int id);
-// Workgroups the instance launches for (M, N, K), and the passes over K one
-// wave makes (skinny: ceil(K/128 / (waves * kblocks)); tile: K/128 blocks).
-int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K);
+// Workgroups the instance launches for (M, N, K) on a device with `cus`
+// compute units (tile: min(tiles, cus * per_cu), each workgroup looping over
+// its share of the tiles), and the passes over K one wave makes (skinny:
+// ceil(K/128 / (waves * kblocks)); tile: K/128 blocks per tile).
+int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus);
 int64_t variant_passes(int id, int64_t K);
 // Raise the dynamic-LDS limit of the instances that need more than 64 KB
 // (once per device, with that device current).
 hipError_t set_kernel_attributes();
 // Enqueue the instance; returns hipSuccess or the launch error.
-hipError_t launch_variant(int id, const Args &a, hipStream_t stream);
+hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream);
 
 }  // namespace a8w8

@@ -234,13 +234,16 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 // all of them before the first fragment read, collapsing the ring to depth 1.
 // The asm has no register outputs (only the addresses, which the hardware reads
 // at issue), and the kernel's own counted waits order the copies against the
-// reads.  The 16-byte form addresses global memory as a wave-uniform 64-bit
-// base (SGPR pair) plus a 32-bit per-lane offset.
-__device__ __forceinline__ void lds_copy16(const uint8_t *sbase, uint32_t voff, uint32_t lds_addr)
+// reads.
+//
+// The 16-byte form reads through a buffer descriptor (see tile_rsrc) at a
+// 32-bit per-lane offset: lanes past the descriptor's range fetch zeros
+// instead of faulting, which is how rows past M or N are handled.
+__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voff), "s"(sbase)
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
 }
 
@@ -249,47 +252,50 @@ __device__ __forceinline__ void lds_copy4(const float *src, uint32_t lds_addr)
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(src) : "memory", "m0");
 }
 
-// Wave-uniform 64-bit pointer forced into scalar registers.
-__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
+// Raw buffer descriptor (stride 0, 32-bit data format) over `bytes` bytes at
+// `base`, built in scalar registers.
+__device__ __forceinline__ v4i tile_rsrc(const uint8_t *base, uint32_t bytes)
 {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const uint8_t *>((uintptr_t)(((uint64_t)hi << 32) | lo));
+    const uint64_t v = (uint64_t)(uintptr_t)base;
+    v4i r;
+    r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32) & 0xFFFFu);
+    r[2] = (int)__builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000;
+    return r;
 }
 
-// Issue the copies of K block kb into the LDS stage at byte address `stage`:
-// A_LOADS 16-byte copies of activation rows, W_LOADS of weight rows, and one
-// 4-byte copy of scale values (see tile_kernel for the stage layout).  Every
-// wave issues exactly A_LOADS + W_LOADS + 1 vector-memory instructions per
-// block, which is what the counted waits in the main loop rely on.
+// Issue the copies of one K block into the LDS stage at byte address `stage`:
+// A_LOADS 16-byte copies of activation rows, W_LOADS of weight rows (ra and rw
+// describe the block's tile rows, see tile_kernel), and one 4-byte copy of
+// scale values.  Every wave issues exactly A_LOADS + W_LOADS + 1
+// vector-memory instructions per block, which is what the counted waits in
+// the main loop rely on.
 template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES>
-__device__ __forceinline__ void issue_tile_loads(const uint8_t *a_tile, const uint8_t *w_tile,
-                                                 const uint32_t (&a_off)[A_LOADS], const uint32_t (&w_off)[W_LOADS],
-                                                 const float *s_src, int kb, uint32_t stage, int wave)
+__device__ __forceinline__ void issue_tile_loads(v4i ra, v4i rw, const uint32_t (&a_off)[A_LOADS],
+                                                 const uint32_t (&w_off)[W_LOADS], const float *s_src, int kb,
+                                                 uint32_t stage, int wave)
 {
-    const uint8_t *ab = uniform_ptr(a_tile + (size_t)kb * 128);
-    const uint8_t *wb = uniform_ptr(w_tile + (size_t)kb * 128);
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-        lds_copy16(ab, a_off[i], stage + (uint32_t)(wave * A_LOADS + i) * 1024u);
+        lds_copy16(ra, a_off[i], stage + (uint32_t)(wave * A_LOADS + i) * 1024u);
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i)
-        lds_copy16(wb, w_off[i], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + i) * 1024));
+        lds_copy16(rw, w_off[i], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + i) * 1024));
     lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
 }
 
 // Copy number j (0 <= j < A_LOADS + W_LOADS + 1) of one block, in the order
-// issue_tile_loads uses; ab and wb already include the block's K offset.
+// issue_tile_loads uses.
 template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES>
-__device__ __forceinline__ void issue_one(int j, const uint8_t *ab, const uint8_t *wb,
-                                          const uint32_t (&a_off)[A_LOADS], const uint32_t (&w_off)[W_LOADS],
-                                          const float *s_src, int kb, uint32_t stage, int wave)
+__device__ __forceinline__ void issue_one(int j, v4i ra, v4i rw, const uint32_t (&a_off)[A_LOADS],
+                                          const uint32_t (&w_off)[W_LOADS], const float *s_src, int kb,
+                                          uint32_t stage, int wave)
 {
     if (j < A_LOADS)
-        lds_copy16(ab, a_off[j], stage + (uint32_t)(wave * A_LOADS + j) * 1024u);
+        lds_copy16(ra, a_off[j], stage + (uint32_t)(wave * A_LOADS + j) * 1024u);
     else if (j < A_LOADS + W_LOADS)
-        lds_copy16(wb, w_off[j - A_LOADS], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + j - A_LOADS) * 1024));
+        lds_copy16(rw, w_off[j - A_LOADS], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + j - A_LOADS) * 1024));
     else
         lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
 }
@@ -323,54 +329,54 @@ __device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
     return cat(lo, hi);
 }
 
-// Tile index of workgroup `b` among T tiles: workgroups are dispatched to the
-// 8 XCDs round-robin (b % 8), so each XCD is given a contiguous range of tile
-// ids; inside it, tiles run in groups of G tile-rows, column by column, so the
-// workgroups that are resident together on one XCD share A rows and W rows in
-// that XCD's L2.  A bijection on [0, T): results do not depend on it.
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int G, int &tm, int &tn)
-{
-    const int T = tiles_m * tiles_n;
-    const int xcd = b & 7, local = b >> 3;
-    const int q = T >> 3, r = T & 7;
-    const int t = xcd * q + min(xcd, r) + local;
-    const int per_group = G * tiles_n;
-    const int group = t / per_group;
-    const int first_m = group * G;
-    const int gsize = min(tiles_m - first_m, G);
-    const int in_group = t - group * per_group;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-}
-
 // ---------------------------------------------------------------------------
-// Tile kernel.  A workgroup of WGM x WGN waves owns a BM x BN output tile and
-// walks K one 128-wide scale block at a time through a STAGES-deep ring of LDS
-// buffers filled by direct global -> LDS copies (no VGPR staging).  Each wave
-// owns a (BM/WGM) x (BN/WGN) sub-tile: TM 16-row activation slices times TN
-// 16-row weight fragments, one MFMA each per block.
+// Tile kernel (persistent).  Workgroup b takes output tiles rank(b),
+// rank(b) + G, rank(b) + 2G, ... of the T = ceil(M/BM) * ceil(N/BN) tiles
+// (G = gridDim.x, launched at about one workgroup per free CU slot), so the
+// prologue and epilogue of one tile overlap the neighbouring tiles' work.
+// A workgroup of WGM x WGN waves walks K one 128-wide scale block at a time
+// through a STAGES-deep ring of LDS buffers filled by direct global -> LDS
+// copies (no VGPR staging); the copy stream runs STAGES-1 blocks ahead and
+// continues straight into the next tile.  Each wave owns a (BM/WGM) x (BN/WGN)
+// sub-tile: TM 16-row activation slices times TN 16-row weight fragments, one
+// MFMA each per block.
 //
-// Per block and wave, slice t does: issue a share of the copies of block
-// kb+STAGES-1 (spread over the first slices so that no wave stalls behind a
-// burst of copies), read the activation fragment of slice t+1, issue the TN
-// MFMAs of slice t, and apply a_scale * w_scale to the results of slice t-1
-// with one FMA per output.  The results of a block's last slice are scaled at
-// the start of the next block.
+// Per block and wave, slice t does: issue a share of the copies of the block
+// STAGES-1 steps ahead (spread over the first slices so that no wave stalls
+// behind a burst of copies), read the activation fragment of slice t+1, issue
+// the TN MFMAs of slice t, and apply a_scale * w_scale to the results of slice
+// t-1 with one FMA per output.  The results of a block's last slice are scaled
+// at the start of the next block (or before the tile's stores).
 //
 // The one workgroup barrier per block sits at the start of the last slice.
-// Before it every wave waits for its own copies of block kb+1; after it those
-// copies are visible to all waves, and every wave has finished reading the
-// stage of block kb (its last fragment read happens before the barrier), so
-// the stage is free for the copies the next block issues.  Right after the
-// barrier each wave issues the last slice's MFMAs from registers and then
-// reads block kb+1's weight fragments, first activation fragment and scales,
-// so the LDS latency at a block boundary hides under that slice's work.
+// Before it every wave waits for its own copies of the next block; after it
+// those copies are visible to all waves, and every wave has finished reading
+// the current block's stage (its last fragment read happens before the
+// barrier), so that stage is free for the copies the next block issues.  Right
+// after the barrier each wave issues the last slice's MFMAs from registers and
+// then reads the next block's weight fragments, first activation fragment and
+// scales, so the LDS latency at a block boundary hides under that slice's work.
 //
 // LDS stage: A tile [BM][128] | W tile [BN][128] | scales [64 * waves] floats.
 // Scale slot s < BM holds a_scale of tile row s; slot BM + j holds w_scale of
 // the tile's j-th 128-row weight block.  Tiles are swizzled as described at
 // chunk_swizzle().
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Tile (tm, tn) of linear tile id L: tiles are numbered in groups of G tile
+// rows, column by column inside a group.  Workgroups of one XCD hold
+// consecutive ids (see tile_kernel), so the tiles resident together on an XCD
+// form a compact G-row block that shares A rows and W rows in its L2.
+__device__ __forceinline__ void linear_tile(int L, int tiles_m, int tiles_n, int G, int &tm, int &tn)
+{
+    const int per_group = G * tiles_n;
+    const int group = L / per_group;
+    const int first_m = group * G;
+    const int gsize = min(tiles_m - first_m, G);
+    const int in_group = L - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
 
 template <int BM, int BN, int WGM, int WGN, int STAGES>
 __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
@@ -389,8 +395,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     constexpr int SPREAD = STAGES == 2 ? cmin(TM - 1, 6) : cmin(TM, 6);
     constexpr int CPS = SPREAD > 0 ? (PER_BLOCK + SPREAD - 1) / SPREAD : PER_BLOCK;
     constexpr int C_BEFORE = cmin(PER_BLOCK, cmin(SPREAD, TM - 1) * CPS);   // issued before the barrier
-    // Copies a wave may still have in flight at the barrier of block kb: all
-    // of those issued after block kb+1's.
+    // Copies a wave may still have in flight at a block's barrier: all of
+    // those issued after the next block's.  (Vector memory operations complete
+    // in issue order; the stores of a finished tile only make this wait
+    // stricter.)
     constexpr int VM_AT_BARRIER = (STAGES - 3) * PER_BLOCK + C_BEFORE;
     static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
                   "each wave copies whole 8-row groups of both tiles");
@@ -407,38 +415,69 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tmi, tni;
-    tile_coords((int)blockIdx.x, tiles_m, tiles_n, BM >= 256 ? 2 : 4, tmi, tni);
-    const int m0 = tmi * BM, n0 = tni * BN;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, T = tiles_m * tiles_n;
+    // Workgroup b runs on XCD b % 8; with the grid a multiple of 8, rank puts
+    // the workgroups of one XCD on consecutive tile ids.
+    const int grid = (int)gridDim.x, b = (int)blockIdx.x;
+    const int rank = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
+    if (rank >= T)
+        return;
+    const int ntiles = (T - 1 - rank) / grid + 1;
+    int G = 1;
+    while (4 * G * G <= (grid >> 3) && G < tiles_m)   // about sqrt(grid / 8) tile rows per group
+        G *= 2;
     const int r16 = lane & 15, g = lane >> 4;
-
-    // Copy sources: lane covers row (lane >> 3) of an 8-row group and physical
-    // chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row).
-    // Offsets are relative to the tile's first row (rows past M or N repeat the
-    // last valid row; their outputs are never stored) and fit in 32 bits
-    // because the host keeps 256 * K below 2^31.
     const int lrow = lane >> 3, pch = lane & 7;
-    const uint8_t *a_tile = p.A + (size_t)m0 * K;
-    const uint8_t *w_tile = p.W + (size_t)n0 * K;
+    const int NB = (N + 127) >> 7;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    const int ws_slot = BM + ((wn * WN) >> 7);   // tiles start on weight-block boundaries
+    const int arow = wm * WM + r16, wrow = wn * WN + r16;
+
+    // Copies.  Lane covers row (lane >> 3) of an 8-row group and physical
+    // chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row);
+    // its offset from the block's first byte in the tile's first row is the
+    // same for every tile (it fits in 32 bits because the host keeps 256 * K
+    // below 2^31).  The per-block buffer descriptors end at the last row of
+    // the matrix, so rows past M or N read zeros (their outputs are never
+    // stored).  The scale copy reads per-lane pointers: lane slot s < BM takes
+    // a_scale of tile row s (the last row past M), the lanes above take w_scale
+    // of the tile's weight blocks.
     uint32_t a_off[A_LOADS], w_off[W_LOADS];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-        const int row = (wave * A_LOADS + i) * 8 + lrow;
-        a_off[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
+    for (int j = 0; j < A_LOADS; ++j) {
+        const int row = (wave * A_LOADS + j) * 8 + lrow;
+        a_off[j] = (uint32_t)row * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
     }
 #pragma unroll
-    for (int i = 0; i < W_LOADS; ++i) {
-        const int row = (wave * W_LOADS + i) * 8 + lrow;
-        w_off[i] = (uint32_t)(min(n0 + row, N - 1) - n0) * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
+    for (int j = 0; j < W_LOADS; ++j) {
+        const int row = (wave * W_LOADS + j) * 8 + lrow;
+        w_off[j] = (uint32_t)row * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
     }
-    const int NB = (N + 127) >> 7, nb0 = n0 >> 7;
     const int slot = wave * 64 + lane;
-    const float *s_src = slot < BM ? p.a_scale + (size_t)min(m0 + slot, M - 1) * KB
-                                   : p.w_scale + (size_t)min(nb0 + slot - BM, NB - 1) * KB;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
-    const int ws_slot = BM + ((n0 + wn * WN) >> 7) - nb0;
-    const int arow = wm * WM + r16, wrow = wn * WN + r16;
+    struct CopyTile {
+        int m0, n0;
+        const float *s_src;
+    };
+    auto copy_tile = [&](int i) {
+        int tm, tn;
+        linear_tile(rank + i * grid, tiles_m, tiles_n, G, tm, tn);
+        CopyTile c;
+        c.m0 = tm * BM;
+        c.n0 = tn * BN;
+        c.s_src = slot < BM ? p.a_scale + (size_t)min(c.m0 + slot, M - 1) * KB
+                            : p.w_scale + (size_t)min((c.n0 >> 7) + slot - BM, NB - 1) * KB;
+        return c;
+    };
+    // Descriptors of K block kb of a tile: the rows that exist, minus the
+    // bytes before the block in the first row.
+    auto rsrc_a = [&](int m0, int kb) {
+        return tile_rsrc(p.A + (size_t)m0 * K + (size_t)kb * 128,
+                         (uint32_t)min(M - m0, BM) * (uint32_t)K - (uint32_t)kb * 128u);
+    };
+    auto rsrc_w = [&](int n0, int kb) {
+        return tile_rsrc(p.W + (size_t)n0 * K + (size_t)kb * 128,
+                         (uint32_t)min(N - n0, BN) * (uint32_t)K - (uint32_t)kb * 128u);
+    };
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -447,12 +486,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         for (int u = 0; u < TN; ++u)
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat
-    // the last block), then the fragments of block 0.
+    // Prologue: the first STAGES-1 blocks of the copy stream in flight, then
+    // the fragments of block 0.  (Stream position q is block q % KB of this
+    // workgroup's tile q / KB; past the end it repeats the last block, into
+    // stages nobody reads again.)
+    const int steps = ntiles * KB;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(a_tile, w_tile, a_off, w_off, s_src, min(s, KB - 1),
-                                                            lds0 + (uint32_t)(s * STAGE), wave);
+    for (int s = 0; s < STAGES - 1; ++s) {
+        const int q = min(s, steps - 1);
+        const CopyTile c = copy_tile(q / KB);
+        const int ckb = q % KB;
+        issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), a_off, w_off,
+                                                            c.s_src, ckb, lds0 + (uint32_t)(s * STAGE), wave);
+    }
     wait_vmcnt<(STAGES - 2) * PER_BLOCK>();
     __syncthreads();
     v8i wf[TN], af;
@@ -472,19 +518,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     }
 
     // Last slice of the previous block, scaled at the start of the next one
-    // (zero before the first block: adds exactly +0).
+    // (zero before a tile's first block: adds exactly +0).
     v4f d_last[TN];
 #pragma unroll
     for (int u = 0; u < TN; ++u)
         d_last[u] = (v4f){0.f, 0.f, 0.f, 0.f};
     float s_last = 0.f;
 
-    for (int kb = 0; kb < KB; ++kb) {
-        const uint8_t *sA = smem + (kb % STAGES) * STAGE;
-        const int kc = min(kb + STAGES - 1, KB - 1);   // block fetched by this block's copies
-        const uint32_t cstage = lds0 + (uint32_t)(((kb + STAGES - 1) % STAGES) * STAGE);
-        const uint8_t *ab = uniform_ptr(a_tile + (size_t)kc * 128);
-        const uint8_t *wb = uniform_ptr(w_tile + (size_t)kc * 128);
+    // One K block at stream position `step`; its copies fetch block ckb of the
+    // copy tile described by ra, rw and s_src.
+    auto block = [&](int step, v4i ra, v4i rw, const float *s_src, int ckb) {
+        const uint8_t *sA = smem + (step % STAGES) * STAGE;
+        const uint32_t cstage = lds0 + (uint32_t)(((step + STAGES - 1) % STAGES) * STAGE);
         float sc[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t)
@@ -497,13 +542,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             if (t == TM - 1) {
-                wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of block kb+1 have landed
-                __syncthreads();               // ... every wave's; stage kb % STAGES is read out
+                wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of the next block have landed
+                __syncthreads();               // ... every wave's; this block's stage is read out
             }
             if (t < SPREAD) {
 #pragma unroll
                 for (int j = t * CPS; j < (t + 1) * CPS && j < PER_BLOCK; ++j)
-                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ab, wb, a_off, w_off, s_src, kc, cstage, wave);
+                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
             }
             v8i af_next = af;
             if (t + 1 < TM)
@@ -513,11 +558,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
             for (int u = 0; u < TN; ++u)
                 dn[u] = mfma_block(wf[u], af);
             if (t == TM - 1) {
-                // Block kb+1: its stage is complete (barrier above); these reads
-                // overwrite fragments the MFMAs just issued have already read.
-                // After the last block they read a stale stage and are unused.
+                // The next block: its stage is complete (barrier above); these
+                // reads overwrite fragments the MFMAs just issued have already
+                // read.  After the last block they read a stale stage, unused.
                 __builtin_amdgcn_sched_barrier(0);
-                const uint8_t *nA = smem + ((kb + 1) % STAGES) * STAGE, *nW = nA + A_BYTES;
+                const uint8_t *nA = smem + ((step + 1) % STAGES) * STAGE, *nW = nA + A_BYTES;
                 const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
                 wf[0] = lds_fragment(nW, wrow, g);
                 af_next = lds_fragment(nA, arow, g);
@@ -544,21 +589,50 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         for (int u = 0; u < TN; ++u)
             d_last[u] = d[u];
         s_last = sc[TM - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < TN; ++u)
-        acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
-    wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
+    };
 
+    // Per tile: the blocks whose copies stay inside the tile, then the last
+    // STAGES-1 blocks, whose copies already fetch the next tile, then the
+    // stores.
+    const int main_blocks = KB - (STAGES - 1) > 0 ? KB - (STAGES - 1) : 0;
+    int step = 0;
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const CopyTile cur = copy_tile(tile);
+        for (int kb = 0; kb < main_blocks; ++kb, ++step)
+            block(step, rsrc_a(cur.m0, kb + STAGES - 1), rsrc_w(cur.n0, kb + STAGES - 1), cur.s_src,
+                  kb + STAGES - 1);
+        for (int kb = main_blocks; kb < KB; ++kb, ++step) {
+            const int q = min(step + STAGES - 1, steps - 1);
+            const CopyTile c = copy_tile(q / KB);
+            const int ckb = q % KB;
+            block(step, rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), c.s_src, ckb);
+        }
+
+        // Tile done: fold in the last slice, round to bf16 and store.
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        const int m = m0 + wm * WM + 16 * t + r16;
-        if (m < M) {
+        for (int u = 0; u < TN; ++u)
+            acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
+        const int n_base = cur.n0 + wn * WN + 4 * g;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int m = cur.m0 + wm * WM + 16 * t + r16;
+            if (m < M) {
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    store4(p.Y, (int64_t)m * N, n_base + 16 * u, N, vec_store != 0, acc[t][u]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                store4(p.Y, (int64_t)m * N, n0 + wn * WN + 16 * u + 4 * g, N, vec_store != 0, acc[t][u]);
-        }
+                acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+            d_last[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        s_last = 0.f;
     }
+    wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
 }
 
 // Explicit instantiations (emit the host-side launch stubs).
@@ -593,9 +667,17 @@ struct Entry {
     int lds_bytes;
 };
 
-#define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, "skinny_r" #TPW "_d" #D "_w" #NW}, \
+#define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, "skinny_r" #TPW "_d" #D "_w" #NW}, \
                             reinterpret_cast<const void *>(&skinny_kernel<TPW, D, NW>), 0}
+// Persistent tile grids are sized for 8 waves per CU (two per SIMD: every
+// tile instance uses more than 128 VGPRs or is LDS-limited below that), or
+// fewer workgroups where their LDS does not fit.
+constexpr int tile_per_cu(int lds_bytes, int waves)
+{
+    return cmin(163840 / lds_bytes, 8 / waves) > 0 ? cmin(163840 / lds_bytes, 8 / waves) : 1;
+}
 #define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, \
+                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN), \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
                                    reinterpret_cast<const void *>(&tile_kernel<BM, BN, WGM, WGN, S>), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
@@ -616,13 +698,15 @@ int num_variants() { return kNumEntries; }
 
 const Variant &variant(int id) { return kEntries[id].v; }
 
-int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K)
+int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
 {
     (void)K;
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return (N + v.bn - 1) / v.bn;
-    return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    const int64_t slots = (int64_t)(cus > 0 ? cus : 1) * v.per_cu;
+    return tiles < slots ? tiles : slots;
 }
 
 int64_t variant_passes(int id, int64_t K)
@@ -647,10 +731,10 @@ hipError_t set_kernel_attributes()
     return hipSuccess;
 }
 
-hipError_t launch_variant(int id, const Args &a, hipStream_t stream)
+hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream)
 {
     const Entry &e = kEntries[id];
-    const int64_t grid = variant_grid(id, a.M, a.N, a.K);
+    const int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;
     void *params[] = {&args, &vec};

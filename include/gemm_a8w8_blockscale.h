@@ -70,10 +70,11 @@ typedef struct {
     int32_t variant;    /* index in [0, gemm_a8w8_num_variants())                         */
     int32_t bm, bn;     /* output tile of one workgroup: rows of Y (M) x columns (N)      */
     int32_t waves;      /* waves (64 lanes) per workgroup                                 */
-    int32_t kblocks;    /* 128-wide K blocks one wave loads at once (skinny); 1 for tile  */
-    int32_t kpasses;    /* passes over K per wave (skinny), K/128 steps (tile)            */
+    int32_t kblocks;    /* 128-wide K blocks one wave loads at once (skinny); LDS ring depth (tile) */
+    int32_t kpasses;    /* passes over K per wave (skinny), K/128 steps per tile (tile)   */
     int32_t fallback;   /* 1: (N,K) has no tuned table, a heuristic plan was chosen       */
-    int64_t grid;       /* workgroups launched for this shape                             */
+    int64_t grid;       /* workgroups launched for this shape (tile: persistent, at most  */
+                        /* a few per CU, each looping over its share of the output tiles) */
     int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
 } a8w8_plan;
 
@@ -94,7 +95,8 @@ int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count,
                               a8w8_plan *out);
 
 /* Number of compiled kernel instances, and the description of one of them
-   (grid and key_m are filled for (M, N, K); M may be 0 for a bare description). */
+   (grid, for a 256-CU device, and key_m are filled for (M, N, K); M may be 0
+   for a bare description). */
 int gemm_a8w8_num_variants(void);
 int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
                                a8w8_plan *out);
