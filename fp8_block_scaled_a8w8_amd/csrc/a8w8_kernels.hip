@@ -336,26 +336,25 @@ __device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
 // prologue and epilogue of one tile overlap the neighbouring tiles' work.
 // A workgroup of WGM x WGN waves walks K one 128-wide scale block at a time
 // through a STAGES-deep ring of LDS buffers filled by direct global -> LDS
-// copies (no VGPR staging); the copy stream runs STAGES-1 blocks ahead and
-// continues straight into the next tile.  Each wave owns a (BM/WGM) x (BN/WGN)
-// sub-tile: TM 16-row activation slices times TN 16-row weight fragments, one
-// MFMA each per block.
+// copies (no VGPR staging); the copy stream runs AHEAD blocks ahead (see the
+// copy schedule below) and continues straight into the next tile.  Each wave
+// owns a (BM/WGM) x (BN/WGN) sub-tile: TM 16-row activation slices times TN
+// 16-row weight fragments, one MFMA each per block.
 //
-// Per block and wave, slice t does: issue a share of the copies of the block
-// STAGES-1 steps ahead (spread over the first slices so that no wave stalls
-// behind a burst of copies), read the activation fragment of slice t+1, issue
-// the TN MFMAs of slice t, and apply a_scale * w_scale to the results of slice
-// t-1 with one FMA per output.  The results of a block's last slice are scaled
-// at the start of the next block (or before the tile's stores).
+// Per block and wave, slice t does: issue its share of the block's copies,
+// read the activation fragment of slice t+1, issue the TN MFMAs of slice t,
+// and apply a_scale * w_scale to the results of slice t-1 with one FMA per
+// output.  The results of a block's last slice are scaled at the start of the
+// next block (or before the tile's stores).
 //
 // The one workgroup barrier per block sits at the start of the last slice.
 // Before it every wave waits for its own copies of the next block; after it
 // those copies are visible to all waves, and every wave has finished reading
 // the current block's stage (its last fragment read happens before the
-// barrier), so that stage is free for the copies the next block issues.  Right
-// after the barrier each wave issues the last slice's MFMAs from registers and
-// then reads the next block's weight fragments, first activation fragment and
-// scales, so the LDS latency at a block boundary hides under that slice's work.
+// barrier).  Right after the barrier each wave issues the last slice's MFMAs
+// from registers and then reads the next block's weight fragments, first
+// activation fragment and scales, so the LDS latency at a block boundary hides
+// under that slice's work.
 //
 // LDS stage: A tile [BM][128] | W tile [BN][128] | scales [64 * waves] floats.
 // Scale slot s < BM holds a_scale of tile row s; slot BM + j holds w_scale of
@@ -389,17 +388,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB copies per wave per block
     constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
     constexpr int NBW = (BN + 127) / 128;                                    // weight blocks a tile spans
-    // Copies of a block go out CPS per slice over its first SPREAD slices.
-    // With two stages they fetch the next block and must all be issued before
-    // the last slice's barrier.
-    constexpr int SPREAD = STAGES == 2 ? cmin(TM - 1, 6) : cmin(TM, 6);
-    constexpr int CPS = SPREAD > 0 ? (PER_BLOCK + SPREAD - 1) / SPREAD : PER_BLOCK;
-    constexpr int C_BEFORE = cmin(PER_BLOCK, cmin(SPREAD, TM - 1) * CPS);   // issued before the barrier
+    // Copy schedule.  Wave tiles of three or more slices spread a block's
+    // copies, CPS per slice, over its first SPREAD slices; those copies run
+    // before the block's barrier, so they can only refill the stage freed by
+    // the previous barrier and fetch the block STAGES-1 steps ahead (with two
+    // stages they must all precede the barrier).  Wave tiles of one or two
+    // slices issue all copies right after the barrier ("late"), which has
+    // just freed the current block's stage (its fragments are in registers),
+    // and fetch the block STAGES steps ahead: a full ring of lookahead.
+    constexpr bool LATE = TM <= 2;
+    constexpr int AHEAD = LATE ? STAGES : STAGES - 1;
+    constexpr int SPREAD = LATE ? 1 : STAGES == 2 ? cmin(TM - 1, 6) : cmin(TM, 6);
+    constexpr int CPS = LATE ? PER_BLOCK : (PER_BLOCK + SPREAD - 1) / SPREAD;
+    constexpr int C_BEFORE = LATE ? 0 : cmin(PER_BLOCK, cmin(SPREAD, TM - 1) * CPS);   // issued before the barrier
     // Copies a wave may still have in flight at a block's barrier: all of
     // those issued after the next block's.  (Vector memory operations complete
     // in issue order; the stores of a finished tile only make this wait
     // stricter.)
-    constexpr int VM_AT_BARRIER = (STAGES - 3) * PER_BLOCK + C_BEFORE;
+    constexpr int VM_AT_BARRIER = (AHEAD - 2) * PER_BLOCK + C_BEFORE;
     static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
                   "each wave copies whole 8-row groups of both tiles");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
@@ -407,8 +413,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     static_assert(BN <= 128 ? 128 % BN == 0 : BN % 128 == 0, "tiles start on weight-block boundaries");
     static_assert(BM + NBW <= NWAVES * 64, "scale slots");
     static_assert(STAGES >= 2 && SPREAD >= 1 && SPREAD * CPS >= PER_BLOCK, "copy schedule");
-    static_assert(STAGES > 2 || C_BEFORE == PER_BLOCK, "two stages: next block's copies precede the barrier");
-    static_assert(VM_AT_BARRIER >= 0 && VM_AT_BARRIER < 64 && (STAGES - 2) * PER_BLOCK < 64, "vmcnt range");
+    static_assert(LATE || STAGES > 2 || C_BEFORE == PER_BLOCK, "two stages: next block's copies precede the barrier");
+    static_assert(VM_AT_BARRIER >= 0 && VM_AT_BARRIER < 64 && (AHEAD - 1) * PER_BLOCK < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
@@ -464,8 +470,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         CopyTile c;
         c.m0 = tm * BM;
         c.n0 = tn * BN;
+        // Lanes past the needed slots repeat the last needed address: one
+        // cache line, not one per lane.
         c.s_src = slot < BM ? p.a_scale + (size_t)min(c.m0 + slot, M - 1) * KB
-                            : p.w_scale + (size_t)min((c.n0 >> 7) + slot - BM, NB - 1) * KB;
+                            : p.w_scale + (size_t)min((c.n0 >> 7) + min(slot - BM, NBW - 1), NB - 1) * KB;
         return c;
     };
     // Descriptors of K block kb of a tile: the rows that exist, minus the
@@ -486,20 +494,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         for (int u = 0; u < TN; ++u)
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: the first STAGES-1 blocks of the copy stream in flight, then
-    // the fragments of block 0.  (Stream position q is block q % KB of this
+    // Prologue: the first AHEAD blocks of the copy stream in flight, then the
+    // fragments of block 0.  (Stream position q is block q % KB of this
     // workgroup's tile q / KB; past the end it repeats the last block, into
     // stages nobody reads again.)
     const int steps = ntiles * KB;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
+    for (int s = 0; s < AHEAD; ++s) {
         const int q = min(s, steps - 1);
         const CopyTile c = copy_tile(q / KB);
         const int ckb = q % KB;
         issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), a_off, w_off,
                                                             c.s_src, ckb, lds0 + (uint32_t)(s * STAGE), wave);
     }
-    wait_vmcnt<(STAGES - 2) * PER_BLOCK>();
+    wait_vmcnt<(AHEAD - 1) * PER_BLOCK>();
     __syncthreads();
     v8i wf[TN], af;
     float sa[TM], ws;
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     // copy tile described by ra, rw and s_src.
     auto block = [&](int step, v4i ra, v4i rw, const float *s_src, int ckb) {
         const uint8_t *sA = smem + (step % STAGES) * STAGE;
-        const uint32_t cstage = lds0 + (uint32_t)(((step + STAGES - 1) % STAGES) * STAGE);
+        const uint32_t cstage = lds0 + (uint32_t)(((step + AHEAD) % STAGES) * STAGE);
         float sc[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t)
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
                 wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of the next block have landed
                 __syncthreads();               // ... every wave's; this block's stage is read out
             }
-            if (t < SPREAD) {
+            if (!LATE && t < SPREAD) {
 #pragma unroll
                 for (int j = t * CPS; j < (t + 1) * CPS && j < PER_BLOCK; ++j)
                     issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
@@ -573,6 +581,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
                 for (int s = 0; s < TM; ++s)
                     sa[s] = nS[arow + 16 * s];
                 ws = nS[ws_slot];
+                if (LATE) {
+#pragma unroll
+                    for (int j = 0; j < PER_BLOCK; ++j)
+                        issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
+                }
             }
             if (t > 0) {
 #pragma unroll
@@ -592,17 +605,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     };
 
     // Per tile: the blocks whose copies stay inside the tile, then the last
-    // STAGES-1 blocks, whose copies already fetch the next tile, then the
-    // stores.
-    const int main_blocks = KB - (STAGES - 1) > 0 ? KB - (STAGES - 1) : 0;
+    // AHEAD blocks, whose copies already fetch the next tile, then the stores.
+    const int main_blocks = KB - AHEAD > 0 ? KB - AHEAD : 0;
     int step = 0;
     for (int tile = 0; tile < ntiles; ++tile) {
         const CopyTile cur = copy_tile(tile);
         for (int kb = 0; kb < main_blocks; ++kb, ++step)
-            block(step, rsrc_a(cur.m0, kb + STAGES - 1), rsrc_w(cur.n0, kb + STAGES - 1), cur.s_src,
-                  kb + STAGES - 1);
+            block(step, rsrc_a(cur.m0, kb + AHEAD), rsrc_w(cur.n0, kb + AHEAD), cur.s_src, kb + AHEAD);
         for (int kb = main_blocks; kb < KB; ++kb, ++step) {
-            const int q = min(step + STAGES - 1, steps - 1);
+            const int q = min(step + AHEAD, steps - 1);
             const CopyTile c = copy_tile(q / KB);
             const int ckb = q % KB;
             block(step, rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), c.s_src, ckb);
@@ -650,6 +661,10 @@ A8W8_TILE_INST(32, 128, 1, 4, 3)
 A8W8_TILE_INST(32, 64, 2, 2, 3)
 A8W8_TILE_INST(64, 32, 2, 2, 3)
 A8W8_TILE_INST(32, 32, 2, 2, 3)
+A8W8_TILE_INST(32, 32, 2, 2, 4)
+A8W8_TILE_INST(32, 32, 2, 2, 8)
+A8W8_TILE_INST(32, 64, 2, 2, 6)
+A8W8_TILE_INST(64, 64, 2, 2, 4)
 #undef A8W8_TILE_INST
 
 }  // namespace kern
@@ -669,15 +684,15 @@ struct Entry {
 
 #define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, "skinny_r" #TPW "_d" #D "_w" #NW}, \
                             reinterpret_cast<const void *>(&skinny_kernel<TPW, D, NW>), 0}
-// Persistent tile grids are sized for 8 waves per CU (two per SIMD: every
-// tile instance uses more than 128 VGPRs or is LDS-limited below that), or
-// fewer workgroups where their LDS does not fit.
-constexpr int tile_per_cu(int lds_bytes, int waves)
+// Persistent tile grids are sized for WPC waves per CU: 8 (two per SIMD) for
+// the instances above 128 VGPRs, 16 for the small ones, or fewer workgroups
+// where their LDS does not fit.
+constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 {
-    return cmin(163840 / lds_bytes, 8 / waves) > 0 ? cmin(163840 / lds_bytes, 8 / waves) : 1;
+    return cmin(163840 / lds_bytes, wpc / waves) > 0 ? cmin(163840 / lds_bytes, wpc / waves) : 1;
 }
-#define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, \
-                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN), \
+#define TILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, \
+                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
                                    reinterpret_cast<const void *>(&tile_kernel<BM, BN, WGM, WGN, S>), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
@@ -685,10 +700,11 @@ constexpr int tile_per_cu(int lds_bytes, int waves)
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
     SKINNY(1, 3, 16), SKINNY(2, 3, 16), SKINNY(1, 10, 4), SKINNY(1, 12, 4), SKINNY(1, 2, 4),
-    TILE(256, 256, 2, 4, 2), TILE(256, 128, 2, 4, 3), TILE(128, 256, 2, 4, 3), TILE(128, 128, 2, 2, 2),
-    TILE(128, 128, 2, 2, 4), TILE(128, 64, 2, 2, 3), TILE(64, 128, 2, 2, 3), TILE(64, 64, 2, 2, 3),
-    TILE(128, 32, 4, 1, 3), TILE(32, 128, 1, 4, 3), TILE(32, 64, 2, 2, 3),
-    TILE(64, 32, 2, 2, 3), TILE(32, 32, 2, 2, 3),
+    TILE(256, 256, 2, 4, 2, 8), TILE(256, 128, 2, 4, 3, 8), TILE(128, 256, 2, 4, 3, 8), TILE(128, 128, 2, 2, 2, 8),
+    TILE(128, 128, 2, 2, 4, 8), TILE(128, 64, 2, 2, 3, 16), TILE(64, 128, 2, 2, 3, 8), TILE(64, 64, 2, 2, 3, 16),
+    TILE(128, 32, 4, 1, 3, 16), TILE(32, 128, 1, 4, 3, 16), TILE(32, 64, 2, 2, 3, 16),
+    TILE(64, 32, 2, 2, 3, 16), TILE(32, 32, 2, 2, 3, 16),
+    TILE(32, 32, 2, 2, 4, 16), TILE(32, 32, 2, 2, 8, 16), TILE(32, 64, 2, 2, 6, 16), TILE(64, 64, 2, 2, 4, 16),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 

@@ -110,7 +110,7 @@ def test_dense_m_sweep_sampled_rows(N, K):
 
 # ---------------------------------------------------------------- every compiled instance
 
-@pytest.mark.parametrize("variant", range(24))
+@pytest.mark.parametrize("variant", range(40))
 def test_every_instance_on_ragged_shape(variant):
     if variant >= g.gemm_a8w8_num_variants():
         pytest.skip("no such instance")
@@ -122,6 +122,34 @@ def test_every_instance_on_ragged_shape(variant):
         y = run(*to_dev(A, a_s, W, w_s), variant=variant)
         assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{info['name']} M={M} N={N}")
     say(f"instance {info['name']} ok")
+
+
+def _tile_instances():
+    return [v for v in g.variants() if v["kernel_name"] == "tile"]
+
+
+@pytest.mark.parametrize("K", [128, 640])
+def test_every_tile_instance_loops_over_tiles(K):
+    """Each workgroup of the persistent tile grid takes several tiles: ragged
+    M and N with at least twice as many tiles as workgroups (K = 128: one
+    K block, so the copies run several tiles ahead)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(11)
+    for v in _tile_instances():
+        bm, bn = v["bm"], v["bn"]
+        per_cu = g.gemm_a8w8_describe_variant(v["variant"], 1 << 24, 1 << 16, K)["grid"] // 256
+        N = 3 * bn + 40
+        tiles_n = (N + bn - 1) // bn
+        tiles_m = (2 * cus * per_cu + tiles_n - 1) // tiles_n + 1
+        M = tiles_m * bm - bm // 2 - 3
+        A, a_s, W, w_s = _inputs(M, N, K, a_seed=30 + bm, w_seed=40 + bn)
+        y = run(*to_dev(A, a_s, W, w_s), variant=v["variant"])
+        rows = _sample_rows(M, rng, extra=[bm * i + j for i in (1, tiles_m // 2, tiles_m - 1) for j in (0, bm - 1)])
+        st = assert_parity(y_host(y)[rows], oracle.gemm(A, a_s, W, w_s, rows=rows),
+                           f"{v['name']} M={M} N={N} K={K}")
+        say(f"instance {v['name']} M={M} N={N} K={K}: {tiles_m * tiles_n} tiles on "
+            f"{min(tiles_m * tiles_n, cus * per_cu)} workgroups, rel_l2={st['rel_l2']:.3e}")
+        del y
 
 
 # ---------------------------------------------------------------- bitwise invariants
