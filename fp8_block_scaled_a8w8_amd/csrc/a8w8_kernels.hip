@@ -234,14 +234,19 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 // all of them before the first fragment read, collapsing the ring to depth 1.
 // The asm has no register outputs (only the addresses, which the hardware reads
 // at issue), and the kernel's own counted waits order the copies against the
-// reads.
+// reads.  The compiler resolves hazards only for instructions it generates,
+// not inside these strings, so the asm pads its own: a scalar write of m0
+// needs one wait state before an LDS-DMA load reads it (without it the load
+// can take a stale m0 as its LDS destination), and an SGPR written by a VALU
+// instruction needs five before a vector-memory instruction reads it; s_nop 4
+// covers both.
 //
 // The 16-byte form reads through a buffer descriptor (see tile_rsrc) at a
 // 32-bit per-lane offset: lanes past the descriptor's range fetch zeros
 // instead of faulting, which is how rows past M or N are handled.
 __device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
@@ -249,7 +254,7 @@ __device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, uint32_t lds
 
 __device__ __forceinline__ void lds_copy4(const float *src, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(src) : "memory", "m0");
 }
 
 // Raw buffer descriptor (stride 0, 32-bit data format) over `bytes` bytes at
