@@ -335,7 +335,7 @@ __device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel (persistent).  Workgroup b takes output tiles rank(b),
+// Persistent tile kernel ("ptile").  Workgroup b takes output tiles rank(b),
 // rank(b) + G, rank(b) + 2G, ... of the T = ceil(M/BM) * ceil(N/BN) tiles
 // (G = gridDim.x, launched at about one workgroup per free CU slot), so the
 // prologue and epilogue of one tile overlap the neighbouring tiles' work.
@@ -383,7 +383,7 @@ __device__ __forceinline__ void linear_tile(int L, int tiles_m, int tiles_n, int
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES>
-__global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
+__global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_store)
 {
     constexpr int NWAVES = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -543,17 +543,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     auto block = [&](int step, v4i ra, v4i rw, const float *s_src, int ckb) {
         const uint8_t *sA = smem + (step % STAGES) * STAGE;
         const uint32_t cstage = lds0 + (uint32_t)(((step + AHEAD) % STAGES) * STAGE);
-        float sc[TM];
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-            sc[t] = sa[t] * ws;
 #pragma unroll
         for (int u = 0; u < TN; ++u)
             acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
 
+        // Scales are formed where they are used, so no wave waits for the
+        // scale reads of the previous block before its barrier.
         v4f d[TN];
+        float s_cur = 0.f;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
+            const float sc_prev = t > 0 ? sa[t - 1] * ws : 0.f;
             if (t == TM - 1) {
                 wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of the next block have landed
                 __syncthreads();               // ... every wave's; this block's stage is read out
@@ -574,6 +574,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
                 // The next block: its stage is complete (barrier above); these
                 // reads overwrite fragments the MFMAs just issued have already
                 // read.  After the last block they read a stale stage, unused.
+                s_cur = sa[TM - 1] * ws;
                 __builtin_amdgcn_sched_barrier(0);
                 const uint8_t *nA = smem + ((step + 1) % STAGES) * STAGE, *nW = nA + A_BYTES;
                 const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
             if (t > 0) {
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    acc[t - 1][u] = fma4(d[u], sc[t - 1], acc[t - 1][u]);
+                    acc[t - 1][u] = fma4(d[u], sc_prev, acc[t - 1][u]);
             }
 #pragma unroll
             for (int u = 0; u < TN; ++u)
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 #pragma unroll
         for (int u = 0; u < TN; ++u)
             d_last[u] = d[u];
-        s_last = sc[TM - 1];
+        s_last = s_cur;
     };
 
     // Per tile: the blocks whose copies stay inside the tile, then the last
@@ -652,6 +653,205 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 }
 
 // Explicit instantiations (emit the host-side launch stubs).
+#define A8W8_PTILE_INST(BM, BN, WGM, WGN, S) template __global__ void ptile_kernel<BM, BN, WGM, WGN, S>(Args, int);
+A8W8_PTILE_INST(256, 256, 2, 4, 2)
+A8W8_PTILE_INST(256, 128, 2, 4, 3)
+A8W8_PTILE_INST(128, 256, 2, 4, 3)
+A8W8_PTILE_INST(128, 128, 2, 2, 2)
+A8W8_PTILE_INST(128, 128, 2, 2, 4)
+A8W8_PTILE_INST(64, 64, 2, 2, 4)
+A8W8_PTILE_INST(32, 64, 2, 2, 6)
+A8W8_PTILE_INST(32, 32, 2, 2, 4)
+A8W8_PTILE_INST(32, 32, 2, 2, 8)
+#undef A8W8_PTILE_INST
+
+// ---------------------------------------------------------------------------
+// One-workgroup-per-tile kernel ("tile").  The same block scaling and LDS
+// layout as ptile_kernel, with a simpler schedule: one barrier at the start of
+// each block, after which every wave issues all copies of the block STAGES-1
+// steps ahead and reads its fragments of the current block.  It keeps a
+// shorter dependence chain per block, which wins where few, short blocks
+// dominate (tiny N, latency-bound) and for some mid-size tiles; the tuner
+// picks between the two per shape.  Copies address global memory with 64-bit
+// per-lane pointers (rows past M or N repeat the last valid row) and the
+// weight scales come through scalar loads.
+
+__device__ __forceinline__ void dma16_at(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4_at(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+}
+
+template <int A_LOADS, int W_LOADS>
+__device__ __forceinline__ void issue_block_copies(const uint8_t *const (&a_src)[A_LOADS],
+                                                 const uint8_t *const (&w_src)[W_LOADS], const float *as_src,
+                                                 int kb, uint8_t *stage, int a_bytes, int w_bytes, int wave)
+{
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+        dma16_at(a_src[i] + (size_t)kb * 128, stage + (wave * A_LOADS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i)
+        dma16_at(w_src[i] + (size_t)kb * 128, stage + a_bytes + (wave * W_LOADS + i) * 1024);
+    dma4_at(as_src + kb, stage + a_bytes + w_bytes + wave * 256);
+}
+
+
+// Tile index of workgroup `b` among T tiles: workgroups are dispatched to the
+// 8 XCDs round-robin (b % 8), so each XCD is given a contiguous range of tile
+// ids; inside it, tiles run in groups of G tile-rows, column by column, so the
+// workgroups that are resident together on one XCD share A rows and W rows in
+// that XCD's L2.  A bijection on [0, T): results do not depend on it.
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int G, int &tm, int &tn)
+{
+    const int T = tiles_m * tiles_n;
+    const int xcd = b & 7, local = b >> 3;
+    const int q = T >> 3, r = T & 7;
+    const int t = xcd * q + min(xcd, r) + local;
+    const int per_group = G * tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * G;
+    const int gsize = min(tiles_m - first_m, G);
+    const int in_group = t - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+
+// Tile kernel.  A workgroup of WGM x WGN waves owns a BM x BN output tile and
+// walks K one 128-wide scale block at a time through a STAGES-deep ring of LDS
+// buffers: block kb+STAGES-1 is copied global -> LDS (direct-to-LDS loads, no
+// VGPR staging) while block kb is multiplied.  Each wave owns a
+// (BM/WGM) x (BN/WGN) sub-tile: per block it reads its W and A fragments from
+// LDS, takes one MFMA per 16 x 16 output, and folds the result into the fp32
+// accumulator with the block's a_scale * w_scale.  The MFMAs of 16-row slice
+// t+1 are issued before the scale FMAs of slice t consume slice t's results,
+// so the matrix core and the VALU work overlap.
+//
+// LDS stage: A tile [BM][128] | W tile [BN][128] | activation scales
+// [64 * waves] floats, tiles swizzled as described at chunk_swizzle().
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+__global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
+{
+    constexpr int NWAVES = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
+    constexpr int STAGE = A_BYTES + W_BYTES + NWAVES * 256;
+    constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB loads per wave per block
+    constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
+    static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
+                  "each wave copies whole 8-row groups of both tiles");
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
+    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-row weight block");
+    static_assert(STAGES >= 2 && (STAGES - 2) * PER_BLOCK < 64, "ring depth");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tmi, tni;
+    tile_coords((int)blockIdx.x, tiles_m, tiles_n, BM >= 256 ? 2 : 4, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    // Direct-load sources: lane covers row (lane >> 3) of an 8-row group and
+    // physical chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row).
+    const int lrow = lane >> 3, pch = lane & 7;
+    const uint8_t *a_src[A_LOADS];
+    const uint8_t *w_src[W_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+        const int row = (wave * A_LOADS + i) * 8 + lrow;
+        a_src[i] = p.A + (size_t)min(m0 + row, M - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i) {
+        const int row = (wave * W_LOADS + i) * 8 + lrow;
+        w_src[i] = p.W + (size_t)min(n0 + row, N - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
+    }
+    // Activation scales: wave w copies tile rows 64w + lane (rows past the tile
+    // or past M repeat a valid row and are never read).
+    const float *as_src = p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB;
+    const int NB = (N + 127) >> 7;
+    const_f32 *wsp = (const_f32 *)(p.w_scale + (size_t)min((n0 + wn * WN) >> 7, NB - 1) * KB);
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+            acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat the last block).
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
+                                           W_BYTES, wave);
+    float ws_next = wsp[0];
+
+    for (int kb = 0; kb < KB; ++kb) {
+        const float ws = ws_next;
+        wait_vmcnt<(STAGES - 2) * PER_BLOCK>();   // this wave's copies of block kb have landed
+        __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
+        const int kn = min(kb + STAGES - 1, KB - 1);
+        issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
+                                           A_BYTES, W_BYTES, wave);
+        ws_next = wsp[min(kb + 1, KB - 1)];
+
+        const uint8_t *sA = smem + (kb % STAGES) * STAGE;
+        const uint8_t *sW = sA + A_BYTES;
+        const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
+        float sc[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            sc[t] = sS[wm * WM + 16 * t + r16] * ws;
+        v8i wf[TN];
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+            wf[u] = lds_fragment(sW, wn * WN + 16 * u + r16, g);
+        v4f d[2][TN];
+        {
+            const v8i af = lds_fragment(sA, wm * WM + r16, g);
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                d[0][u] = mfma_block(wf[u], af);
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            if (t + 1 < TM) {
+                const v8i af = lds_fragment(sA, wm * WM + 16 * (t + 1) + r16, g);
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    d[(t + 1) & 1][u] = mfma_block(wf[u], af);
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                acc[t][u] = fma4(d[t & 1][u], sc[t], acc[t][u]);
+        }
+    }
+    wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
+
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        const int m = m0 + wm * WM + 16 * t + r16;
+        if (m < M) {
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                store4(p.Y, (int64_t)m * N, n0 + wn * WN + 16 * u + 4 * g, N, vec_store != 0, acc[t][u]);
+        }
+    }
+}
+
+
 #define A8W8_TILE_INST(BM, BN, WGM, WGN, S) template __global__ void tile_kernel<BM, BN, WGM, WGN, S>(Args, int);
 A8W8_TILE_INST(256, 256, 2, 4, 2)
 A8W8_TILE_INST(256, 128, 2, 4, 3)
@@ -666,10 +866,6 @@ A8W8_TILE_INST(32, 128, 1, 4, 3)
 A8W8_TILE_INST(32, 64, 2, 2, 3)
 A8W8_TILE_INST(64, 32, 2, 2, 3)
 A8W8_TILE_INST(32, 32, 2, 2, 3)
-A8W8_TILE_INST(32, 32, 2, 2, 4)
-A8W8_TILE_INST(32, 32, 2, 2, 8)
-A8W8_TILE_INST(32, 64, 2, 2, 6)
-A8W8_TILE_INST(64, 64, 2, 2, 4)
 #undef A8W8_TILE_INST
 
 }  // namespace kern
@@ -696,20 +892,25 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 {
     return cmin(163840 / lds_bytes, wpc / waves) > 0 ? cmin(163840 / lds_bytes, wpc / waves) : 1;
 }
-#define TILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, \
-                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
+#define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
                                    reinterpret_cast<const void *>(&tile_kernel<BM, BN, WGM, WGN, S>), \
+                                   S * ((BM + BN) * 128 + WGM * WGN * 256)}
+#define PTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_PTILE, BM, BN, WGM * WGN, S, 0, \
+                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
+                                    "ptile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
+                                   reinterpret_cast<const void *>(&ptile_kernel<BM, BN, WGM, WGN, S>), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
     SKINNY(1, 3, 16), SKINNY(2, 3, 16), SKINNY(1, 10, 4), SKINNY(1, 12, 4), SKINNY(1, 2, 4),
-    TILE(256, 256, 2, 4, 2, 8), TILE(256, 128, 2, 4, 3, 8), TILE(128, 256, 2, 4, 3, 8), TILE(128, 128, 2, 2, 2, 8),
-    TILE(128, 128, 2, 2, 4, 8), TILE(128, 64, 2, 2, 3, 16), TILE(64, 128, 2, 2, 3, 8), TILE(64, 64, 2, 2, 3, 16),
-    TILE(128, 32, 4, 1, 3, 16), TILE(32, 128, 1, 4, 3, 16), TILE(32, 64, 2, 2, 3, 16),
-    TILE(64, 32, 2, 2, 3, 16), TILE(32, 32, 2, 2, 3, 16),
-    TILE(32, 32, 2, 2, 4, 16), TILE(32, 32, 2, 2, 8, 16), TILE(32, 64, 2, 2, 6, 16), TILE(64, 64, 2, 2, 4, 16),
+    TILE(256, 256, 2, 4, 2), TILE(256, 128, 2, 4, 3), TILE(128, 256, 2, 4, 3), TILE(128, 128, 2, 2, 2),
+    TILE(128, 128, 2, 2, 4), TILE(128, 64, 2, 2, 3), TILE(64, 128, 2, 2, 3), TILE(64, 64, 2, 2, 3),
+    TILE(128, 32, 4, 1, 3), TILE(32, 128, 1, 4, 3), TILE(32, 64, 2, 2, 3), TILE(64, 32, 2, 2, 3), TILE(32, 32, 2, 2, 3),
+    PTILE(256, 256, 2, 4, 2, 8), PTILE(256, 128, 2, 4, 3, 8), PTILE(128, 256, 2, 4, 3, 8), PTILE(128, 128, 2, 2, 2, 8),
+    PTILE(128, 128, 2, 2, 4, 8), PTILE(64, 64, 2, 2, 4, 16), PTILE(32, 64, 2, 2, 6, 16), PTILE(32, 32, 2, 2, 4, 16),
+    PTILE(32, 32, 2, 2, 8, 16),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -726,6 +927,8 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return (N + v.bn - 1) / v.bn;
     const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    if (v.kernel == A8W8_KERNEL_TILE)
+        return tiles;
     const int64_t slots = (int64_t)(cus > 0 ? cus : 1) * v.per_cu;
     return tiles < slots ? tiles : slots;
 }

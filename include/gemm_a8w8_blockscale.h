@@ -58,7 +58,8 @@ enum {
 /* Kernels behind the selector. */
 enum {
     A8W8_KERNEL_SKINNY = 1,  /* M <= 16: streams W once, K split over the waves of a workgroup */
-    A8W8_KERNEL_TILE = 2     /* LDS double-buffered fp8-MFMA output tiles                     */
+    A8W8_KERNEL_TILE = 2,    /* fp8-MFMA output tiles, one workgroup per tile, LDS ring       */
+    A8W8_KERNEL_PTILE = 3    /* fp8-MFMA output tiles, persistent workgroups, LDS ring        */
 };
 
 /*

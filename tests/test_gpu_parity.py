@@ -124,18 +124,18 @@ def test_every_instance_on_ragged_shape(variant):
     say(f"instance {info['name']} ok")
 
 
-def _tile_instances():
-    return [v for v in g.variants() if v["kernel_name"] == "tile"]
+def _persistent_instances():
+    return [v for v in g.variants() if v["kernel_name"] == "ptile"]
 
 
 @pytest.mark.parametrize("K", [128, 640])
-def test_every_tile_instance_loops_over_tiles(K):
-    """Each workgroup of the persistent tile grid takes several tiles: ragged
+def test_every_persistent_instance_loops_over_tiles(K):
+    """Each workgroup of a persistent tile grid takes several tiles: ragged
     M and N with at least twice as many tiles as workgroups (K = 128: one
     K block, so the copies run several tiles ahead)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rng = np.random.default_rng(11)
-    for v in _tile_instances():
+    for v in _persistent_instances():
         bm, bn = v["bm"], v["bn"]
         per_cu = g.gemm_a8w8_describe_variant(v["variant"], 1 << 24, 1 << 16, K)["grid"] // 256
         N = 3 * bn + 40
