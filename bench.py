@@ -14,6 +14,8 @@ prefill measurement (M >= 4096, fp8 TFLOP/s against the MFMA peak) and the
 oracle's own time on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--decode-nk N:K] [--decode-ms 1,2,...]   (other decode shapes, e.g. 34816:5120)
+       [--workload sweep]                         (the dense-M sweep report)
 """
 from __future__ import annotations
 
@@ -137,6 +139,9 @@ def main():
     ap.add_argument("--workload", choices=["decode", "sweep"], default="decode",
                     help="decode: the headline decode workload (default); sweep: dense-M sweep report")
     ap.add_argument("--sweep-out", default=None, help="where the sweep writes its per-point table (markdown)")
+    ap.add_argument("--decode-nk", default="14336:5120",
+                    help="N:K of the decode workload (default: the qkv shape 14336:5120)")
+    ap.add_argument("--decode-ms", default="1,2,4,8,16", help="M values the decode workload cycles through")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the run, copy 256 MiB device-to-device three times (traffic calibration)")
     args = ap.parse_args()
@@ -161,8 +166,11 @@ def main():
         return sweep(args, torch, g, inputgen, oracle)
 
     # ------------------------------------------------------------ decode, cold W
-    N, K = 14336, 5120
-    Ms = [1, 2, 4, 8, 16]
+    N, K = (int(x) for x in args.decode_nk.split(":"))
+    Ms = [int(x) for x in args.decode_ms.split(",")]
+    if K % 128 or not Ms or min(Ms) < 1 or max(Ms) > 16:
+        raise SystemExit("decode workload: K must be a multiple of 128 and every M in 1..16")
+    qkv = (N, K, Ms) == (14336, 5120, [1, 2, 4, 8, 16])
     t = time.time()
     A, a_s = inputgen.make_activations(16, K, seed=0)
     W0, w_s = inputgen.make_weights(N, K, seed=1)
@@ -275,14 +283,16 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8e4m3 x fp8e4m3 -> fp32 accumulate -> bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, 1x128 / 128x128 fp32 scales)",
-        "config": {"workload": f"decode qkv-like: M in {{1,2,4,8,16}}, N={N}, K={K}, cold weights "
+        "config": {"workload": f"decode{' qkv-like' if qkv else ''}: M in {{{','.join(map(str, Ms))}}}, "
+                               f"N={N}, K={K}, cold weights "
                                f"rotated over {R} copies ({R * w_bytes / 2**30:.2f} GiB); one step = one "
                                f"HIP-graph replay of {R} calls",
                    "calls_per_step": R, "rotate_bytes": R * w_bytes,
                    "table_hash": f"0x{g.gemm_a8w8_table_hash():016x}"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "kernel": "skinny (M<=16) weight-streaming kernel",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic() if qkv else None,
+                     "kernel": "M<=16 weight-streaming kernels: "
+                               + ", ".join(sorted({v["plan"] for v in per_m.values()})),
                      "bytes_per_launch": round(bytes_mean)},
         "per_m": per_m,
         "prefill": prefill,

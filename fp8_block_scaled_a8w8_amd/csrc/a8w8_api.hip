@@ -108,6 +108,8 @@ bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
     const Variant &v = a8w8::variant(id);
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return M <= v.max_m && skinny_fits(N, K);
+    if (v.kernel == A8W8_KERNEL_PSKINNY)
+        return M <= v.max_m && skinny_fits(N, K) && K / 128 <= (int64_t)v.waves * v.kblocks;
     return true;
 }
 

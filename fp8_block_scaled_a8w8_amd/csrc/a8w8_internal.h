@@ -8,12 +8,12 @@ namespace a8w8 {
 
 // One compiled kernel instance.
 struct Variant {
-    int32_t kernel;    // A8W8_KERNEL_SKINNY or A8W8_KERNEL_TILE
+    int32_t kernel;    // A8W8_KERNEL_*
     int32_t bm, bn;    // output tile per workgroup (skinny: 16 x 16 * tiles per wave)
     int32_t waves;     // waves per workgroup
-    int32_t kblocks;   // K blocks each wave loads (skinny), LDS ring depth (tile)
-    int32_t max_m;     // largest M the instance accepts (skinny: 16), 0 = any
-    int32_t per_cu;    // tile: workgroups per CU the persistent grid is sized for
+    int32_t kblocks;   // K blocks each wave loads (skinny, pskinny), LDS ring depth (tile)
+    int32_t max_m;     // largest M the instance accepts (skinny, pskinny: 16), 0 = any
+    int32_t per_cu;    // ptile, pskinny: workgroups per CU the persistent grid is sized for
     const char *name;
 };
 
@@ -30,9 +30,9 @@ struct Args {
 int num_variants();
 const Variant &variant(int id);
 // Workgroups the instance launches for (M, N, K) on a device with `cus`
-// compute units (tile: min(tiles, cus * per_cu), each workgroup looping over
-// its share of the tiles), and the passes over K one wave makes (skinny:
-// ceil(K/128 / (waves * kblocks)); tile: K/128 blocks per tile).
+// compute units (ptile, pskinny: min(tiles, cus * per_cu), each workgroup
+// looping over its share of the tiles), and the passes over K one wave makes
+// (skinny: ceil(K/128 / (waves * kblocks)); pskinny: 1; tile: K/128 blocks per tile).
 int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus);
 int64_t variant_passes(int id, int64_t K);
 // Raise the dynamic-LDS limit of the instances that need more than 64 KB

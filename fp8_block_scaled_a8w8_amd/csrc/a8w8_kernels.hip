@@ -224,6 +224,138 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent skinny kernel, M <= 16, for tall weights.  The skinny kernel
+// above gives a workgroup RG rows and all of K; when N is many times 16 x the
+// CU count that leaves either a partly filled last wave of workgroups (wide
+// row groups) or every workgroup fetching the whole M x K activation again
+// (16-row groups).  Here about one workgroup per CU walks the 16-row tiles
+// b, b + G, b + 2G, ... of W (G = grid size): each wave loads its activation
+// fragments once and keeps them in registers, and the weight loads of the
+// next tile are in flight while the current tile is multiplied.
+//
+// Wave w owns the K blocks [D w, D w + D) (the instance needs NW * D >= K/128).
+// Its weight loads run P - 1 tiles ahead of the tile it multiplies.  Per
+// tile it loads its blocks of the 16 weight rows with the whole-line
+// pattern of the skinny kernel (plus each block's w_scale, through the same
+// vector-memory queue so that one counter orders them), takes one MFMA and
+// one scale FMA per block, and writes its partial sum to one of two LDS
+// slots.  After one barrier the wave whose turn it is adds the NW partials in
+// wave order (fixed order: bitwise deterministic) and stores the 16 x 16
+// bf16 tile.  Loads for tiles past the workgroup's share go through a
+// descriptor of zero records, which returns zeros without touching memory.
+template <int D, int NW, int P>
+__global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
+{
+    __shared__ v4f red[2][NW][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
+    const int r16 = lane & 15, g = lane >> 4;
+    const bool mval = r16 < M;
+    const int ntiles = (N + 15) >> 4;
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int mine = b < ntiles ? (ntiles - 1 - b) / G + 1 : 0;
+    const int kb0 = wave * D;
+    const bool vec = vec_store != 0;
+
+    const int lrow = r16 & 7;
+    const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, (uint32_t)N * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.W, 0u);
+    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(p.w_scale, (uint32_t)((N + 127) >> 7) * (uint32_t)KB * 4u);
+
+    // This wave's activation blocks and scales, held for the whole kernel
+    // (put into the MFMA layout once the first weight loads are issued).
+    v4i araw[D][2];
+    v8i af[D];
+    float sa[D];
+    {
+        const float *asp = p.a_scale + (size_t)(mval ? r16 : 0) * KB;
+        uint32_t aoff[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = 8 * h + lrow;
+            aoff[h] = (uint32_t)(m < M ? m : 0) * (uint32_t)K + lcol;   // rows past M: row 0, never stored
+        }
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int kb = min(kb0 + j, KB - 1);   // blocks past K load a valid block, skipped below
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                araw[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[h], kb * 128, 0);
+            sa[j] = asp[kb];
+        }
+    }
+
+    // Issue the weight and w_scale loads of this workgroup's tile i.
+    auto load_tile = [&](int i, v4i (&wr)[D][2], float (&sw)[D]) {
+        const bool live = i < mine;
+        const int n0 = (b + (live ? i : 0) * G) * 16;
+        const __amdgpu_buffer_rsrc_t r = live ? wres : none;
+        uint32_t woff[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            woff[h] = (uint32_t)min(n0 + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
+        const int srow = (n0 >> 7) * KB;
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int kb = min(kb0 + j, KB - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wr[j][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[h], kb * 128, 2 /* nt */);
+            sw[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, 0, (srow + kb) * 4, 0));
+        }
+    };
+    // Multiply tile i, reduce it over the waves and store it.
+    auto finish_tile = [&](int i, const v4i (&wr)[D][2], const float (&sw)[D]) {
+        v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (kb0 + j < KB)
+                acc = fma4(mfma_block(fix_row_layout(wr[j][0], wr[j][1]), af[j]), sa[j] * sw[j], acc);
+        red[i & 1][wave][lane] = acc;
+        __syncthreads();
+        if (wave == i % NW) {
+            v4f v = red[i & 1][0][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                const v4f o = red[i & 1][w][lane];
+                v[0] += o[0];
+                v[1] += o[1];
+                v[2] += o[2];
+                v[3] += o[3];
+            }
+            if (mval)
+                store4(p.Y, (int64_t)r16 * N, (b + i * G) * 16 + 4 * g, N, vec, v);
+        }
+    };
+
+    // P register sets: the loads of tiles i+1 .. i+P-1 are in flight while
+    // tile i is finished.
+    v4i wr[P][D][2];
+    float sw[P][D];
+#pragma unroll
+    for (int q = 0; q + 1 < P; ++q)
+        load_tile(q, wr[q], sw[q]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        af[j] = fix_row_layout(araw[j][0], araw[j][1]);
+    // The grid never exceeds the tile count: every workgroup has a tile.
+    int i = 0;
+    do {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            load_tile(i + q + P - 1, wr[(q + P - 1) % P], sw[(q + P - 1) % P]);
+            if (i + q < mine)
+                finish_tile(i + q, wr[q], sw[q]);
+        }
+        i += P;
+    } while (i < mine);
+}
+
 // Direct global -> LDS copies.  Each wave instruction moves one value per lane
 // and writes them to consecutive LDS addresses starting at the wave-uniform
 // address in m0 (lane i at byte 16 i for the 16-byte form, 4 i for the 4-byte
@@ -403,7 +535,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     // and fetch the block STAGES steps ahead: a full ring of lookahead.
     constexpr bool LATE = TM <= 2;
     constexpr int AHEAD = LATE ? STAGES : STAGES - 1;
-    constexpr int SPREAD = LATE ? 1 : STAGES == 2 ? cmin(TM - 1, 6) : cmin(TM, 6);
+    constexpr int SPREAD = LATE ? 1 : STAGES == 2 ? cmin(TM - 1, 4) : cmin(TM, 4);
     constexpr int CPS = LATE ? PER_BLOCK : (PER_BLOCK + SPREAD - 1) / SPREAD;
     constexpr int C_BEFORE = LATE ? 0 : cmin(PER_BLOCK, cmin(SPREAD, TM - 1) * CPS);   // issued before the barrier
     // Copies a wave may still have in flight at a block's barrier: all of
@@ -411,6 +543,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     // in issue order; the stores of a finished tile only make this wait
     // stricter.)
     constexpr int VM_AT_BARRIER = (AHEAD - 2) * PER_BLOCK + C_BEFORE;
+    // VALU instructions issued after each MFMA (a slice's 4 * TN scale FMAs
+    // and its scale product go behind the first MFMAs).
+    constexpr int FMA_GROUP = 6;
     static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
                   "each wave copies whole 8-row groups of both tiles");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
@@ -543,17 +678,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     auto block = [&](int step, v4i ra, v4i rw, const float *s_src, int ckb) {
         const uint8_t *sA = smem + (step % STAGES) * STAGE;
         const uint32_t cstage = lds0 + (uint32_t)(((step + AHEAD) % STAGES) * STAGE);
-#pragma unroll
-        for (int u = 0; u < TN; ++u)
-            acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
 
-        // Scales are formed where they are used, so no wave waits for the
-        // scale reads of the previous block before its barrier.
+        // Slice t multiplies activation slice t and scales the MFMA results of
+        // slice t-1 (slice 0: the previous block's last slice).  Scales are
+        // formed where they are used, so no wave waits for the scale reads of
+        // the previous block before its barrier.
         v4f d[TN];
         float s_cur = 0.f;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const float sc_prev = t > 0 ? sa[t - 1] * ws : 0.f;
+            const float sc_prev = t > 0 ? sa[t - 1] * ws : s_last;
             if (t == TM - 1) {
                 wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of the next block have landed
                 __syncthreads();               // ... every wave's; this block's stage is read out
@@ -567,36 +701,53 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             if (t + 1 < TM)
                 af_next = lds_fragment(sA, arow + 16 * (t + 1), g);
             v4f dn[TN];
+            // Raised wave priority while this slice's MFMAs issue: the matrix
+            // core is fed first when both waves of a SIMD have work.
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int u = 0; u < TN; ++u)
                 dn[u] = mfma_block(wf[u], af);
             if (t == TM - 1) {
-                // The next block: its stage is complete (barrier above); these
-                // reads overwrite fragments the MFMAs just issued have already
-                // read.  After the last block they read a stale stage, unused.
+                // The next block: its stage is complete (barrier above).  Weight
+                // fragment u is read right after MFMA u has taken the old one.
+                // After the last block these read a stale stage, unused.
                 s_cur = sa[TM - 1] * ws;
-                __builtin_amdgcn_sched_barrier(0);
                 const uint8_t *nA = smem + ((step + 1) % STAGES) * STAGE, *nW = nA + A_BYTES;
                 const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
-                wf[0] = lds_fragment(nW, wrow, g);
-                af_next = lds_fragment(nA, arow, g);
 #pragma unroll
-                for (int u = 1; u < TN; ++u)
+                for (int u = 0; u < TN; ++u)
                     wf[u] = lds_fragment(nW, wrow + 16 * u, g);
+                af_next = lds_fragment(nA, arow, g);
 #pragma unroll
                 for (int s = 0; s < TM; ++s)
                     sa[s] = nS[arow + 16 * s];
                 ws = nS[ws_slot];
-                if (LATE) {
-#pragma unroll
-                    for (int j = 0; j < PER_BLOCK; ++j)
-                        issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
-                }
             }
-            if (t > 0) {
 #pragma unroll
-                for (int u = 0; u < TN; ++u)
+            for (int u = 0; u < TN; ++u) {
+                if (t > 0)
                     acc[t - 1][u] = fma4(d[u], sc_prev, acc[t - 1][u]);
+                else
+                    acc[TM - 1][u] = fma4(d_last[u], sc_prev, acc[TM - 1][u]);
+            }
+            // Issue order: the next slice's activation fragment reads first
+            // (most time to land), then each MFMA followed by a share of the
+            // scale FMAs, which run on the vector ALU while the matrix core
+            // works (in the last slice also the next block's weight fragment).
+            if (t + 1 < TM)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (t == TM - 1)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, FMA_GROUP, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            if (LATE && t == TM - 1) {
+#pragma unroll
+                for (int j = 0; j < PER_BLOCK; ++j)
+                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
             }
 #pragma unroll
             for (int u = 0; u < TN; ++u)
@@ -902,6 +1053,9 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
                                    reinterpret_cast<const void *>(&ptile_kernel<BM, BN, WGM, WGN, S>), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
+#define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
+                           reinterpret_cast<const void *>(&pskinny_kernel<D, NW, P>), 0}
+
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
     SKINNY(1, 3, 16), SKINNY(2, 3, 16), SKINNY(1, 10, 4), SKINNY(1, 12, 4), SKINNY(1, 2, 4),
@@ -911,6 +1065,7 @@ const Entry kEntries[] = {
     PTILE(256, 256, 2, 4, 2, 8), PTILE(256, 128, 2, 4, 3, 8), PTILE(128, 256, 2, 4, 3, 8), PTILE(128, 128, 2, 2, 2, 8),
     PTILE(128, 128, 2, 2, 4, 8), PTILE(64, 64, 2, 2, 4, 16), PTILE(32, 64, 2, 2, 6, 16), PTILE(32, 32, 2, 2, 4, 16),
     PTILE(32, 32, 2, 2, 8, 16),
+    PSKINNY(5, 8, 2), PSKINNY(4, 10, 3), PSKINNY(6, 8, 2),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -926,6 +1081,13 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return (N + v.bn - 1) / v.bn;
+    if (v.kernel == A8W8_KERNEL_PSKINNY) {
+        // As few workgroups as still give each the fewest tiles the slots
+        // allow, so that all but the last few take exactly that many.
+        const int64_t tiles16 = (N + 15) / 16, slots = (int64_t)(cus > 0 ? cus : 1) * v.per_cu;
+        const int64_t each = (tiles16 + slots - 1) / slots;
+        return (tiles16 + each - 1) / each;
+    }
     const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
     if (v.kernel == A8W8_KERNEL_TILE)
         return tiles;
@@ -936,6 +1098,8 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
 int64_t variant_passes(int id, int64_t K)
 {
     const Variant &v = kEntries[id].v;
+    if (v.kernel == A8W8_KERNEL_PSKINNY)
+        return 1;
     if (v.kernel != A8W8_KERNEL_SKINNY)
         return K / 128;
     const int64_t per_pass = (int64_t)v.waves * v.kblocks;

@@ -46,11 +46,15 @@ def key_grid(limit: int = 8192) -> list[int]:
     return keys
 
 
-def candidates(M: int, N: int) -> list[dict]:
+def candidates(M: int, N: int, K: int) -> list[dict]:
     out = []
     for v in variants():
         if v["kernel_name"] == "skinny":
             if M <= 16:
+                out.append(v)
+            continue
+        if v["kernel_name"] == "pskinny":
+            if M <= 16 and K // 128 <= v["waves"] * v["kblocks"]:
                 out.append(v)
             continue
         # tile instances: skip tiles far taller than M and tiles much wider than N
@@ -110,7 +114,7 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log) 
         if key in done:
             rows.append(done[key])
             continue
-        cands = candidates(M, N)
+        cands = candidates(M, N, K)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         graphs = {}
         for v in cands:

@@ -80,6 +80,18 @@ def test_run_variant_rejects_skinny_above_16_rows():
     assert rc == g.A8W8_ERR_PLAN
 
 
+def test_run_variant_rejects_persistent_skinny_beyond_its_k():
+    ps = [v for v in g.variants() if v["kernel_name"] == "pskinny"]
+    assert ps
+    for v in ps:
+        kb = v["waves"] * v["kblocks"]
+        lib = g.lib()
+        assert lib.gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, 17, 512, 128 * kb,
+                                                    None) == g.A8W8_ERR_PLAN
+        assert lib.gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, 4, 512, 128 * (kb + 1),
+                                                    None) == g.A8W8_ERR_PLAN
+
+
 def test_variant_shapes_are_launchable():
     for v in g.variants():
         if v["kernel_name"] in ("tile", "ptile"):

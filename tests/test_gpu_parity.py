@@ -116,7 +116,7 @@ def test_every_instance_on_ragged_shape(variant):
         pytest.skip("no such instance")
     info = g.gemm_a8w8_describe_variant(variant)
     K = 640
-    for (M, N) in ([(1, 300), (7, 130), (16, 64)] if info["kernel_name"] == "skinny"
+    for (M, N) in ([(1, 300), (7, 130), (16, 64)] if info["kernel_name"] in ("skinny", "pskinny")
                    else [(77, 300), (200, 520), (33, 32)]):
         A, a_s, W, w_s = _inputs(M, N, K, a_seed=10 + M, w_seed=20 + N)
         y = run(*to_dev(A, a_s, W, w_s), variant=variant)
@@ -149,6 +149,27 @@ def test_every_persistent_instance_loops_over_tiles(K):
                            f"{v['name']} M={M} N={N} K={K}")
         say(f"instance {v['name']} M={M} N={N} K={K}: {tiles_m * tiles_n} tiles on "
             f"{min(tiles_m * tiles_n, cus * per_cu)} workgroups, rel_l2={st['rel_l2']:.3e}")
+        del y
+
+
+def _persistent_skinny_instances():
+    return [v for v in g.variants() if v["kernel_name"] == "pskinny"]
+
+
+def test_every_persistent_skinny_instance_loops_over_tiles():
+    """Each workgroup of a persistent skinny grid walks two or three 16-row
+    tiles (ragged last tile), at K = 128 (one block: most waves idle), at the
+    largest K the instance takes, and at a K that leaves the last wave's run
+    of blocks short."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 16 * (2 * cus + 37) + 5
+    for v in _persistent_skinny_instances():
+        kb_max = v["waves"] * v["kblocks"]
+        for K, M in ((128, 16), (128 * kb_max, 9), (128 * (kb_max - v["kblocks"] // 2 - 1), 1)):
+            A, a_s, W, w_s = _inputs(M, N, K, a_seed=50 + M, w_seed=60 + K // 128)
+            y = run(*to_dev(A, a_s, W, w_s), variant=v["variant"])
+            st = assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{v['name']} M={M} N={N} K={K}")
+            say(f"instance {v['name']} M={M} N={N} K={K}: rel_l2={st['rel_l2']:.3e}")
         del y
 
 
