@@ -27,7 +27,7 @@ A8W8_ERR_ALIGN = 3
 A8W8_ERR_ARCH = 4
 A8W8_ERR_HIP = 5
 A8W8_ERR_PLAN = 6
-KERNEL_NAMES = {1: "skinny", 2: "tile", 3: "ptile", 4: "pskinny"}
+KERNEL_NAMES = {1: "skinny", 2: "tile", 3: "ptile", 4: "pskinny", 5: "tall"}
 
 EXPORTED = (
     "gemm_a8w8_blockscale",

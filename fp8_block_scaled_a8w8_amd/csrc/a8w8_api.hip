@@ -97,7 +97,7 @@ int check_pointers(const void *A, const float *a_scale, const void *W, const flo
     return A8W8_OK;
 }
 
-// The skinny kernel addresses A and W with 32-bit per-lane offsets.
+// The skinny and tall kernels address A and W with 32-bit per-lane offsets.
 bool skinny_fits(int64_t N, int64_t K)
 {
     return N * K < ((int64_t)1 << 32) && 16 * K < ((int64_t)1 << 32);
@@ -110,6 +110,8 @@ bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
         return M <= v.max_m && skinny_fits(N, K);
     if (v.kernel == A8W8_KERNEL_PSKINNY)
         return M <= v.max_m && skinny_fits(N, K) && K / 128 <= (int64_t)v.waves * v.kblocks;
+    if (v.kernel == A8W8_KERNEL_TALL)
+        return N <= v.bn && skinny_fits(N, K) && skinny_fits(M, K);
     return true;
 }
 
@@ -127,8 +129,10 @@ int find_variant(int kernel, int bm, int bn, int waves, int kblocks)
 // Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
 // with the widest row group that still yields at least ~200 workgroups (wider
 // groups share each activation fragment across more weight tiles), covering
-// K in one pass with the fewest blocks per wave.  Above: the largest tile that
-// still gives every compute unit at least two workgroups, else the smallest.
+// K in one pass with the fewest blocks per wave.  Above, for N <= 32: the
+// tall kernel (16-row activation groups, 16 waves; 32-row groups from
+// M = 4096).  Otherwise the largest tile that still gives every compute unit
+// at least two workgroups, else the smallest.
 int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
 {
     if (M <= 16 && skinny_fits(N, K)) {
@@ -150,6 +154,13 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
         }
         if (best >= 0)
             return best;
+    }
+    if (N <= 32 && skinny_fits(N, K) && skinny_fits(M, K)) {
+        const int bn = N <= 16 ? 16 : 32;
+        const int id = M < 4096 ? find_variant(A8W8_KERNEL_TALL, 16, bn, bn == 32 ? 16 : 8, 3)
+                                : find_variant(A8W8_KERNEL_TALL, 32, bn, 8, bn == 32 ? 6 : 3);
+        if (id >= 0)
+            return id;
     }
     static const int kTiles[][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}, {32, 64}, {32, 32}};
     const int nt = (int)(sizeof(kTiles) / sizeof(kTiles[0]));

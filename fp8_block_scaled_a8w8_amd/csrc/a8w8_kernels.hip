@@ -356,6 +356,120 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
     } while (i < mine);
 }
 
+// ---------------------------------------------------------------------------
+// Tall kernel, N <= 16 * NT (a few weight rows, many activation rows): the
+// skinny kernel with the roles of the two dimensions exchanged.  Here the
+// activations are the stream read once from HBM and the small weight matrix
+// is re-read from L2.  A workgroup owns 16 * TPW activation rows and all N;
+// its NW waves split K into runs of D blocks exactly as in the skinny kernel
+// (same whole-line loads and DPP fix, same operand roles: W is the MFMA "A"
+// operand, so a lane's four outputs are four consecutive columns of one
+// output row and take one a_scale per block).  Per block: TPW * NT MFMAs,
+// each followed by one scale FMA per output; the wave partials are summed
+// through LDS in wave order and rounded once.
+template <int TPW, int NT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
+    const int m0 = (int)blockIdx.x * (16 * TPW);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int lrow = r16 & 7;
+    const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, (uint32_t)N * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
+    // Rows past N or M load the last row: they only feed outputs that are never stored.
+    uint32_t woff[NT][2], aoff[TPW][2];
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            woff[u][h] = (uint32_t)min(16 * u + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            aoff[t][h] = (uint32_t)min(m0 + 16 * t + 8 * h + lrow, M - 1) * (uint32_t)K + lcol;
+    const float *asp[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        asp[t] = p.a_scale + (size_t)min(m0 + 16 * t + r16, M - 1) * KB;
+    // 16 * NT <= 128: every weight row lies in weight block 0.
+    const float *wsp = p.w_scale;
+
+    v4f acc[TPW][NT];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+            acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
+        v4i wr[D][NT][2], ar[D][TPW][2];
+        float sa[D][TPW], sw[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int kb = min(kb_begin + j, KB - 1);   // blocks past the end load a valid block, skipped below
+            const int koff = kb * 128;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    ar[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[t][h], koff, 2 /* nt */);
+#pragma unroll
+            for (int u = 0; u < NT; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wr[j][u][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[u][h], koff, 0);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                sa[j][t] = asp[t][kb];
+            sw[j] = wsp[kb];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            if (kb_begin + j < KB) {
+                v8i wf[NT];
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    wf[u] = fix_row_layout(wr[j][u][0], wr[j][u][1]);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const v8i af = fix_row_layout(ar[j][t][0], ar[j][t][1]);
+                    const float sc = sa[j][t] * sw[j];
+#pragma unroll
+                    for (int u = 0; u < NT; ++u)
+                        acc[t][u] = fma4(mfma_block(wf[u], af), sc, acc[t][u]);
+                }
+            }
+        }
+    }
+
+    __shared__ v4f red[NW][TPW * NT][64];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+            red[wave][t * NT + u][lane] = acc[t][u];
+    __syncthreads();
+    for (int i = wave; i < TPW * NT; i += NW) {
+        v4f v = red[0][i][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            const v4f o = red[w][i][lane];
+            v[0] += o[0];
+            v[1] += o[1];
+            v[2] += o[2];
+            v[3] += o[3];
+        }
+        const int m = m0 + 16 * (i / NT) + r16;
+        if (m < M)
+            store4(p.Y, (int64_t)m * N, 16 * (i % NT) + 4 * g, N, vec_store != 0, v);
+    }
+}
+
 // Direct global -> LDS copies.  Each wave instruction moves one value per lane
 // and writes them to consecutive LDS addresses starting at the wave-uniform
 // address in m0 (lane i at byte 16 i for the 16-byte form, 4 i for the 4-byte
@@ -1053,6 +1167,9 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
                                    reinterpret_cast<const void *>(&ptile_kernel<BM, BN, WGM, WGN, S>), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
+#define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, \
+                               "tall_r" #TPW "_n" #NT "_d" #D "_w" #NW}, \
+                              reinterpret_cast<const void *>(&tall_kernel<TPW, NT, D, NW>), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
                            reinterpret_cast<const void *>(&pskinny_kernel<D, NW, P>), 0}
 
@@ -1066,6 +1183,8 @@ const Entry kEntries[] = {
     PTILE(128, 128, 2, 2, 4, 8), PTILE(64, 64, 2, 2, 4, 16), PTILE(32, 64, 2, 2, 6, 16), PTILE(32, 32, 2, 2, 4, 16),
     PTILE(32, 32, 2, 2, 8, 16),
     PSKINNY(5, 8, 2), PSKINNY(4, 10, 3), PSKINNY(6, 8, 2),
+    TALL(1, 2, 3, 8), TALL(2, 2, 3, 8), TALL(4, 2, 3, 8), TALL(2, 2, 6, 8), TALL(1, 2, 6, 8), TALL(1, 2, 3, 16),
+    TALL(1, 1, 3, 8), TALL(2, 1, 3, 8), TALL(4, 1, 3, 8),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -1081,6 +1200,8 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return (N + v.bn - 1) / v.bn;
+    if (v.kernel == A8W8_KERNEL_TALL)
+        return (M + v.bm - 1) / v.bm;
     if (v.kernel == A8W8_KERNEL_PSKINNY) {
         // As few workgroups as still give each the fewest tiles the slots
         // allow, so that all but the last few take exactly that many.
@@ -1100,7 +1221,7 @@ int64_t variant_passes(int id, int64_t K)
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_PSKINNY)
         return 1;
-    if (v.kernel != A8W8_KERNEL_SKINNY)
+    if (v.kernel != A8W8_KERNEL_SKINNY && v.kernel != A8W8_KERNEL_TALL)
         return K / 128;
     const int64_t per_pass = (int64_t)v.waves * v.kblocks;
     return (K / 128 + per_pass - 1) / per_pass;

@@ -57,6 +57,10 @@ def candidates(M: int, N: int, K: int) -> list[dict]:
             if M <= 16 and K // 128 <= v["waves"] * v["kblocks"]:
                 out.append(v)
             continue
+        if v["kernel_name"] == "tall":
+            if N <= v["bn"] < 2 * max(N, 16):
+                out.append(v)
+            continue
         # tile instances: skip tiles far taller than M and tiles much wider than N
         if v["bm"] > max(32, 2 * M) or (N <= 32 and v["bn"] > 32) or v["bn"] > max(32, 2 * N):
             continue

@@ -60,7 +60,8 @@ enum {
     A8W8_KERNEL_SKINNY = 1,  /* M <= 16: streams W once, K split over the waves of a workgroup */
     A8W8_KERNEL_TILE = 2,    /* fp8-MFMA output tiles, one workgroup per tile, LDS ring       */
     A8W8_KERNEL_PTILE = 3,   /* fp8-MFMA output tiles, persistent workgroups, LDS ring        */
-    A8W8_KERNEL_PSKINNY = 4  /* M <= 16, tall W: about one workgroup per CU walks 16-row tiles */
+    A8W8_KERNEL_PSKINNY = 4, /* M <= 16, tall W: about one workgroup per CU walks 16-row tiles */
+    A8W8_KERNEL_TALL = 5     /* N <= 32: streams A once, K split over the waves of a workgroup */
 };
 
 /*
@@ -72,8 +73,8 @@ typedef struct {
     int32_t variant;    /* index in [0, gemm_a8w8_num_variants())                         */
     int32_t bm, bn;     /* output tile of one workgroup: rows of Y (M) x columns (N)      */
     int32_t waves;      /* waves (64 lanes) per workgroup                                 */
-    int32_t kblocks;    /* 128-wide K blocks one wave loads at once (skinny, pskinny); LDS ring depth (tile) */
-    int32_t kpasses;    /* passes over K per wave (skinny), K/128 steps per tile (tile)   */
+    int32_t kblocks;    /* 128-wide K blocks one wave loads at once (skinny, pskinny, tall); LDS ring depth (tile) */
+    int32_t kpasses;    /* passes over K per wave (skinny, tall), K/128 steps per tile (tile) */
     int32_t fallback;   /* 1: (N,K) has no tuned table, a heuristic plan was chosen       */
     int64_t grid;       /* workgroups launched for this shape (tile: persistent, at most  */
                         /* a few per CU, each looping over its share of the output tiles) */
@@ -106,7 +107,8 @@ int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
 /*
  * Run a specific instance (for tuning).  Same contract as gemm_a8w8_blockscale;
  * returns A8W8_ERR_PLAN if the instance cannot handle the shape (the skinny
- * kernels need M <= 16; a pskinny instance also needs K/128 <= waves * kblocks).
+ * kernels need M <= 16, a pskinny instance also K/128 <= waves * kblocks; a
+ * tall instance needs N <= its bn).
  */
 int gemm_a8w8_blockscale_run_variant(int32_t variant,
                                      const void *A, const float *a_scale,

@@ -98,6 +98,8 @@ def test_variant_shapes_are_launchable():
             assert v["bm"] % 32 == 0 and v["bn"] % 32 == 0 and v["bn"] // 2 <= 128
             assert 128 % (v["bn"] // 2) == 0, v          # a wave's columns stay in one weight block
             assert 2 * (v["bm"] + v["bn"]) * 128 <= 160 * 1024
+        elif v["kernel_name"] == "tall":
+            assert v["bn"] in (16, 32) and v["bm"] in (16, 32, 64), v     # all weight rows in weight block 0
         else:
             assert v["bm"] == 16 and v["bn"] in (16, 32, 64, 128), v   # row group inside one weight block
             assert v["waves"] >= 1 and v["kblocks"] >= 1
@@ -156,3 +158,7 @@ def test_unregistered_shape_falls_back_not_fails():
     assert p["fallback"] == 1 and p["kernel_name"] == "tile"
     tiles = ((5000 + p["bm"] - 1) // p["bm"]) * ((1000 + p["bn"] - 1) // p["bn"])
     assert min(tiles, 256) <= p["grid"] <= tiles          # persistent: at most one workgroup per tile
+    for n, m in ((8, 100), (17, 100), (32, 5000), (12, 9000)):
+        p = g.gemm_a8w8_blockscale_plan(m, n, 384)
+        assert p["fallback"] == 1 and p["kernel_name"] == "tall" and n <= p["bn"], (n, m, p)
+        assert p["grid"] == (m + p["bm"] - 1) // p["bm"]

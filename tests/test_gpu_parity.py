@@ -110,14 +110,19 @@ def test_dense_m_sweep_sampled_rows(N, K):
 
 # ---------------------------------------------------------------- every compiled instance
 
-@pytest.mark.parametrize("variant", range(40))
+@pytest.mark.parametrize("variant", range(64))
 def test_every_instance_on_ragged_shape(variant):
     if variant >= g.gemm_a8w8_num_variants():
         pytest.skip("no such instance")
     info = g.gemm_a8w8_describe_variant(variant)
     K = 640
-    for (M, N) in ([(1, 300), (7, 130), (16, 64)] if info["kernel_name"] in ("skinny", "pskinny")
-                   else [(77, 300), (200, 520), (33, 32)]):
+    if info["kernel_name"] in ("skinny", "pskinny"):
+        shapes = [(1, 300), (7, 130), (16, 64)]
+    elif info["kernel_name"] == "tall":
+        shapes = [(300, info["bn"]), (1000, info["bn"] - 5), (77, 3), (5, info["bn"])]
+    else:
+        shapes = [(77, 300), (200, 520), (33, 32)]
+    for (M, N) in shapes:
         A, a_s, W, w_s = _inputs(M, N, K, a_seed=10 + M, w_seed=20 + N)
         y = run(*to_dev(A, a_s, W, w_s), variant=variant)
         assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{info['name']} M={M} N={N}")
@@ -171,6 +176,18 @@ def test_every_persistent_skinny_instance_loops_over_tiles():
             st = assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{v['name']} M={M} N={N} K={K}")
             say(f"instance {v['name']} M={M} N={N} K={K}: rel_l2={st['rel_l2']:.3e}")
         del y
+
+
+def test_every_tall_instance_several_k_passes():
+    """K = 6144 takes two or more passes of the waves over K; ragged M and N."""
+    K = 6144
+    for v in [v for v in g.variants() if v["kernel_name"] == "tall"]:
+        M = 3 * v["bm"] + 5
+        for N in (v["bn"], v["bn"] - 3):
+            A, a_s, W, w_s = _inputs(M, N, K, a_seed=70 + M, w_seed=80 + N)
+            y = run(*to_dev(A, a_s, W, w_s), variant=v["variant"])
+            st = assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{v['name']} M={M} N={N} K={K}")
+            say(f"instance {v['name']} M={M} N={N} K={K}: rel_l2={st['rel_l2']:.3e}")
 
 
 # ---------------------------------------------------------------- bitwise invariants
