@@ -228,7 +228,7 @@ def test_doubling_activation_scales_doubles_output(M, N, K):
     assert np.array_equal(y2, 2 * y1)
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 14336, 5120), (1000, 2048, 1024)])
+@pytest.mark.parametrize("M,N,K", [(4, 14336, 5120), (1000, 2048, 1024), (8, 34816, 5120), (300, 32, 6144)])
 def test_repeat_calls_bitwise_identical(M, N, K):
     A, a_s, W, w_s = _inputs(M, N, K)
     d = to_dev(A, a_s, W, w_s)
@@ -239,7 +239,7 @@ def test_repeat_calls_bitwise_identical(M, N, K):
 
 def test_graph_replay_matches_eager():
     cases = []
-    for (M, N, K) in ((2, 14336, 5120), (600, 1536, 1024)):
+    for (M, N, K) in ((2, 14336, 5120), (600, 1536, 1024), (5, 34816, 5120), (700, 32, 6144)):
         A, a_s, W, w_s = _inputs(M, N, K)
         d = to_dev(A, a_s, W, w_s)
         eager = y_bits(run(*d))
@@ -249,8 +249,8 @@ def test_graph_replay_matches_eager():
     s.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
-        run(*cases[0][0], out=cases[0][1])      # warm-up on the capture stream
-        run(*cases[1][0], out=cases[1][1])
+        for d, out, _ in cases:                  # warm-up on the capture stream
+            run(*d, out=out)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=s):
@@ -269,7 +269,8 @@ def test_graph_replay_matches_eager():
 # ---------------------------------------------------------------- bounds
 
 @pytest.mark.parametrize("M,N,K", [(1, 32, 6144), (5, 130, 256), (17, 32, 6144), (33, 300, 384),
-                                   (255, 256, 6144), (257, 520, 640), (6016, 96, 256)])
+                                   (255, 256, 6144), (257, 520, 640), (6016, 96, 256), (9, 34816, 5120),
+                                   (100, 30, 640), (4100, 20, 256)])
 def test_output_guard_bands_untouched(M, N, K):
     A, a_s, W, w_s = _inputs(M, N, K, a_seed=M, w_seed=N)
     pad = 64
