@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for the a8w8 block-scale GEMM -- TEST INFRASTRUCTURE ONLY.
+"""CPU fp64 oracle for the a8w8 block-scale GEMM and its activation
+quantisation step -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never does, and the
@@ -8,7 +9,10 @@ loops (``a8w8_oracle.c``, plain C in fp64).
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (exact rational brute force, exact doubling, zero scales, identity-like and
 permutation weights, a numpy float64 matmul special case, the bf16 rounding
-floor printed on the "Retune gfx942 ... a8w8 blockscale decode rows" page).
+floor printed on the "Retune gfx942 ... a8w8 blockscale decode rows" page;
+for ``quantize_1x128``: hand-derived codes at rounding ties, torch's fp8 cast
+of the same quotients, zero groups, the group maximum, the half-spacing
+error bound).
 """
 from __future__ import annotations
 
@@ -100,3 +104,51 @@ def gemm(A: np.ndarray, a_scale: np.ndarray, W: np.ndarray, w_scale: np.ndarray,
     if rc != 0:
         raise RuntimeError("a8w8_oracle_gemm failed with code %d" % rc)
     return Y
+
+
+FP8_MAX = 448.0      # largest finite e4m3fn magnitude (code 0x7E)
+
+
+def quantize_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per 1 x 128 activation quantisation, the step upstream of the GEMM.
+
+    The pages name the activation operand of the op only as "FP8" with
+    per-group scales; this is the project's reading (the one its inputs are
+    generated with): for each row and 128-wide group along K,
+    ``s = fp32(amax / 448)`` and each value becomes the e4m3fn code nearest
+    to ``clamp(fp32(x / s), -448, 448)`` (ties to the even code; the sign bit
+    follows the sign of the fp32 quotient, so a negative value that rounds to
+    zero gives 0x80).  A group with amax 0 gets ``s = 0`` and all-zero codes.
+    The quotient decides an integer, so it is formed in fp32 here exactly as
+    the kernel forms it (IEEE division, round to nearest even); the encoding
+    step is exact (a search over the oracle's own table of code values).
+
+    x: float32 [M, K] (finite), K % 128 == 0.  Returns (codes uint8 [M, K],
+    scales float32 [M, K/128]).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    g = x.reshape(M, K // 128, 128)
+    amax = np.abs(g).max(axis=-1)                                    # exact
+    s = (amax / np.float32(FP8_MAX)).astype(np.float32)              # fp32 division
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        y = (g / safe[..., None]).astype(np.float32)                 # fp32 division
+    y = np.clip(y, np.float32(-FP8_MAX), np.float32(FP8_MAX))
+    # Non-negative finite codes 0x00..0x7E have strictly increasing values.
+    vals = e4m3fn_table()[:0x7F]
+    mag = np.abs(y.astype(np.float64)).ravel()
+    hi = np.searchsorted(vals, mag, side="left")                     # vals[hi] >= mag
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - vals[lo]
+    d_hi = vals[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(mag == vals[hi], hi, code).astype(np.uint8)      # exact hits
+    code = code | (np.signbit(y.ravel()).astype(np.uint8) << 7)
+    code = code.reshape(M, K // 128, 128)
+    code = np.where((s > 0)[..., None], code, np.uint8(0))
+    return np.ascontiguousarray(code.reshape(M, K)), s

@@ -261,3 +261,75 @@ def test_dequantisation_direction_against_unquantised_product(decode_like):
     ref = xa @ xw.T
     rel = np.linalg.norm(Y - ref) / np.linalg.norm(ref)
     assert 2e-2 < rel < 5e-2, rel
+
+
+# ---------------------------------------------------------------- activation quantisation
+
+def _group_with(values, amax=448.0):
+    """One 1 x 128 group: the given values, then zeros, with one element = amax (so s = amax/448)."""
+    g = np.zeros(128, dtype=np.float32)
+    g[0] = amax
+    g[1:1 + len(values)] = np.asarray(values, dtype=np.float32)
+    return g
+
+
+def test_quantize_ties_and_boundaries_hand_derived():
+    """amax = 448 gives s = 1 exactly, so each code is the e4m3fn rounding of the value itself.
+    Expected bytes worked out by hand from the format (bias 7, 3 mantissa bits, subnormal
+    step 2^-9, largest finite 448 = 0x7E), ties going to the even mantissa."""
+    cases = [
+        (2.0 ** -10, 0x00),            # half of the smallest subnormal: tie -> 0 (even)
+        (1.5 * 2.0 ** -9, 0x02),       # between 1 and 2 subnormal steps: tie -> 2
+        (7.5 * 2.0 ** -9, 0x08),       # between 7 * 2^-9 and 2^-6: tie -> 0x08 (smallest normal)
+        (1.0625, 0x38),                # between 1.0 (0x38) and 1.125 (0x39): tie -> 0x38
+        (1.1875, 0x3A),                # between 1.125 (0x39) and 1.25 (0x3A): tie -> 0x3A
+        (432.0, 0x7E),                 # between 416 (0x7D) and 448 (0x7E): tie -> 0x7E
+        (-3.0, 0xC4),                  # -1.5 * 2^1: sign 1, exponent field 8, mantissa 4
+        (-(2.0 ** -12), 0x80),         # negative value rounding to zero keeps the sign bit
+        (0.1, 0x1D),                   # 0.1 -> 1.625 * 2^-4 = 0.1015625 (nearest): 0x1D
+    ]
+    g = _group_with([v for v, _ in cases])
+    q, s = oracle.quantize_1x128(g[None, :])
+    assert s[0, 0] == np.float32(1.0)
+    got = [int(c) for c in q[0, 1:1 + len(cases)]]
+    assert got == [c for _, c in cases], [hex(c) for c in got]
+    assert q[0, 0] == 0x7E and np.all(q[0, 1 + len(cases):] == 0)
+
+
+def test_quantize_matches_torch_fp8_cast_of_the_same_quotient():
+    """Library special case: torch's float8_e4m3fn cast (round to nearest even) of the same
+    fp32 quotients gives the same bytes, and the scales are amax / 448 in fp32."""
+    x = torch.randn(37, 1024, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).float()
+    x[5, 128:256] = 0.0                                   # a zero group
+    x[6, :128] *= 1e-30                                   # tiny values
+    q, s = oracle.quantize_1x128(x.numpy())
+    g = x.reshape(37, 8, 128)
+    amax = g.abs().amax(-1)
+    s_ref = (amax / 448.0).to(torch.float32)
+    assert np.array_equal(s, s_ref.numpy())
+    safe = torch.where(s_ref > 0, s_ref, torch.ones_like(s_ref))
+    y = (g / safe[..., None]).clamp(-448.0, 448.0)
+    ref = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(37, 1024).numpy()
+    ref = np.where(np.repeat((s_ref > 0).numpy(), 128, axis=1), ref, 0)
+    assert np.array_equal(q, ref)
+
+
+def test_quantize_zero_group_max_element_and_error_bound():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((6, 512)).astype(np.float32)
+    x[2, 256:384] = 0.0
+    q, s = oracle.quantize_1x128(x)
+    assert s[2, 2] == 0 and np.all(q[2, 256:384] == 0)
+    table = oracle.e4m3fn_table()
+    for m in range(6):
+        for gi in range(4):
+            grp = x[m, 128 * gi:128 * gi + 128].astype(np.float64)
+            if s[m, gi] == 0:
+                continue
+            k = int(np.argmax(np.abs(grp)))
+            assert q[m, 128 * gi + k] in (0x7E, 0xFE)               # the group maximum maps to +-448
+            deq = table[q[m, 128 * gi:128 * gi + 128]] * float(s[m, gi])
+            # e4m3fn spacing at |v| is at most 2^(floor(log2|v|) - 3) (2^-9 below 2^-6)
+            v = np.abs(grp) / float(s[m, gi])
+            spacing = np.where(v >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(v, 1e-300))) - 3), 2.0 ** -9)
+            assert np.all(np.abs(deq - grp) <= 0.5 * spacing * float(s[m, gi]) * (1 + 1e-6))
