@@ -38,6 +38,7 @@ EXPORTED = (
     "gemm_a8w8_variant_name",
     "gemm_a8w8_status_string",
     "gemm_a8w8_table_hash",
+    "a8w8_quantize_1x128",
 )
 
 
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_status_string.argtypes = [ctypes.c_int]
         L.gemm_a8w8_table_hash.restype = ctypes.c_uint64
         L.gemm_a8w8_table_hash.argtypes = []
+        L.a8w8_quantize_1x128.restype = ctypes.c_int
+        L.a8w8_quantize_1x128.argtypes = [vp] * 3 + [i64] * 2 + [vp]
         _lib = L
     return _lib
 
@@ -184,6 +187,30 @@ def gemm_a8w8_blockscale_run_variant(variant: int, A, a_scale, W, w_scale, out=N
     if rc != A8W8_OK:
         raise A8W8Error(rc, f"gemm_a8w8_blockscale_run_variant({variant})")
     return out
+
+
+def quantize_1x128(X: torch.Tensor, out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                   stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 activations [M,K] -> (e4m3fn codes [M,K], fp32 scales [M,K/128]), one scale per 1x128 group.
+
+    The A / a_scale operands of gemm_a8w8_blockscale (see a8w8_quantize_1x128 in the C header)."""
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or not X.is_cuda or not X.is_contiguous():
+        raise ValueError("X must be a contiguous bfloat16 [M,K] GPU tensor")
+    M, K = X.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=X.device)
+    elif out.dtype not in (torch.float8_e4m3fn, torch.uint8) or tuple(out.shape) != (M, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float8_e4m3fn (or uint8) [M,K] tensor")
+    if scale_out is None:
+        scale_out = torch.empty((M, K // 128), dtype=torch.float32, device=X.device)
+    elif scale_out.dtype != torch.float32 or tuple(scale_out.shape) != (M, K // 128) or not scale_out.is_contiguous():
+        raise ValueError("scale_out must be a contiguous float32 [M,K/128] tensor")
+    rc = lib().a8w8_quantize_1x128(X.data_ptr(), out.data_ptr(), scale_out.data_ptr(), M, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "a8w8_quantize_1x128")
+    return out, scale_out
 
 
 def variants() -> list[dict]:

@@ -355,4 +355,25 @@ const char *gemm_a8w8_status_string(int status)
 
 uint64_t gemm_a8w8_table_hash(void) { return a8w8_table::kTableHash; }
 
+int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64_t K, void *stream)
+{
+    if (M < 0 || K < 1 || (K % 128) != 0 || M > kMaxDim || K > kMaxK)
+        return A8W8_ERR_SHAPE;
+    if (M == 0)
+        return A8W8_OK;
+    if (!X || !A || !a_scale)
+        return A8W8_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(X) & 15) || (reinterpret_cast<uintptr_t>(A) & 7) ||
+        (reinterpret_cast<uintptr_t>(a_scale) & 3))
+        return A8W8_ERR_ALIGN;
+    int cus = 0;
+    const int rc = device_ready(&cus);
+    if (rc != A8W8_OK)
+        return rc;
+    if (a8w8::launch_quant_1x128(X, A, a_scale, M * (K / 128), cus, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return A8W8_ERR_HIP;
+    return A8W8_OK;
+}
+
 }  // extern "C"

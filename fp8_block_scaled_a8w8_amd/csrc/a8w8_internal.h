@@ -40,5 +40,7 @@ int64_t variant_passes(int id, int64_t K);
 hipError_t set_kernel_attributes();
 // Enqueue the instance; returns hipSuccess or the launch error.
 hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream);
+// Enqueue the per-1x128 activation quantisation of `groups` groups.
+hipError_t launch_quant_1x128(const void *X, void *A, float *a_scale, int64_t groups, int cus, hipStream_t stream);
 
 }  // namespace a8w8

@@ -125,6 +125,32 @@ const char *gemm_a8w8_status_string(int status);
 /* Hash of the compiled selector table (identifies the tuning that is deployed). */
 uint64_t gemm_a8w8_table_hash(void);
 
+/*
+ * Per-1x128 activation quantisation: the step upstream of the GEMM, which
+ * produces its A and a_scale operands from bf16 activations.  For each row m
+ * and 128-wide group g along K:
+ *
+ *   a_scale[m,g] = fp32(amax over the group of |X| / 448)
+ *   A[m,k]       = e4m3fn code nearest to clamp(fp32(X[m,k] / a_scale[m,g]), -448, 448)
+ *
+ * (IEEE fp32 division; ties to the even code; the sign bit follows the fp32
+ * quotient).  A group whose amax is 0 gets a_scale 0 and zero codes.  The
+ * pages describe the activation operand only as FP8 with per-group scales;
+ * this is the library's reading, the one its GEMM inputs are generated with.
+ *
+ * Buffers (device memory, row-major, owned by the caller):
+ *   X        bf16 (uint16 bit patterns) [M, K]   16-byte aligned, finite values
+ *                                                (non-finite inputs give unspecified
+ *                                                codes and scales in their group)
+ *   A        uint8 e4m3fn [M, K]                 8-byte aligned; overwritten
+ *   a_scale  float32 [M, K/128]                  4-byte aligned; overwritten
+ * Outputs must not overlap X.  K % 128 == 0, K <= 2^22, M <= 2^30; M == 0 is a
+ * no-op.  Same asynchrony and error rules as gemm_a8w8_blockscale: one kernel
+ * enqueued on `stream`, no allocation, no memset, no host synchronisation;
+ * errors are returned before anything is enqueued.
+ */
+int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64_t K, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

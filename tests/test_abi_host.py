@@ -24,7 +24,7 @@ REGISTERED = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_a8w8_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:gemm_)?a8w8_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -50,6 +50,22 @@ def test_bad_shapes(M, N, K):
 
 def test_m_zero_is_a_no_op_even_with_null_pointers():
     assert g.lib().gemm_a8w8_blockscale(None, None, None, None, None, 0, 512, 1024, None) == g.A8W8_OK
+    assert g.lib().a8w8_quantize_1x128(None, None, None, 0, 1024, None) == g.A8W8_OK
+
+
+@pytest.mark.parametrize("M,K", [(-1, 1024), (4, 0), (4, 1000), (4, 127), (1 << 31, 1024), (4, (1 << 22) + 128)])
+def test_quantize_bad_shapes(M, K):
+    assert g.lib().a8w8_quantize_1x128(16, 16, 16, M, K, None) == g.A8W8_ERR_SHAPE
+
+
+def test_quantize_null_and_misaligned_pointers():
+    q = g.lib().a8w8_quantize_1x128
+    assert q(None, 16, 16, 4, 1024, None) == g.A8W8_ERR_NULL
+    assert q(16, None, 16, 4, 1024, None) == g.A8W8_ERR_NULL
+    assert q(16, 16, None, 4, 1024, None) == g.A8W8_ERR_NULL
+    assert q(24, 16, 16, 4, 1024, None) == g.A8W8_ERR_ALIGN      # X needs 16 bytes
+    assert q(16, 20, 16, 4, 1024, None) == g.A8W8_ERR_ALIGN      # A needs 8
+    assert q(16, 16, 18, 4, 1024, None) == g.A8W8_ERR_ALIGN      # a_scale needs 4
 
 
 @pytest.mark.parametrize("which", ["A", "a_s", "W", "w_s", "Y"])
