@@ -128,6 +128,34 @@ def timed_replays(torch, graph, n):
     return t0.elapsed_time(t1) / n
 
 
+def quantize_bytes(M: int, K: int) -> int:
+    """Algorithmic bytes of the activation quantisation: bf16 in, e4m3fn codes and fp32 scales out."""
+    return 2 * M * K + M * K + 4 * M * (K // 128)
+
+
+def quantize_block(torch, g, inputgen, oracle, dev, replays):
+    """Per-1x128 activation quantisation at K = 5120, M in {16, 8192}: bit-exact parity gate
+    against the oracle, then HIP-graph timing with the input rotated over distinct copies."""
+    K = 5120
+    out = {}
+    for M in (16, 8192):
+        x = inputgen.normal_bf16(M, K, 1.0, seed=50 + M)
+        xb = x.to(torch.bfloat16).to(dev)
+        q, s = g.quantize_1x128(xb)
+        q_ref, s_ref = oracle.quantize_1x128(x.numpy())
+        if not (np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref) and np.array_equal(s.cpu().numpy(), s_ref)):
+            raise SystemExit(f"parity gate failed (quantize M={M})")
+        R = min(256, max(2, math.ceil(ROTATE_BYTES / 2 / xb.numel() / 2)))   # >= 1 GiB of inputs when large
+        xs = [xb] + [xb.clone() for _ in range(R - 1)]
+        gr = time_graph(torch, [(lambda xr=xr: g.quantize_1x128(xr, out=q, scale_out=s)) for xr in xs], 0, 2)
+        us = timed_replays(torch, gr, replays) * 1000.0 / R
+        gbs = quantize_bytes(M, K) / (us * 1e-6) / 1e9
+        out[f"M{M}_K{K}"] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "input_copies": R}
+        del gr, xs
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +283,10 @@ def main():
             del dWp
         log("prefill:", json.dumps(prefill))
 
+    # ------------------------------------------------------------ activation quantisation
+    quant = quantize_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
+    log("quantize:", json.dumps(quant))
+
     # ------------------------------------------------------------ CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -296,6 +328,7 @@ def main():
                      "bytes_per_launch": round(bytes_mean)},
         "per_m": per_m,
         "prefill": prefill,
+        "quantize": quant,
         "parity": {"worst_rel_l2": round(gate, 6)},
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": cpu,

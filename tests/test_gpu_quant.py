@@ -105,3 +105,31 @@ def test_quantize_guard_bands_and_empty():
     assert np.all(sb[:pad] == -7.0) and np.all(sb[-pad:] == -7.0)
     q0, s0 = g.quantize_1x128(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV))
     assert q0.shape == (0, 256) and s0.shape == (0, 2)
+
+
+def test_quantize_every_bf16_value_under_many_scales():
+    """The kernel forms x / s with a reciprocal and one FMA correction; this sweeps every finite
+    bf16 value below each of 24 group maxima (7 of them not multiples of 7 times a power of two,
+    so s = amax/448 is inexact) and compares every code with the oracle's IEEE division."""
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    allv = bits.view(np.float32)
+    allv = allv[np.isfinite(allv)]
+    rng = np.random.default_rng(12)
+    amaxes = [448.0, 1.0, 3.0, 5.0, 7.0, 1e-3, 2.0 ** -120, 1e30, 0.3, 11.0, 13.0, 100.0]
+    amaxes += [float(np.float32(v)) for v in rng.lognormal(0.0, 8.0, 12)]
+    rows = []
+    for a in amaxes:
+        a = float(torch.tensor([a]).to(torch.bfloat16).float())
+        v = allv[np.abs(allv) <= a]
+        n = (len(v) + 126) // 127
+        v = np.concatenate([v, np.zeros(n * 127 - len(v), np.float32)]).reshape(n, 127)
+        rows.append(np.concatenate([np.full((n, 1), a, np.float32), v], axis=1))
+    groups = np.concatenate(rows)                                   # [G, 128]
+    G = groups.shape[0]
+    K = 1024
+    M = (G + K // 128 - 1) // (K // 128)
+    pad = M * (K // 128) - G
+    groups = np.concatenate([groups, np.zeros((pad, 128), np.float32)])
+    x = torch.from_numpy(groups.reshape(M, K).copy())
+    _check(x, f"bf16 sweep ({G} groups)")
+    say(f"quantize: every bf16 value under {len(amaxes)} maxima ({G} groups) bit-exact")
