@@ -250,6 +250,39 @@ def main():
         del gm
     log("per-M:", json.dumps(per_m))
 
+    # the same workload with the weights prepacked offline (a8w8_prepack_weights)
+    pcopies = [g.prepack_weights(c) for c in copies]
+    for r in (0, R - 1):                                  # bitwise the same as the row-major call
+        for M in Ms:
+            y_row = g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw)
+            y_pk = g.gemm_a8w8_blockscale_packed(dA[:M], da[:M], pcopies[r], dw, N)
+            if not torch.equal(y_row.view(torch.int16), y_pk.view(torch.int16)):
+                raise SystemExit(f"parity gate failed (packed weights, copy {r}, M={M})")
+
+    def call_pk(r):
+        M = Ms[r % len(Ms)]
+        return lambda: g.gemm_a8w8_blockscale_packed(dA[:M], da[:M], pcopies[r], dw, N, out=outs[r])
+
+    graph = time_graph(torch, [call_pk(r) for r in range(R)], 0, args.warmup)
+    us_pk = timed_replays(torch, graph, args.steps) * 1000.0 / R
+    del graph
+    per_m_pk = {}
+    for M in Ms:
+        outM = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gm = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale_packed(dA[:M], da[:M], pcopies[r], dw, N,
+                                                                            out=outM)) for r in range(R)], 0, 2)
+        us = timed_replays(torch, gm, max(5, args.steps // 5)) * 1000.0 / R
+        per_m_pk[str(M)] = {"us_per_call": round(us, 3),
+                            "hbm_frac": round(algorithmic_bytes(M, N, K) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del gm
+    packed = {"us_per_call": round(us_pk, 3),
+              "hbm_frac": round(bytes_mean / (us_pk * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "per_m": per_m_pk,
+              "note": "same workload and plans, weights prepacked offline into the kernels' fragment order; "
+                      "outputs bitwise equal to the row-major call"}
+    del pcopies
+    log("prepacked:", json.dumps(packed))
+
     # ------------------------------------------------------------ prefill (compute-bound)
     prefill = {}
     if not args.no_prefill:
@@ -327,6 +360,7 @@ def main():
                                + ", ".join(sorted({v["plan"] for v in per_m.values()})),
                      "bytes_per_launch": round(bytes_mean)},
         "per_m": per_m,
+        "prepacked_weights": packed,
         "prefill": prefill,
         "quantize": quant,
         "parity": {"worst_rel_l2": round(gate, 6)},

@@ -39,6 +39,9 @@ EXPORTED = (
     "gemm_a8w8_status_string",
     "gemm_a8w8_table_hash",
     "a8w8_quantize_1x128",
+    "a8w8_prepack_weights",
+    "gemm_a8w8_blockscale_packed",
+    "gemm_a8w8_blockscale_packed_run_variant",
 )
 
 
@@ -91,6 +94,12 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_table_hash.argtypes = []
         L.a8w8_quantize_1x128.restype = ctypes.c_int
         L.a8w8_quantize_1x128.argtypes = [vp] * 3 + [i64] * 2 + [vp]
+        L.a8w8_prepack_weights.restype = ctypes.c_int
+        L.a8w8_prepack_weights.argtypes = [vp] * 2 + [i64] * 2 + [vp]
+        L.gemm_a8w8_blockscale_packed.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_packed.argtypes = [vp] * 5 + [i64] * 3 + [vp]
+        L.gemm_a8w8_blockscale_packed_run_variant.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_packed_run_variant.argtypes = [i32] + [vp] * 5 + [i64] * 3 + [vp]
         _lib = L
     return _lib
 
@@ -211,6 +220,59 @@ def quantize_1x128(X: torch.Tensor, out: torch.Tensor | None = None, scale_out: 
     if rc != A8W8_OK:
         raise A8W8Error(rc, "a8w8_quantize_1x128")
     return out, scale_out
+
+
+def packed_rows(N: int) -> int:
+    """Rows of the packed weight layout: N padded to a multiple of 16."""
+    return (N + 15) // 16 * 16
+
+
+def prepack_weights(W: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-major e4m3fn W [N,K] -> the packed layout (uint8 [16*ceil(N/16), K]); see the C header."""
+    if W.dtype not in (torch.float8_e4m3fn, torch.uint8) or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
+        raise ValueError("W must be a contiguous float8_e4m3fn (or uint8) [N,K] GPU tensor")
+    N, K = W.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    if out is None:
+        out = torch.empty((packed_rows(N), K), dtype=torch.uint8, device=W.device)
+    elif tuple(out.shape) != (packed_rows(N), K) or out.dtype not in (torch.uint8, torch.float8_e4m3fn) \
+            or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 [{packed_rows(N)},{K}] tensor")
+    rc = lib().a8w8_prepack_weights(W.data_ptr(), out.data_ptr(), N, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "a8w8_prepack_weights")
+    return out
+
+
+def _check_packed(A, a_scale, Wp, w_scale, N, out):
+    if Wp.dtype not in (torch.float8_e4m3fn, torch.uint8) or Wp.dim() != 2:
+        raise TypeError("Wp must be a 2-D uint8 (or float8_e4m3fn) tensor")
+    if Wp.shape[0] != packed_rows(N):
+        raise ValueError(f"packed weights for N={N} have {packed_rows(N)} rows, got {Wp.shape[0]}")
+    return _check(A, a_scale, Wp[:N], w_scale, out)
+
+
+def gemm_a8w8_blockscale_packed(A: torch.Tensor, a_scale: torch.Tensor, Wp: torch.Tensor, w_scale: torch.Tensor,
+                                N: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Same result as gemm_a8w8_blockscale, with W given in the packed layout (prepack_weights)."""
+    M, N, K, out = _check_packed(A, a_scale, Wp, w_scale, N, out)
+    rc = lib().gemm_a8w8_blockscale_packed(A.data_ptr(), a_scale.data_ptr(), Wp.data_ptr(), w_scale.data_ptr(),
+                                           out.data_ptr(), M, N, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_blockscale_packed")
+    return out
+
+
+def gemm_a8w8_blockscale_packed_run_variant(variant: int, A, a_scale, Wp, w_scale, N: int, out=None, stream=None):
+    """gemm_a8w8_blockscale_packed with a fixed kernel instance (tuning and tests)."""
+    M, N, K, out = _check_packed(A, a_scale, Wp, w_scale, N, out)
+    rc = lib().gemm_a8w8_blockscale_packed_run_variant(variant, A.data_ptr(), a_scale.data_ptr(), Wp.data_ptr(),
+                                                       w_scale.data_ptr(), out.data_ptr(), M, N, K,
+                                                       _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, f"gemm_a8w8_blockscale_packed_run_variant({variant})")
+    return out
 
 
 def variants() -> list[dict]:

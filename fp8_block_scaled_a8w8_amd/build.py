@@ -8,7 +8,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libgemm_a8w8.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("a8w8_api.hip", "a8w8_kernels.hip", "a8w8_quant.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("a8w8_api.hip", "a8w8_kernels.hip", "a8w8_quant.hip", "a8w8_prepack.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -97,10 +97,11 @@ int check_pointers(const void *A, const float *a_scale, const void *W, const flo
     return A8W8_OK;
 }
 
-// The skinny and tall kernels address A and W with 32-bit per-lane offsets.
+// The skinny and tall kernels address A and W with 32-bit per-lane offsets
+// (W rows counted padded to a multiple of 16, as the packed layout stores them).
 bool skinny_fits(int64_t N, int64_t K)
 {
-    return N * K < ((int64_t)1 << 32) && 16 * K < ((int64_t)1 << 32);
+    return ((N + 15) & ~(int64_t)15) * K < ((int64_t)1 << 32) && 16 * K < ((int64_t)1 << 32);
 }
 
 bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
@@ -242,7 +243,7 @@ void log_plan(int64_t M, int64_t N, int64_t K, int id, int64_t key_m, int fallba
 }
 
 int launch(int id, const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
-           int64_t M, int64_t N, int64_t K, int cus, void *stream)
+           int64_t M, int64_t N, int64_t K, int cus, void *stream, int wpk)
 {
     Args a;
     a.A = static_cast<const uint8_t *>(A);
@@ -253,17 +254,14 @@ int launch(int id, const void *A, const float *a_scale, const void *W, const flo
     a.M = (int32_t)M;
     a.N = (int32_t)N;
     a.K = (int32_t)K;
+    a.wpk = wpk;
     if (a8w8::launch_variant(id, a, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
         return A8W8_ERR_HIP;
     return A8W8_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
-                         int64_t M, int64_t N, int64_t K, void *stream)
+int gemm_impl(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y, int64_t M,
+              int64_t N, int64_t K, void *stream, int wpk)
 {
     int rc = check_shape(M, N, K);
     if (rc != A8W8_OK)
@@ -279,7 +277,45 @@ int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, con
         return rc;
     const Choice c = select_variant(M, N, K, cus);
     log_plan(M, N, K, c.variant, c.key_m, c.fallback);
-    return launch(c.variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream);
+    return launch(c.variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream, wpk);
+}
+
+int run_variant_impl(int32_t variant, const void *A, const float *a_scale, const void *W, const float *w_scale,
+                     void *Y, int64_t M, int64_t N, int64_t K, void *stream, int wpk)
+{
+    if (variant < 0 || variant >= a8w8::num_variants())
+        return A8W8_ERR_PLAN;
+    int rc = check_shape(M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M == 0)
+        return A8W8_OK;
+    if (!variant_accepts(variant, M, N, K))
+        return A8W8_ERR_PLAN;
+    rc = check_pointers(A, a_scale, W, w_scale, Y);
+    if (rc != A8W8_OK)
+        return rc;
+    int cus = 0;
+    rc = device_ready(&cus);
+    if (rc != A8W8_OK)
+        return rc;
+    return launch(variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream, wpk);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
+                         int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl(A, a_scale, W, w_scale, Y, M, N, K, stream, 0);
+}
+
+int gemm_a8w8_blockscale_packed(const void *A, const float *a_scale, const void *Wp, const float *w_scale, void *Y,
+                                int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl(A, a_scale, Wp, w_scale, Y, M, N, K, stream, 1);
 }
 
 int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
@@ -313,23 +349,31 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant, const void *A, const float
                                      const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
                                      void *stream)
 {
-    if (variant < 0 || variant >= a8w8::num_variants())
-        return A8W8_ERR_PLAN;
-    int rc = check_shape(M, N, K);
-    if (rc != A8W8_OK)
-        return rc;
-    if (M == 0)
-        return A8W8_OK;
-    if (!variant_accepts(variant, M, N, K))
-        return A8W8_ERR_PLAN;
-    rc = check_pointers(A, a_scale, W, w_scale, Y);
-    if (rc != A8W8_OK)
-        return rc;
+    return run_variant_impl(variant, A, a_scale, W, w_scale, Y, M, N, K, stream, 0);
+}
+
+int gemm_a8w8_blockscale_packed_run_variant(int32_t variant, const void *A, const float *a_scale, const void *Wp,
+                                            const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
+                                            void *stream)
+{
+    return run_variant_impl(variant, A, a_scale, Wp, w_scale, Y, M, N, K, stream, 1);
+}
+
+int a8w8_prepack_weights(const void *W, void *Wp, int64_t N, int64_t K, void *stream)
+{
+    if (N < 1 || K < 1 || (K % 128) != 0 || N > kMaxDim || K > kMaxK)
+        return A8W8_ERR_SHAPE;
+    if (!W || !Wp)
+        return A8W8_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(W) & 15) || (reinterpret_cast<uintptr_t>(Wp) & 15))
+        return A8W8_ERR_ALIGN;
     int cus = 0;
-    rc = device_ready(&cus);
+    const int rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    return launch(variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream);
+    if (a8w8::launch_prepack(W, Wp, N, K, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return A8W8_ERR_HIP;
+    return A8W8_OK;
 }
 
 const char *gemm_a8w8_variant_name(int32_t variant)

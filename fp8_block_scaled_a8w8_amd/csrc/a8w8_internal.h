@@ -25,6 +25,7 @@ struct Args {
     const float *w_scale;
     uint16_t *Y;
     int32_t M, N, K;
+    int32_t wpk;       // 1: W is in the packed (fragment-order) layout, see packed_piece
 };
 
 int num_variants();
@@ -40,6 +41,8 @@ int64_t variant_passes(int id, int64_t K);
 hipError_t set_kernel_attributes();
 // Enqueue the instance; returns hipSuccess or the launch error.
 hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream);
+// Enqueue the conversion of row-major W [N, K] to the packed layout.
+hipError_t launch_prepack(const void *W, void *Wp, int64_t N, int64_t K, int cus, hipStream_t stream);
 // Enqueue the per-1x128 activation quantisation of `groups` groups.
 hipError_t launch_quant_1x128(const void *X, void *A, float *a_scale, int64_t groups, int cus, hipStream_t stream);
 

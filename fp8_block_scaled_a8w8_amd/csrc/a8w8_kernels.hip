@@ -123,7 +123,29 @@ __device__ __forceinline__ v8i fix_row_layout(v4i v0, v4i v1)
     return cat(a, b);
 }
 
-template <int TPW, int D, int NW>
+// Packed weights (the optional offline layout a8w8_prepack_weights writes):
+// rows padded with zeros to a multiple of 16; for every 16-row tile t and K
+// block kb, 2 KB in MFMA operand order, [h][lane][16 bytes], lane l holding
+// row 16t + l%16, 16-byte chunk 2(l/16) + h of the block.  A wave then reads
+// each half of a fragment (1 KB) with one contiguous load and needs no lane
+// exchange.  Byte offset of tile t, block kb:
+__device__ __forceinline__ uint32_t packed_block(uint32_t tile, uint32_t kb, uint32_t KB)
+{
+    return (tile * KB + kb) << 11;
+}
+// Weight fragment from its two 16-byte loads (row layout needs the lane exchange).
+__device__ __forceinline__ v8i w_fragment(v4i w0, v4i w1, bool pk)
+{
+    return pk ? cat(w0, w1) : fix_row_layout(w0, w1);
+}
+// Weight rows the buffer holds: padded to a multiple of 16 when packed.
+template <bool PK>
+__device__ __forceinline__ uint32_t w_rows(const Args &p)
+{
+    return PK ? (uint32_t)((p.N + 15) & ~15) : (uint32_t)p.N;
+}
+
+template <int TPW, int D, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 {
     const int lane = threadIdx.x & 63;
@@ -139,14 +161,19 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     // M*K below 2^32) plus the wave-uniform block offset kb*128.
     const int lrow = r16 & 7;
     const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
-    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, (uint32_t)N * (uint32_t)K);
+    constexpr bool pk = PK;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
+    // Row layout: per-lane row offsets, block offset kb * 128.  Packed: lane l
+    // reads bytes 16 l (+1024 for the second half) of the tile's block.
+    const int last_tile = ((N + 15) >> 4) - 1;
     uint32_t woff[TPW][2];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            woff[t][h] = (uint32_t)min(n0 + 16 * t + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
+            woff[t][h] = pk ? (uint32_t)(lane * 16 + h * 1024)
+                            : (uint32_t)min(n0 + 16 * t + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
     // Activation rows past M load row 0: they only feed output columns that are never stored.
     uint32_t aoff[2];
 #pragma unroll
@@ -173,10 +200,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
             const int kb = min(kb_begin + j, KB - 1);   // blocks past the end load a valid block, skipped below
             const int koff = kb * 128;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t)
+            for (int t = 0; t < TPW; ++t) {
+                const int wso = pk ? (int)packed_block(min((n0 >> 4) + t, last_tile), kb, KB) : koff;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[t][h], koff, 2 /* nt */);
+                    wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[t][h], wso, 2 /* nt */);
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[h], koff, 0);
@@ -191,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
                 const float sc = sa[j] * sw[j];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
-                    acc[t] = fma4(mfma_block(fix_row_layout(wr[j][t][0], wr[j][t][1]), af), sc, acc[t]);
+                    acc[t] = fma4(mfma_block(w_fragment(wr[j][t][0], wr[j][t][1], pk), af), sc, acc[t]);
             }
         }
     }
@@ -244,7 +273,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 // wave order (fixed order: bitwise deterministic) and stores the 16 x 16
 // bf16 tile.  Loads for tiles past the workgroup's share go through a
 // descriptor of zero records, which returns zeros without touching memory.
-template <int D, int NW, int P>
+template <int D, int NW, int P, bool PK>
 __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 {
     __shared__ v4f red[2][NW][64];
@@ -261,7 +290,8 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 
     const int lrow = r16 & 7;
     const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
-    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, (uint32_t)N * (uint32_t)K);
+    constexpr bool pk = PK;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.W, 0u);
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(p.w_scale, (uint32_t)((N + 127) >> 7) * (uint32_t)KB * 4u);
@@ -297,14 +327,16 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
         uint32_t woff[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            woff[h] = (uint32_t)min(n0 + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
+            woff[h] = pk ? (uint32_t)(lane * 16 + h * 1024)
+                         : (uint32_t)min(n0 + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
         const int srow = (n0 >> 7) * KB;
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int kb = min(kb0 + j, KB - 1);
+            const int wso = pk ? (int)packed_block((uint32_t)(n0 >> 4), kb, KB) : kb * 128;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                wr[j][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[h], kb * 128, 2 /* nt */);
+                wr[j][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[h], wso, 2 /* nt */);
             sw[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, 0, (srow + kb) * 4, 0));
         }
     };
@@ -314,7 +346,7 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 #pragma unroll
         for (int j = 0; j < D; ++j)
             if (kb0 + j < KB)
-                acc = fma4(mfma_block(fix_row_layout(wr[j][0], wr[j][1]), af[j]), sa[j] * sw[j], acc);
+                acc = fma4(mfma_block(w_fragment(wr[j][0], wr[j][1], pk), af[j]), sa[j] * sw[j], acc);
         red[i & 1][wave][lane] = acc;
         __syncthreads();
         if (wave == i % NW) {
@@ -367,7 +399,7 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 // output row and take one a_scale per block).  Per block: TPW * NT MFMAs,
 // each followed by one scale FMA per output; the wave partials are summed
 // through LDS in wave order and rounded once.
-template <int TPW, int NT, int D, int NW>
+template <int TPW, int NT, int D, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
 {
     const int lane = threadIdx.x & 63;
@@ -377,15 +409,19 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
     const int r16 = lane & 15, g = lane >> 4;
     const int lrow = r16 & 7;
     const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
-    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, (uint32_t)N * (uint32_t)K);
+    constexpr bool pk = PK;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
-    // Rows past N or M load the last row: they only feed outputs that are never stored.
+    // Rows past N or M load the last row (packed: the last tile): they only
+    // feed outputs that are never stored.
+    const int last_tile = ((N + 15) >> 4) - 1;
     uint32_t woff[NT][2], aoff[TPW][2];
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            woff[u][h] = (uint32_t)min(16 * u + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
+            woff[u][h] = pk ? (uint32_t)(lane * 16 + h * 1024)
+                            : (uint32_t)min(16 * u + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -418,10 +454,12 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
                 for (int h = 0; h < 2; ++h)
                     ar[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[t][h], koff, 2 /* nt */);
 #pragma unroll
-            for (int u = 0; u < NT; ++u)
+            for (int u = 0; u < NT; ++u) {
+                const int wso = pk ? (int)packed_block((uint32_t)min(u, last_tile), kb, KB) : koff;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    wr[j][u][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[u][h], koff, 0);
+                    wr[j][u][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[u][h], wso, 0);
+            }
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
                 sa[j][t] = asp[t][kb];
@@ -434,7 +472,7 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
                 v8i wf[NT];
 #pragma unroll
                 for (int u = 0; u < NT; ++u)
-                    wf[u] = fix_row_layout(wr[j][u][0], wr[j][u][1]);
+                    wf[u] = w_fragment(wr[j][u][0], wr[j][u][1], pk);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const v8i af = fix_row_layout(ar[j][t][0], ar[j][t][1]);
@@ -580,6 +618,21 @@ __device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
     return cat(lo, hi);
 }
 
+// Weight stages hold either row-layout rows (as above) or, for packed weights,
+// each 16-row tile's 2 KB exactly as stored in memory (operand order): the
+// copies then move whole contiguous kilobytes, and lane l reads bytes 16 l of
+// each half of the tile that holds `row` (its first row plus l % 16).
+template <bool PK>
+__device__ __forceinline__ v8i lds_w_fragment(const uint8_t *sW, int row, int g, int lane)
+{
+    if constexpr (PK) {
+        const uint8_t *tp = sW + (row >> 4) * 2048 + lane * 16;
+        return cat(*reinterpret_cast<const v4i *>(tp), *reinterpret_cast<const v4i *>(tp + 1024));
+    } else {
+        return lds_fragment(sW, row, g);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Persistent tile kernel ("ptile").  Workgroup b takes output tiles rank(b),
 // rank(b) + G, rank(b) + 2G, ... of the T = ceil(M/BM) * ceil(N/BN) tiles
@@ -628,7 +681,7 @@ __device__ __forceinline__ void linear_tile(int L, int tiles_m, int tiles_n, int
     tn = in_group / gsize;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK>
 __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_store)
 {
     constexpr int NWAVES = WGM * WGN;
@@ -711,7 +764,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 #pragma unroll
     for (int j = 0; j < W_LOADS; ++j) {
         const int row = (wave * W_LOADS + j) * 8 + lrow;
-        w_off[j] = (uint32_t)row * (uint32_t)K + (uint32_t)((pch ^ chunk_swizzle(row)) << 4);
+        const uint32_t q = (uint32_t)(pch ^ chunk_swizzle(row));
+        // packed: copy j moves kilobyte (wave * W_LOADS + j) of the tile's stage unchanged
+        const uint32_t half = (uint32_t)(wave * W_LOADS + j);
+        w_off[j] = PK ? ((((half >> 1) * (uint32_t)KB) << 11) + ((half & 1u) << 10) + (uint32_t)lane * 16u)
+                      : (uint32_t)row * (uint32_t)K + (q << 4);
     }
     const int slot = wave * 64 + lane;
     struct CopyTile {
@@ -736,7 +793,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         return tile_rsrc(p.A + (size_t)m0 * K + (size_t)kb * 128,
                          (uint32_t)min(M - m0, BM) * (uint32_t)K - (uint32_t)kb * 128u);
     };
+    // Packed weights: the tile's 16-row tiles from block kb of its first one
+    // to the end of its last one that exists.
     auto rsrc_w = [&](int n0, int kb) {
+        if (PK) {
+            const int t0 = n0 >> 4, tiles = min(((N + 15) >> 4) - t0, BN / 16);
+            return tile_rsrc(p.W + (((size_t)t0 * KB + kb) << 11),
+                             ((uint32_t)tiles * (uint32_t)KB - (uint32_t)kb) << 11);
+        }
         return tile_rsrc(p.W + (size_t)n0 * K + (size_t)kb * 128,
                          (uint32_t)min(N - n0, BN) * (uint32_t)K - (uint32_t)kb * 128u);
     };
@@ -768,11 +832,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     {
         const uint8_t *sA = smem, *sW = smem + A_BYTES;
         const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
-        wf[0] = lds_fragment(sW, wrow, g);
+        wf[0] = lds_w_fragment<PK>(sW, wrow, g, lane);
         af = lds_fragment(sA, arow, g);
 #pragma unroll
         for (int u = 1; u < TN; ++u)
-            wf[u] = lds_fragment(sW, wrow + 16 * u, g);
+            wf[u] = lds_w_fragment<PK>(sW, wrow + 16 * u, g, lane);
 #pragma unroll
         for (int t = 0; t < TM; ++t)
             sa[t] = sS[arow + 16 * t];
@@ -830,7 +894,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
                 const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    wf[u] = lds_fragment(nW, wrow + 16 * u, g);
+                    wf[u] = lds_w_fragment<PK>(nW, wrow + 16 * u, g, lane);
                 af_next = lds_fragment(nA, arow, g);
 #pragma unroll
                 for (int s = 0; s < TM; ++s)
@@ -918,7 +982,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 }
 
 // Explicit instantiations (emit the host-side launch stubs).
-#define A8W8_PTILE_INST(BM, BN, WGM, WGN, S) template __global__ void ptile_kernel<BM, BN, WGM, WGN, S>(Args, int);
+#define A8W8_PTILE_INST(BM, BN, WGM, WGN, S)                                                  \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false>(Args, int);             \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true>(Args, int);
 A8W8_PTILE_INST(256, 256, 2, 4, 2)
 A8W8_PTILE_INST(256, 128, 2, 4, 3)
 A8W8_PTILE_INST(128, 256, 2, 4, 3)
@@ -956,14 +1022,15 @@ __device__ __forceinline__ void dma4_at(const void *src, const void *lds_dst)
 template <int A_LOADS, int W_LOADS>
 __device__ __forceinline__ void issue_block_copies(const uint8_t *const (&a_src)[A_LOADS],
                                                  const uint8_t *const (&w_src)[W_LOADS], const float *as_src,
-                                                 int kb, uint8_t *stage, int a_bytes, int w_bytes, int wave)
+                                                 int kb, uint8_t *stage, int a_bytes, int w_bytes, int wave,
+                                                 int w_block_stride)
 {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
         dma16_at(a_src[i] + (size_t)kb * 128, stage + (wave * A_LOADS + i) * 1024);
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i)
-        dma16_at(w_src[i] + (size_t)kb * 128, stage + a_bytes + (wave * W_LOADS + i) * 1024);
+        dma16_at(w_src[i] + (size_t)kb * w_block_stride, stage + a_bytes + (wave * W_LOADS + i) * 1024);
     dma4_at(as_src + kb, stage + a_bytes + w_bytes + wave * 256);
 }
 
@@ -1001,7 +1068,7 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 //
 // LDS stage: A tile [BM][128] | W tile [BN][128] | activation scales
 // [64 * waves] floats, tiles swizzled as described at chunk_swizzle().
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK>
 __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
 {
     constexpr int NWAVES = WGM * WGN;
@@ -1041,11 +1108,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i) {
         const int row = (wave * W_LOADS + i) * 8 + lrow;
-        w_src[i] = p.W + (size_t)min(n0 + row, N - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
+        // packed: copy i moves kilobyte (wave * W_LOADS + i) of the tile's stage unchanged
+        const int half = wave * W_LOADS + i;
+        const int tile = min((n0 >> 4) + (half >> 1), ((N + 15) >> 4) - 1);
+        w_src[i] = PK ? p.W + (((size_t)tile * KB) << 11) + ((half & 1) << 10) + lane * 16
+                      : p.W + (size_t)min(n0 + row, N - 1) * K + ((pch ^ chunk_swizzle(row)) << 4);
     }
     // Activation scales: wave w copies tile rows 64w + lane (rows past the tile
     // or past M repeat a valid row and are never read).
     const float *as_src = p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB;
+    const int w_stride = PK ? 2048 : 128;   // bytes from one K block of a weight row to the next
     const int NB = (N + 127) >> 7;
     const_f32 *wsp = (const_f32 *)(p.w_scale + (size_t)min((n0 + wn * WN) >> 7, NB - 1) * KB);
 
@@ -1060,7 +1132,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
-                                           W_BYTES, wave);
+                                           W_BYTES, wave, w_stride);
     float ws_next = wsp[0];
 
     for (int kb = 0; kb < KB; ++kb) {
@@ -1069,7 +1141,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
         const int kn = min(kb + STAGES - 1, KB - 1);
         issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
-                                           A_BYTES, W_BYTES, wave);
+                                           A_BYTES, W_BYTES, wave, w_stride);
         ws_next = wsp[min(kb + 1, KB - 1)];
 
         const uint8_t *sA = smem + (kb % STAGES) * STAGE;
@@ -1082,7 +1154,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         v8i wf[TN];
 #pragma unroll
         for (int u = 0; u < TN; ++u)
-            wf[u] = lds_fragment(sW, wn * WN + 16 * u + r16, g);
+            wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u + r16, g, lane);
         v4f d[2][TN];
         {
             const v8i af = lds_fragment(sA, wm * WM + r16, g);
@@ -1117,7 +1189,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 }
 
 
-#define A8W8_TILE_INST(BM, BN, WGM, WGN, S) template __global__ void tile_kernel<BM, BN, WGM, WGN, S>(Args, int);
+#define A8W8_TILE_INST(BM, BN, WGM, WGN, S)                                                   \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false>(Args, int);              \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true>(Args, int);
 A8W8_TILE_INST(256, 256, 2, 4, 2)
 A8W8_TILE_INST(256, 128, 2, 4, 3)
 A8W8_TILE_INST(128, 256, 2, 4, 3)
@@ -1142,14 +1216,18 @@ using namespace kern;
 // ---------------------------------------------------------------------------
 // Instance table.
 
+// Each instance is compiled twice: for row-layout weights (fn) and for the
+// packed layout (fn_pk).
 struct Entry {
     Variant v;
     const void *fn;
+    const void *fn_pk;
     int lds_bytes;
 };
 
+#define FN2(...) reinterpret_cast<const void *>(&__VA_ARGS__, false>), reinterpret_cast<const void *>(&__VA_ARGS__, true>)
 #define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, "skinny_r" #TPW "_d" #D "_w" #NW}, \
-                            reinterpret_cast<const void *>(&skinny_kernel<TPW, D, NW>), 0}
+                            FN2(skinny_kernel<TPW, D, NW), 0}
 // Persistent tile grids are sized for WPC waves per CU: 8 (two per SIMD) for
 // the instances above 128 VGPRs, 16 for the small ones, or fewer workgroups
 // where their LDS does not fit.
@@ -1159,19 +1237,19 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 }
 #define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   reinterpret_cast<const void *>(&tile_kernel<BM, BN, WGM, WGN, S>), \
+                                   FN2(tile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 #define PTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_PTILE, BM, BN, WGM * WGN, S, 0, \
                                     tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
                                     "ptile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   reinterpret_cast<const void *>(&ptile_kernel<BM, BN, WGM, WGN, S>), \
+                                   FN2(ptile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
 #define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, \
                                "tall_r" #TPW "_n" #NT "_d" #D "_w" #NW}, \
-                              reinterpret_cast<const void *>(&tall_kernel<TPW, NT, D, NW>), 0}
+                              FN2(tall_kernel<TPW, NT, D, NW), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
-                           reinterpret_cast<const void *>(&pskinny_kernel<D, NW, P>), 0}
+                           FN2(pskinny_kernel<D, NW, P), 0}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
@@ -1231,10 +1309,12 @@ hipError_t set_kernel_attributes()
 {
     for (int i = 0; i < kNumEntries; ++i) {
         if (kEntries[i].lds_bytes > 0) {
-            hipError_t e = hipFuncSetAttribute(kEntries[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               kEntries[i].lds_bytes);
-            if (e != hipSuccess)
-                return e;
+            for (const void *fn : {kEntries[i].fn, kEntries[i].fn_pk}) {
+                hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   kEntries[i].lds_bytes);
+                if (e != hipSuccess)
+                    return e;
+            }
         }
     }
     return hipSuccess;
@@ -1247,7 +1327,7 @@ hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream)
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;
     void *params[] = {&args, &vec};
-    return hipLaunchKernel(e.fn, dim3((unsigned)grid), dim3(e.v.waves * 64), params,
+    return hipLaunchKernel(a.wpk ? e.fn_pk : e.fn, dim3((unsigned)grid), dim3(e.v.waves * 64), params,
                            (size_t)e.lds_bytes, stream);
 }
 

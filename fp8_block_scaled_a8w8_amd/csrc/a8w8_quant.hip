@@ -143,7 +143,9 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t *X, uin
 
 hipError_t launch_quant_1x128(const void *X, void *A, float *a_scale, int64_t groups, int cus, hipStream_t stream)
 {
-    const int64_t wgs = (groups + 16 * kern::kGroupsPerTrip - 1) / (16 * kern::kGroupsPerTrip);
+    // Small problems: one group per lane group (more workgroups in flight);
+    // large ones: the capped grid walks kGroupsPerTrip groups per trip.
+    const int64_t wgs = (groups + 15) / 16;
     const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * 8;
     const unsigned grid = (unsigned)(wgs < cap ? wgs : cap);
     hipLaunchKernelGGL(kern::quant_1x128_kernel, dim3(grid), dim3(256), 0, stream,

@@ -116,6 +116,32 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant,
                                      void *Y, int64_t M, int64_t N, int64_t K,
                                      void *stream);
 
+/*
+ * Packed weights (optional offline layout; the pre-shuffled-weight idea of
+ * the pages' "bpreshuffle" kernels, laid out for this library's MFMA):
+ * W [N, K] row-major -> Wp of 16 * ceil(N/16) * K bytes.  For every 16-row
+ * tile t and 128-wide K block kb, the 2048 bytes at (t * K/128 + kb) * 2048
+ * hold, in order h = 0, 1 and lane l = 0..63, the 16 bytes of row 16 t + l%16
+ * at columns 128 kb + 32 (l/16) + 16 h .. + 16; rows past N are zero.  Every
+ * kernel then reads a weight fragment as two contiguous 1 KB loads.
+ *
+ * a8w8_prepack_weights enqueues the conversion (W and Wp device memory,
+ * 16-byte aligned, not overlapping; K % 128 == 0).  gemm_a8w8_blockscale_packed
+ * computes exactly what gemm_a8w8_blockscale computes from the same W (the
+ * same kernels and instances, bitwise identical Y) reading Wp instead; N is
+ * the real row count.  Same contract otherwise.
+ */
+int a8w8_prepack_weights(const void *W, void *Wp, int64_t N, int64_t K, void *stream);
+int gemm_a8w8_blockscale_packed(const void *A, const float *a_scale,
+                                const void *Wp, const float *w_scale,
+                                void *Y, int64_t M, int64_t N, int64_t K,
+                                void *stream);
+int gemm_a8w8_blockscale_packed_run_variant(int32_t variant,
+                                            const void *A, const float *a_scale,
+                                            const void *Wp, const float *w_scale,
+                                            void *Y, int64_t M, int64_t N, int64_t K,
+                                            void *stream);
+
 /* Static name of a compiled instance, e.g. "tile_256x128" (NULL if out of range). */
 const char *gemm_a8w8_variant_name(int32_t variant);
 

@@ -58,6 +58,19 @@ def test_quantize_bad_shapes(M, K):
     assert g.lib().a8w8_quantize_1x128(16, 16, 16, M, K, None) == g.A8W8_ERR_SHAPE
 
 
+def test_packed_entry_points_check_arguments():
+    L = g.lib()
+    assert L.a8w8_prepack_weights(16, 16, 0, 1024, None) == g.A8W8_ERR_SHAPE
+    assert L.a8w8_prepack_weights(16, 16, 64, 1000, None) == g.A8W8_ERR_SHAPE
+    assert L.a8w8_prepack_weights(None, 16, 64, 1024, None) == g.A8W8_ERR_NULL
+    assert L.a8w8_prepack_weights(16, 24, 64, 1024, None) == g.A8W8_ERR_ALIGN
+    assert L.gemm_a8w8_blockscale_packed(16, 16, 16, 16, 16, 4, 512, 1000, None) == g.A8W8_ERR_SHAPE
+    assert L.gemm_a8w8_blockscale_packed(16, 16, None, 16, 16, 4, 512, 1024, None) == g.A8W8_ERR_NULL
+    assert L.gemm_a8w8_blockscale_packed(None, None, None, None, None, 0, 512, 1024, None) == g.A8W8_OK
+    skinny = [v["variant"] for v in g.variants() if v["kernel_name"] == "skinny"][0]
+    assert L.gemm_a8w8_blockscale_packed_run_variant(skinny, 16, 16, 16, 16, 16, 17, 512, 1024, None) == g.A8W8_ERR_PLAN
+
+
 def test_quantize_null_and_misaligned_pointers():
     q = g.lib().a8w8_quantize_1x128
     assert q(None, 16, 16, 4, 1024, None) == g.A8W8_ERR_NULL
