@@ -36,6 +36,7 @@ __all__ = [
     "GROUP", "FP8_MAX", "normal_bf16", "quantize_rows_1x128",
     "quantize_blocks_128x128", "make_activations", "make_weights",
     "sign_flip_copy", "random_m_values",
+    "MX_GROUP", "E4M3_EMAX", "quantize_mx", "make_mx_activations", "make_mx_weights",
 ]
 
 
@@ -110,3 +111,54 @@ def random_m_values(count: int, lo: int = 1, hi: int = 8192, seed: int = 2) -> l
     """`count` i.i.d. uniform integers in [lo, hi] (dense arbitrary M)."""
     rng = np.random.default_rng(seed)
     return [int(v) for v in rng.integers(lo, hi + 1, size=count)]
+
+
+# ---------------------------------------------------------------------------
+# MX-scaled operands (mxfp8 with 32 x 32 weight-scale blocks, the variant the
+# gfx1250 BF16 and MX32 tuned-rows page, ROCm/aiter #7247, tunes).  The page
+# gives the block shape only; the encoding is the OCP Microscaling one: a
+# block of values shares one E8M0 byte e (value 2^(e - 127)) with
+# e - 127 = floor(log2(amax)) - 8 (8 = the exponent of e4m3fn's largest
+# normal), and each value becomes e4m3fn_RNE(clamp(x / 2^(e-127), -448, 448))
+# -- the division is exact (a power of two), and the clamp saturates the top
+# of the binade, [448, 512).  A block whose amax is 0 gets e = 127 and zero
+# codes.  Activations: one scale per row per 32-wide K group,
+# ``a_scale`` uint8 [M, K/32]; weights: one per 32 x 32 block,
+# ``w_scale`` uint8 [ceil(N/32), K/32] (the last block along N covers the
+# rows that exist).
+
+MX_GROUP = 32
+E4M3_EMAX = 8        # largest normal e4m3fn value is 1.75 * 2^8
+
+
+def quantize_mx(x: torch.Tensor, rows_per_block: int) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise fp32 [R, K] with one E8M0 scale per rows_per_block x 32 block.
+
+    Returns (codes uint8 [R, K], scales uint8 [ceil(R / rows_per_block), K / 32]).
+    """
+    R, K = x.shape
+    assert K % MX_GROUP == 0, "K must be a multiple of 32"
+    rb = rows_per_block
+    RB, KG = (R + rb - 1) // rb, K // MX_GROUP
+    pad = RB * rb - R
+    xp = torch.nn.functional.pad(x, (0, 0, 0, pad)) if pad else x
+    b = xp.reshape(RB, rb, KG, MX_GROUP)
+    amax = b.abs().amax(dim=(1, 3))                            # [RB, KG]
+    _, ex = torch.frexp(amax)                                  # amax = f * 2^ex, f in [0.5, 1)
+    shared = (ex - 1 - E4M3_EMAX).clamp(-127, 127)             # floor(log2(amax)) - 8
+    shared = torch.where(amax > 0, shared, torch.zeros_like(shared))
+    code = (shared + 127).to(torch.uint8)
+    y = torch.ldexp(b, -shared[:, None, :, None].to(torch.float32))
+    y = y.clamp(-FP8_MAX, FP8_MAX)
+    q = _encode_e4m3fn(y).reshape(RB * rb, K)[:R]
+    return q.numpy().copy(), code.numpy().copy()
+
+
+def make_mx_activations(M: int, K: int, seed: int = 0, std: float = 1.0):
+    """MX activation operand: (A uint8 [M, K], a_scale uint8 E8M0 [M, K/32])."""
+    return quantize_mx(normal_bf16(M, K, std, seed), 1)
+
+
+def make_mx_weights(N: int, K: int, seed: int = 1, std: float = 0.02):
+    """MX weight operand: (W uint8 [N, K], w_scale uint8 E8M0 [ceil(N/32), K/32])."""
+    return quantize_mx(normal_bf16(N, K, std, seed), MX_GROUP)

@@ -1,5 +1,5 @@
-"""CPU fp64 oracle for the a8w8 block-scale GEMM and its activation
-quantisation step -- TEST INFRASTRUCTURE ONLY.
+"""CPU fp64 oracle for the a8w8 block-scale GEMM, its MX-scaled variant and
+its activation quantisation step -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never does, and the
@@ -12,7 +12,10 @@ permutation weights, a numpy float64 matmul special case, the bf16 rounding
 floor printed on the "Retune gfx942 ... a8w8 blockscale decode rows" page;
 for ``quantize_1x128``: hand-derived codes at rounding ties, torch's fp8 cast
 of the same quotients, zero groups, the group maximum, the half-spacing
-error bound).
+error bound; for ``gemm_mx``: the E8M0 format definition, exact rational
+brute force, one-group and one-block power-of-two changes that move exactly
+their own K range and rows, a unit-scale numpy matmul special case, and the
+reduction to ``gemm`` when every 32-wide scale of a 128-wide block agrees).
 """
 from __future__ import annotations
 
@@ -50,6 +53,11 @@ def _load():
         lib.a8w8_oracle_threads.restype = ctypes.c_int
         lib.a8w8_oracle_gemm.restype = ctypes.c_int
         lib.a8w8_oracle_gemm.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + \
+            [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.a8w8_oracle_e8m0_value.restype = ctypes.c_double
+        lib.a8w8_oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.a8w8_oracle_gemm_mx.restype = ctypes.c_int
+        lib.a8w8_oracle_gemm_mx.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + \
             [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         _lib = lib
     return _lib
@@ -152,3 +160,56 @@ def quantize_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     code = code.reshape(M, K // 128, 128)
     code = np.where((s > 0)[..., None], code, np.uint8(0))
     return np.ascontiguousarray(code.reshape(M, K)), s
+
+
+MX_GROUP = 32        # K-extent of one MX scale group; also the N-extent of a weight scale block
+
+
+def e8m0_value(code: int) -> float:
+    """fp64 value of one E8M0 scale byte (OCP MX: 2^(code - 127), 0xFF is NaN)."""
+    return _load().a8w8_oracle_e8m0_value(int(code) & 0xFF)
+
+
+def gemm_mx(A: np.ndarray, a_scale: np.ndarray, W: np.ndarray, w_scale: np.ndarray,
+            rows=None) -> np.ndarray:
+    """MX-scaled Y (float64) = dequant(A) . dequant(W)^T, all rows or only ``rows``.
+
+    The mxfp8 GEMM with 32 x 32 weight-scale blocks that the gfx1250 BF16 and
+    MX32 tuned-rows page (ROCm/aiter #7247) tunes, read with OCP MX scales:
+    A uint8 e4m3fn [M,K]; a_scale uint8 E8M0 [M, ceil(K/32)] (one per row and
+    32-wide K group); W uint8 e4m3fn [N,K]; w_scale uint8 E8M0
+    [ceil(N/32), ceil(K/32)] (one per 32 x 32 block).  A value is
+    e4m3fn(code) * 2^(scale - 127).  Returns [len(rows) or M, N].
+    """
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.uint8)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.uint8)
+    M, K = A.shape
+    N, K2 = W.shape
+    if K2 != K:
+        raise ValueError("A and W disagree on K")
+    KG = (K + MX_GROUP - 1) // MX_GROUP
+    NB = (N + MX_GROUP - 1) // MX_GROUP
+    if a_scale.shape != (M, KG) or w_scale.shape != (NB, KG):
+        raise ValueError("scale shapes must be [M, ceil(K/32)] and [ceil(N/32), ceil(K/32)]")
+    if rows is None:
+        n_rows, rows_ptr = M, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows, rows_ptr = rows_arr.size, rows_arr.ctypes.data
+    Y = np.empty((n_rows, N), dtype=np.float64)
+    rc = _load().a8w8_oracle_gemm_mx(A.ctypes.data, a_scale.ctypes.data, W.ctypes.data,
+                                     w_scale.ctypes.data, M, N, K, rows_ptr, n_rows,
+                                     Y.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("a8w8_oracle_gemm_mx failed with code %d" % rc)
+    return Y
+
+
+def gemm_mx_batched(A, a_scale, W, w_scale, rows=None) -> np.ndarray:
+    """The batched form (page: b = 8 batches of N = 1024, K = 4096): batch i is
+    ``gemm_mx`` of the i-th slice of every operand.  Shapes carry a leading batch
+    dimension; ``rows`` (optional) selects the same rows of every batch."""
+    return np.stack([gemm_mx(A[i], a_scale[i], W[i], w_scale[i], rows=rows)
+                     for i in range(A.shape[0])])

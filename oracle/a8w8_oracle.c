@@ -142,3 +142,103 @@ int a8w8_oracle_gemm(const uint8_t *A, const float *a_scale,
     free(Ad);
     return bad ? -2 : 0;
 }
+
+/*
+ * MX-scaled variant: the "32x32" weight-scale blocks of the mxfp8 GEMMs on the
+ * gfx1250 BF16 and MX32 tuned-rows page (ROCm/aiter #7247, Motivation and
+ * Technical Details).  That page gives the block shape of the weight scales
+ * and the "mxfp8" element type but no formula; the reading here follows the
+ * OCP Microscaling (MX) format: every scale is one E8M0 byte (an unsigned
+ * power-of-two exponent with bias 127, 0xFF = NaN), activations carry one
+ * scale per row per 32-wide K group and weights one per 32 x 32 block.
+ *
+ *   Ad[m,k] = e4m3fn(A[m,k]) * e8m0(a_scale[m, k/32])
+ *   Wd[n,k] = e4m3fn(W[n,k]) * e8m0(w_scale[n/32, k/32])
+ *   Y[m,n]  = sum_k Ad[m,k] * Wd[n,k]            (fp64, k ascending, not rounded)
+ *
+ * Layouts (row-major): A uint8 [M,K]; a_scale uint8 [M, ceil(K/32)];
+ * W uint8 [N,K]; w_scale uint8 [ceil(N/32), ceil(K/32)]; Y double [n_rows, N].
+ */
+double a8w8_oracle_e8m0_value(uint8_t code)
+{
+    if (code == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+int a8w8_oracle_gemm_mx(const uint8_t *A, const uint8_t *a_scale,
+                        const uint8_t *W, const uint8_t *w_scale,
+                        int64_t M, int64_t N, int64_t K,
+                        const int64_t *rows, int64_t n_rows, double *Y)
+{
+    const int64_t G = 32;
+    int64_t KG, r, nb, NB;
+    double table[256], scale[256];
+    double *Ad;
+    int bad = 0;
+
+    if (M < 0 || N < 0 || K < 0 || n_rows < 0)
+        return -1;
+    if (rows == NULL && n_rows != M)
+        return -1;
+    if (n_rows == 0 || N == 0)
+        return 0;
+    if (K == 0) {
+        memset(Y, 0, (size_t)(n_rows * N) * sizeof(double));
+        return 0;
+    }
+    if (!A || !a_scale || !W || !w_scale || !Y)
+        return -1;
+    for (r = 0; r < n_rows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        if (m < 0 || m >= M)
+            return -1;
+    }
+
+    for (int c = 0; c < 256; ++c) {
+        table[c] = a8w8_oracle_e4m3fn_value((uint8_t)c);
+        scale[c] = a8w8_oracle_e8m0_value((uint8_t)c);
+    }
+
+    KG = (K + G - 1) / G;
+    NB = (N + G - 1) / G;
+
+    /* Dequantised activation rows (each dec(q) * 2^e is exact in fp64). */
+    Ad = (double *)malloc((size_t)(n_rows * K) * sizeof(double));
+    if (!Ad)
+        return -2;
+    for (r = 0; r < n_rows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t k = 0; k < K; ++k)
+            Ad[r * K + k] = table[A[m * K + k]] * scale[a_scale[m * KG + k / G]];
+    }
+
+    /* One 32-row block of W at a time: dequantise it, then take the dots. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (nb = 0; nb < NB; ++nb) {
+        int64_t n0 = nb * G;
+        int64_t rows_here = (N - n0 < G) ? (N - n0) : G;
+        double *Wd = (double *)malloc((size_t)(rows_here * K) * sizeof(double));
+        if (!Wd) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (int64_t i = 0; i < rows_here; ++i)
+            for (int64_t k = 0; k < K; ++k)
+                Wd[i * K + k] = table[W[(n0 + i) * K + k]] * scale[w_scale[nb * KG + k / G]];
+        for (int64_t rr = 0; rr < n_rows; ++rr) {
+            const double *a = Ad + rr * K;
+            for (int64_t i = 0; i < rows_here; ++i) {
+                const double *w = Wd + i * K;
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += a[k] * w[k];
+                Y[rr * N + n0 + i] = acc;
+            }
+        }
+        free(Wd);
+    }
+    free(Ad);
+    return bad ? -2 : 0;
+}
