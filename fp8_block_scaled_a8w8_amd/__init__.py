@@ -9,6 +9,11 @@ the C ABI in ``include/gemm_a8w8_blockscale.h``.
 A ``float8_e4m3fn`` (or uint8 bytes) [M,K]; a_scale float32 [M,K/128];
 W ``float8_e4m3fn`` (or uint8) [N,K]; w_scale float32 [ceil(N/128),K/128];
 Y bfloat16 [M,N].
+
+The MX-scaled variant (``gemm_a8w8_mxscale`` and its batched and packed
+forms) takes E8M0 scale bytes instead: a_scale uint8 [M,K/32] (one per row
+per 32-wide K group), w_scale uint8 [ceil(N/32),K/32] (one per 32x32 block),
+value 2^(e-127).
 """
 from __future__ import annotations
 
@@ -42,6 +47,12 @@ EXPORTED = (
     "a8w8_prepack_weights",
     "gemm_a8w8_blockscale_packed",
     "gemm_a8w8_blockscale_packed_run_variant",
+    "gemm_a8w8_mxscale",
+    "gemm_a8w8_mxscale_packed",
+    "batched_gemm_a8w8_mxscale",
+    "batched_gemm_a8w8_mxscale_packed",
+    "gemm_a8w8_mxscale_plan",
+    "gemm_a8w8_mxscale_run_variant",
 )
 
 
@@ -100,6 +111,16 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_blockscale_packed.argtypes = [vp] * 5 + [i64] * 3 + [vp]
         L.gemm_a8w8_blockscale_packed_run_variant.restype = ctypes.c_int
         L.gemm_a8w8_blockscale_packed_run_variant.argtypes = [i32] + [vp] * 5 + [i64] * 3 + [vp]
+        for name in ("gemm_a8w8_mxscale", "gemm_a8w8_mxscale_packed"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [vp] * 5 + [i64] * 3 + [vp]
+        for name in ("batched_gemm_a8w8_mxscale", "batched_gemm_a8w8_mxscale_packed"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [vp] * 5 + [i64] * 4 + [vp]
+        L.gemm_a8w8_mxscale_plan.restype = ctypes.c_int
+        L.gemm_a8w8_mxscale_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        L.gemm_a8w8_mxscale_run_variant.restype = ctypes.c_int
+        L.gemm_a8w8_mxscale_run_variant.argtypes = [i32] + [vp] * 5 + [i64] * 4 + [i32, vp]
         _lib = L
     return _lib
 
@@ -278,3 +299,98 @@ def gemm_a8w8_blockscale_packed_run_variant(variant: int, A, a_scale, Wp, w_scal
 def variants() -> list[dict]:
     """Descriptions of every compiled kernel instance."""
     return [gemm_a8w8_describe_variant(i) for i in range(gemm_a8w8_num_variants())]
+
+
+# ---------------------------------------------------------------------------
+# MX-scaled variant (E8M0 scales: 1x32 activation groups, 32x32 weight blocks)
+
+_E8M0_DTYPES = tuple(d for d in (torch.uint8, getattr(torch, "float8_e8m0fnu", None)) if d is not None)
+
+
+def _check_mx(A, a_scale, W, w_scale, out, batched: bool, N: int | None = None):
+    """Validate MX operands; W is row-major [.., N, K] or (N given) packed [.., 16*ceil(N/16), K]."""
+    nd = 3 if batched else 2
+    for name, t in (("A", A), ("W", W)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or t.dim() != nd:
+            raise TypeError(f"{name} must be a {nd}-D float8_e4m3fn (or uint8) tensor")
+    for name, t in (("a_scale", a_scale), ("w_scale", w_scale)):
+        if t.dtype not in _E8M0_DTYPES or t.dim() != nd:
+            raise TypeError(f"{name} must be a {nd}-D uint8 (E8M0 code) tensor")
+    batch = A.shape[0] if batched else 1
+    M, K = A.shape[-2:]
+    rows, K2 = W.shape[-2:]
+    if N is None:
+        N = rows
+    elif rows != packed_rows(N):
+        raise ValueError(f"packed weights for N={N} have {packed_rows(N)} rows, got {rows}")
+    if K2 != K:
+        raise ValueError(f"A is [..,M,{K}] but W is [..,N,{K2}]")
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    lead = (batch,) if batched else ()
+    if batched and (W.shape[0] != batch or a_scale.shape[0] != batch or w_scale.shape[0] != batch):
+        raise ValueError("every operand needs the same batch count")
+    if tuple(a_scale.shape) != lead + (M, K // 32) or tuple(w_scale.shape) != lead + ((N + 31) // 32, K // 32):
+        raise ValueError(f"MX scale shapes must be {lead + (M, K // 32)} and {lead + ((N + 31) // 32, K // 32)}, "
+                         f"got {tuple(a_scale.shape)} and {tuple(w_scale.shape)}")
+    for name, t in (("A", A), ("a_scale", a_scale), ("W", W), ("w_scale", w_scale)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty(lead + (M, N), dtype=torch.bfloat16, device=A.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != lead + (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 {lead + (M, N)} tensor")
+    return batch, M, N, K, out
+
+
+def _mx_call(name, A, a_scale, W, w_scale, out, batched, N, stream):
+    batch, M, N, K, out = _check_mx(A, a_scale, W, w_scale, out, batched, N)
+    args = [A.data_ptr(), a_scale.data_ptr(), W.data_ptr(), w_scale.data_ptr(), out.data_ptr()]
+    args += [batch, M, N, K] if batched else [M, N, K]
+    rc = getattr(lib(), name)(*args, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, name)
+    return out
+
+
+def gemm_a8w8_mxscale(A, a_scale, W, w_scale, out=None, stream=None) -> torch.Tensor:
+    """MX-scaled Y = A . W^T (E8M0 scales per 1x32 activation group and 32x32 weight block); bf16 [M,N]."""
+    return _mx_call("gemm_a8w8_mxscale", A, a_scale, W, w_scale, out, False, None, stream)
+
+
+def gemm_a8w8_mxscale_packed(A, a_scale, Wp, w_scale, N: int, out=None, stream=None) -> torch.Tensor:
+    """gemm_a8w8_mxscale with W in the packed layout (prepack_weights)."""
+    return _mx_call("gemm_a8w8_mxscale_packed", A, a_scale, Wp, w_scale, out, False, N, stream)
+
+
+def batched_gemm_a8w8_mxscale(A, a_scale, W, w_scale, out=None, stream=None) -> torch.Tensor:
+    """Batched MX GEMM: A [b,M,K], a_scale [b,M,K/32], W [b,N,K], w_scale [b,ceil(N/32),K/32] -> bf16 [b,M,N]."""
+    return _mx_call("batched_gemm_a8w8_mxscale", A, a_scale, W, w_scale, out, True, None, stream)
+
+
+def batched_gemm_a8w8_mxscale_packed(A, a_scale, Wp, w_scale, N: int, out=None, stream=None) -> torch.Tensor:
+    """batched_gemm_a8w8_mxscale with each batch's W packed (Wp [b,16*ceil(N/16),K])."""
+    return _mx_call("batched_gemm_a8w8_mxscale_packed", A, a_scale, Wp, w_scale, out, True, N, stream)
+
+
+def gemm_a8w8_mxscale_plan(M: int, N: int, K: int, cu_count: int = 0) -> dict:
+    p = Plan()
+    rc = lib().gemm_a8w8_mxscale_plan(M, N, K, cu_count, ctypes.byref(p))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_mxscale_plan")
+    d = p.as_dict()
+    d["name"] = gemm_a8w8_variant_name(d["variant"])
+    return d
+
+
+def gemm_a8w8_mxscale_run_variant(variant: int, A, a_scale, W, w_scale, out=None, stream=None,
+                                  packed_n: int | None = None) -> torch.Tensor:
+    """MX GEMM with a fixed kernel instance; 2-D operands or 3-D (batched); packed W when packed_n is given."""
+    batched = A.dim() == 3
+    batch, M, N, K, out = _check_mx(A, a_scale, W, w_scale, out, batched, packed_n)
+    rc = lib().gemm_a8w8_mxscale_run_variant(variant, A.data_ptr(), a_scale.data_ptr(), W.data_ptr(),
+                                             w_scale.data_ptr(), out.data_ptr(), batch, M, N, K,
+                                             1 if packed_n is not None else 0, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, f"gemm_a8w8_mxscale_run_variant({variant})")
+    return out

@@ -36,6 +36,8 @@ constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // The tile kernel addresses a tile's rows with 32-bit offsets: 256 * K < 2^31.
 constexpr int64_t kMaxK = (int64_t)1 << 22;
+// Batches are the grid's y dimension.
+constexpr int64_t kMaxBatch = 65535;
 
 // Per-device state: 0 = not yet checked, 1 = gfx950 ready, 2 = unsupported.
 std::atomic<int> g_dev_state[kMaxDevices];
@@ -84,7 +86,7 @@ int check_shape(int64_t M, int64_t N, int64_t K)
     return A8W8_OK;
 }
 
-int check_pointers(const void *A, const float *a_scale, const void *W, const float *w_scale, const void *Y)
+int check_pointers(const void *A, const void *a_scale, const void *W, const void *w_scale, const void *Y)
 {
     if (!A || !a_scale || !W || !w_scale || !Y)
         return A8W8_ERR_NULL;
@@ -242,64 +244,104 @@ void log_plan(int64_t M, int64_t N, int64_t K, int id, int64_t key_m, int fallba
                  (long long)K, a8w8::variant(id).name, (long long)key_m, fallback ? " fallback" : "");
 }
 
-int launch(int id, const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
-           int64_t M, int64_t N, int64_t K, int cus, void *stream, int wpk)
+// Operand set of one call: `batch` consecutive problems of one shape.
+struct Operands {
+    const void *A;
+    const void *a_scale;
+    const void *W;
+    const void *w_scale;
+    void *Y;
+    int64_t batch;
+    int wpk;   // W in the packed layout
+    int mx;    // MX (E8M0) scales instead of fp32 block scales
+};
+
+// Elements of each array per batch (scale arrays in 32-bit words: an MX row of
+// K/32 bytes is K/128 words, the same count as a row of fp32 block scales).
+void batch_strides(const Operands &o, int64_t M, int64_t N, int64_t K, Args &a)
+{
+    const int64_t KB = K / 128;
+    const int64_t w_rows = o.wpk ? (N + 15) / 16 * 16 : N;
+    const int64_t s_rows = o.mx ? (N + 31) / 32 : (N + 127) / 128;
+    a.bs_a = M * K;
+    a.bs_as = M * KB;
+    a.bs_w = w_rows * K;
+    a.bs_ws = s_rows * KB;
+    a.bs_y = M * N;
+}
+
+int launch(int id, const Operands &o, int64_t M, int64_t N, int64_t K, int cus, void *stream)
 {
     Args a;
-    a.A = static_cast<const uint8_t *>(A);
-    a.a_scale = a_scale;
-    a.W = static_cast<const uint8_t *>(W);
-    a.w_scale = w_scale;
-    a.Y = static_cast<uint16_t *>(Y);
+    a.A = static_cast<const uint8_t *>(o.A);
+    a.a_scale = static_cast<const float *>(o.a_scale);
+    a.W = static_cast<const uint8_t *>(o.W);
+    a.w_scale = static_cast<const float *>(o.w_scale);
+    a.Y = static_cast<uint16_t *>(o.Y);
     a.M = (int32_t)M;
     a.N = (int32_t)N;
     a.K = (int32_t)K;
-    a.wpk = wpk;
-    if (a8w8::launch_variant(id, a, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
+    a.wpk = o.wpk;
+    a.mx = o.mx;
+    batch_strides(o, M, N, K, a);
+    if (a8w8::launch_variant(id, a, (int)o.batch, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
         return A8W8_ERR_HIP;
     return A8W8_OK;
 }
 
-int gemm_impl(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y, int64_t M,
-              int64_t N, int64_t K, void *stream, int wpk)
+// Shape checks common to every call, plus the batched and MX limits.
+int check_call(const Operands &o, int64_t M, int64_t N, int64_t K)
 {
     int rc = check_shape(M, N, K);
     if (rc != A8W8_OK)
         return rc;
-    if (M == 0)
+    if (o.batch < 0 || o.batch > kMaxBatch)
+        return A8W8_ERR_SHAPE;
+    // MX weight-scale rows (one per 32 weight rows): the pskinny kernel's
+    // descriptor spans them in 32 bits, the kernels index them in 31.
+    if (o.mx && (N + 31) / 32 * (K / 128) * 4 >= ((int64_t)1 << 31))
+        return A8W8_ERR_SHAPE;
+    return A8W8_OK;
+}
+
+int gemm_impl(const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    int rc = check_call(o, M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M == 0 || o.batch == 0)
         return A8W8_OK;
-    rc = check_pointers(A, a_scale, W, w_scale, Y);
+    rc = check_pointers(o.A, o.a_scale, o.W, o.w_scale, o.Y);
     if (rc != A8W8_OK)
         return rc;
     int cus = 0;
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    const Choice c = select_variant(M, N, K, cus);
+    const Choice c = o.mx ? Choice{heuristic_variant(M, N, K, cus), M, 1} : select_variant(M, N, K, cus);
     log_plan(M, N, K, c.variant, c.key_m, c.fallback);
-    return launch(c.variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream, wpk);
+    return launch(c.variant, o, M, N, K, cus, stream);
 }
 
-int run_variant_impl(int32_t variant, const void *A, const float *a_scale, const void *W, const float *w_scale,
-                     void *Y, int64_t M, int64_t N, int64_t K, void *stream, int wpk)
+int run_variant_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
 {
     if (variant < 0 || variant >= a8w8::num_variants())
         return A8W8_ERR_PLAN;
-    int rc = check_shape(M, N, K);
+    int rc = check_call(o, M, N, K);
     if (rc != A8W8_OK)
         return rc;
-    if (M == 0)
+    if (M == 0 || o.batch == 0)
         return A8W8_OK;
     if (!variant_accepts(variant, M, N, K))
         return A8W8_ERR_PLAN;
-    rc = check_pointers(A, a_scale, W, w_scale, Y);
+    rc = check_pointers(o.A, o.a_scale, o.W, o.w_scale, o.Y);
     if (rc != A8W8_OK)
         return rc;
     int cus = 0;
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    return launch(variant, A, a_scale, W, w_scale, Y, M, N, K, cus, stream, wpk);
+    return launch(variant, o, M, N, K, cus, stream);
 }
 
 }  // namespace
@@ -309,13 +351,56 @@ extern "C" {
 int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
                          int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl(A, a_scale, W, w_scale, Y, M, N, K, stream, 0);
+    return gemm_impl({A, a_scale, W, w_scale, Y, 1, 0, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_blockscale_packed(const void *A, const float *a_scale, const void *Wp, const float *w_scale, void *Y,
                                 int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl(A, a_scale, Wp, w_scale, Y, M, N, K, stream, 1);
+    return gemm_impl({A, a_scale, Wp, w_scale, Y, 1, 1, 0}, M, N, K, stream);
+}
+
+int gemm_a8w8_mxscale(const void *A, const void *a_scale, const void *W, const void *w_scale, void *Y, int64_t M,
+                      int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl({A, a_scale, W, w_scale, Y, 1, 0, 1}, M, N, K, stream);
+}
+
+int gemm_a8w8_mxscale_packed(const void *A, const void *a_scale, const void *Wp, const void *w_scale, void *Y,
+                             int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl({A, a_scale, Wp, w_scale, Y, 1, 1, 1}, M, N, K, stream);
+}
+
+int batched_gemm_a8w8_mxscale(const void *A, const void *a_scale, const void *W, const void *w_scale, void *Y,
+                              int64_t batch, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl({A, a_scale, W, w_scale, Y, batch, 0, 1}, M, N, K, stream);
+}
+
+int batched_gemm_a8w8_mxscale_packed(const void *A, const void *a_scale, const void *Wp, const void *w_scale,
+                                     void *Y, int64_t batch, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl({A, a_scale, Wp, w_scale, Y, batch, 1, 1}, M, N, K, stream);
+}
+
+int gemm_a8w8_mxscale_run_variant(int32_t variant, const void *A, const void *a_scale, const void *W,
+                                  const void *w_scale, void *Y, int64_t batch, int64_t M, int64_t N, int64_t K,
+                                  int32_t w_packed, void *stream)
+{
+    return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, batch, w_packed ? 1 : 0, 1}, M, N, K, stream);
+}
+
+int gemm_a8w8_mxscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
+{
+    if (!out)
+        return A8W8_ERR_NULL;
+    const int rc = check_call({nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0, 1}, M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    const int cus = cu_count > 0 ? cu_count : 256;
+    fill_plan(heuristic_variant(M > 0 ? M : 1, N, K, cus), M, N, K, cus, M, 1, out);
+    return A8W8_OK;
 }
 
 int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
@@ -349,14 +434,14 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant, const void *A, const float
                                      const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
                                      void *stream)
 {
-    return run_variant_impl(variant, A, a_scale, W, w_scale, Y, M, N, K, stream, 0);
+    return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, 1, 0, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_blockscale_packed_run_variant(int32_t variant, const void *A, const float *a_scale, const void *Wp,
                                             const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
                                             void *stream)
 {
-    return run_variant_impl(variant, A, a_scale, Wp, w_scale, Y, M, N, K, stream, 1);
+    return run_variant_impl(variant, {A, a_scale, Wp, w_scale, Y, 1, 1, 0}, M, N, K, stream);
 }
 
 int a8w8_prepack_weights(const void *W, void *Wp, int64_t N, int64_t K, void *stream)
@@ -388,7 +473,7 @@ const char *gemm_a8w8_status_string(int status)
     switch (status) {
     case A8W8_OK: return "ok";
     case A8W8_ERR_NULL: return "a required pointer is NULL";
-    case A8W8_ERR_SHAPE: return "invalid shape (need M >= 0, N >= 1, K >= 1, K % 128 == 0, M, N <= 2^30, K <= 2^22)";
+    case A8W8_ERR_SHAPE: return "invalid shape (need M >= 0, N >= 1, K >= 1, K % 128 == 0, M, N <= 2^30, K <= 2^22, 0 <= batch <= 65535)";
     case A8W8_ERR_ALIGN: return "misaligned buffer (A and W need 16 bytes, scales 4, Y 2)";
     case A8W8_ERR_ARCH: return "the current device is not gfx950 (MI355X)";
     case A8W8_ERR_HIP: return "HIP runtime call or kernel launch failed";

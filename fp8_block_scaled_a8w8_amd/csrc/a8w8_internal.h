@@ -25,7 +25,11 @@ struct Args {
     const float *w_scale;
     uint16_t *Y;
     int32_t M, N, K;
-    int32_t wpk;       // 1: W is in the packed (fragment-order) layout, see packed_piece
+    int32_t wpk;       // 1: W is in the packed (fragment-order) layout, see packed_block
+    int32_t mx;        // 1: MX scales (E8M0 bytes: 1 x 32 activation groups, 32 x 32 weight blocks)
+    // Batched calls: gridDim.y batches; batch z reads A + z * bs_a, a_scale + z * bs_as,
+    // W + z * bs_w, w_scale + z * bs_ws and writes Y + z * bs_y (elements of each array).
+    int64_t bs_a, bs_as, bs_w, bs_ws, bs_y;
 };
 
 int num_variants();
@@ -39,8 +43,8 @@ int64_t variant_passes(int id, int64_t K);
 // Raise the dynamic-LDS limit of the instances that need more than 64 KB
 // (once per device, with that device current).
 hipError_t set_kernel_attributes();
-// Enqueue the instance; returns hipSuccess or the launch error.
-hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream);
+// Enqueue the instance for `batch` batches (grid y); returns hipSuccess or the launch error.
+hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t stream);
 // Enqueue the conversion of row-major W [N, K] to the packed layout.
 hipError_t launch_prepack(const void *W, void *Wp, int64_t N, int64_t K, int cus, hipStream_t stream);
 // Enqueue the per-1x128 activation quantisation of `groups` groups.

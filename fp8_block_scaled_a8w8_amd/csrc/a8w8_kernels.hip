@@ -13,10 +13,26 @@
 //
 // Operand roles: the MFMA "A" operand is W (rows n), the "B" operand is the
 // activation (columns m).  Lane l of a wave holds, for both operands, row
-// (l % 16) of its 16-row slice and the 32 K bytes [32*(l/16), 32*(l/16)+32) of
-// the block; its 4 results are D[n = 4*(l/16)+i][m = l%16], i = 0..3.  So one
+// (l % 16) of its 16-row slice and two 16-byte K chunks of the block: chunk
+// g = l/16 (K bytes 16g..16g+15) in its first four registers and chunk g + 4
+// (K bytes 64+16g..) in the last four -- the K order the instruction itself
+// uses (measured: a byte's position selects its 32-wide scale group exactly
+// so).  Its 4 results are D[n = 4*(l/16)+i][m = l%16], i = 0..3.  So one
 // lane's outputs share one activation row, and a single a_scale value per
 // (lane, block) suffices.
+//
+// MX-scaled variant (compile-time MX): the mxfp8 GEMM with 32 x 32
+// weight-scale blocks of the gfx1250 BF16 and MX32 tuned-rows page (ROCm/aiter
+// #7247, Motivation and Technical Details), read with OCP MX scales: one E8M0
+// byte (2^(e-127)) per activation row and 32-wide K group and per 32 x 32
+// weight block.  A row of such scales holds K/32 bytes = K/128 32-bit words,
+// word kb packing the four groups of K block kb (lowest K in the low byte), so
+// every kernel fetches MX scale words exactly where it fetches fp32 block
+// scales (weight rows counted per 32 instead of per 128).  The instruction
+// takes the scale of its K group q (K bytes 32q..32q+31 in its own K order,
+// which the operand layout below follows) from lane 16q + row, so lane l hands
+// byte l/16 of its words to the scaled MFMA, which applies both operands'
+// 2^(e-127) itself and accumulates in place: no per-block scale FMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,6 +79,44 @@ __device__ __forceinline__ v4f fma4(v4f d, float s, v4f acc)
     return acc;
 }
 
+// MX block step: acc += the block's 16 x 16 dot with every operand group
+// scaled by its E8M0 value.  w_word / a_word are the 32-bit scale words (in
+// float registers, never used as numbers) of the lane's weight row and
+// activation row; byte g = l/16 is the lane's K group.  Scale operand "a"
+// belongs to the first MFMA operand (W), "b" to the second (activations).
+__device__ __forceinline__ v4f mfma_mx(v8i w, v8i a, v4f acc, float w_word, float a_word, int g)
+{
+    const int ws = (int)(__float_as_uint(w_word) >> (8 * g));
+    const int as = (int)(__float_as_uint(a_word) >> (8 * g));
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, acc, 0, 0, 0, ws, 0, as);
+}
+
+// One K block into the accumulator: block scale (the fp32 product of the two
+// scales, one FMA per output) or MX (E8M0 scales inside the MFMA).
+template <bool MX>
+__device__ __forceinline__ v4f block_step(v4f acc, v8i w, v8i a, float sw, float sa, int g)
+{
+    if constexpr (MX)
+        return mfma_mx(w, a, acc, sw, sa, g);
+    else
+        return fma4(mfma_block(w, a), sa * sw, acc);
+}
+
+// Weight rows covered by one scale row: 128 (block scale) or 32 (MX).
+template <bool MX>
+constexpr int wscale_shift() { return MX ? 5 : 7; }
+
+// Batched launches: batch blockIdx.y works on its own slice of every array.
+__device__ __forceinline__ void select_batch(Args &p)
+{
+    const int64_t z = (int64_t)blockIdx.y;
+    p.A += z * p.bs_a;
+    p.a_scale += z * p.bs_as;
+    p.W += z * p.bs_w;
+    p.w_scale += z * p.bs_ws;
+    p.Y += z * p.bs_y;
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f)
 {
@@ -106,9 +160,9 @@ __device__ __forceinline__ void store4(uint16_t *Y, int64_t row_off, int n, int 
 //
 // Weight loads cover whole 128-byte lines: load 0 of a block takes rows 0-7 of
 // the 16-row tile and load 1 rows 8-15, lane (rho = l/16, p = l%16) reading
-// chunk 2 rho + (p >= 8) of row (p & 7) (+8).  A row_ror:8 DPP exchange between
-// lanes p and p+8 of each 16-lane row then leaves lane l with row l%16, bytes
-// [32 rho, 32 rho + 32) of the block -- the MFMA operand layout.  Streaming
+// chunk rho + 4 (p >= 8) of row (p & 7) (+8).  A row_ror:8 DPP exchange between
+// lanes p and p+8 of each 16-lane row then leaves lane l with row l%16, chunks
+// rho and rho + 4 of the block -- the MFMA operand layout.  Streaming
 // whole lines per instruction is what lets the loads run at the HBM ceiling;
 // the half-line pattern of a direct MFMA-layout load measured ~35% slower.
 __device__ __forceinline__ v8i fix_row_layout(v4i v0, v4i v1)
@@ -126,7 +180,7 @@ __device__ __forceinline__ v8i fix_row_layout(v4i v0, v4i v1)
 // Packed weights (the optional offline layout a8w8_prepack_weights writes):
 // rows padded with zeros to a multiple of 16; for every 16-row tile t and K
 // block kb, 2 KB in MFMA operand order, [h][lane][16 bytes], lane l holding
-// row 16t + l%16, 16-byte chunk 2(l/16) + h of the block.  A wave then reads
+// row 16t + l%16, 16-byte chunk l/16 + 4h of the block.  A wave then reads
 // each half of a fragment (1 KB) with one contiguous load and needs no lane
 // exchange.  Byte offset of tile t, block kb:
 __device__ __forceinline__ uint32_t packed_block(uint32_t tile, uint32_t kb, uint32_t KB)
@@ -145,9 +199,10 @@ __device__ __forceinline__ uint32_t w_rows(const Args &p)
     return PK ? (uint32_t)((p.N + 15) & ~15) : (uint32_t)p.N;
 }
 
-template <int TPW, int D, int NW, bool PK>
+template <int TPW, int D, int NW, bool PK, bool MX>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 {
+    select_batch(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
@@ -156,11 +211,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     const bool mval = r16 < M;
 
     // Whole-line load addressing (see fix_row_layout): load h of a block takes
-    // row 8h + (r16 & 7), 16-byte chunk 2g + (r16 >> 3).  Loads go through
+    // row 8h + (r16 & 7), 16-byte chunk g + 4 (r16 >> 3).  Loads go through
     // buffer descriptors: a 32-bit per-lane offset (the host keeps N*K and
     // M*K below 2^32) plus the wave-uniform block offset kb*128.
     const int lrow = r16 & 7;
-    const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
+    const uint32_t lcol = (uint32_t)(g + 4 * (r16 >> 3)) * 16;
     constexpr bool pk = PK;
     const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
@@ -182,8 +237,14 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
         aoff[h] = (uint32_t)(m < M ? m : 0) * (uint32_t)K + lcol;
     }
     const float *asp = p.a_scale + (size_t)(mval ? r16 : 0) * KB;
-    // RG divides 128, so the row group lies in one 128-row weight block.
-    const float *wsp = p.w_scale + (size_t)(n0 >> 7) * KB;
+    // Weight scale rows.  Block scale: RG divides 128, so the row group lies in
+    // one 128-row block.  MX: tiles 2i and 2i+1 lie in one 32-row block (RG is
+    // 16 or a multiple of 32); tiles past N read the last block.
+    constexpr int WS = MX ? (TPW + 1) / 2 : 1;
+    const float *wsp[WS];
+#pragma unroll
+    for (int i = 0; i < WS; ++i)
+        wsp[i] = p.w_scale + (size_t)(MX ? min((n0 >> 5) + i, (N - 1) >> 5) : (n0 >> 7)) * KB;
 
     v4f acc[TPW];
 #pragma unroll
@@ -193,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
         v4i ar[D][2];
         v4i wr[D][TPW][2];
-        float sa[D], sw[D];
+        float sa[D], sw[D][WS];
         // Issue every load of the pass before consuming any of them.
 #pragma unroll
         for (int j = 0; j < D; ++j) {
@@ -210,17 +271,19 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
             for (int h = 0; h < 2; ++h)
                 ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[h], koff, 0);
             sa[j] = asp[kb];
-            sw[j] = wsp[kb];
+#pragma unroll
+            for (int i = 0; i < WS; ++i)
+                sw[j][i] = wsp[i][kb];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             if (kb_begin + j < KB) {
                 const v8i af = fix_row_layout(ar[j][0], ar[j][1]);
-                const float sc = sa[j] * sw[j];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
-                    acc[t] = fma4(mfma_block(w_fragment(wr[j][t][0], wr[j][t][1], pk), af), sc, acc[t]);
+                    acc[t] = block_step<MX>(acc[t], w_fragment(wr[j][t][0], wr[j][t][1], pk), af,
+                                            sw[j][MX ? t >> 1 : 0], sa[j], g);
             }
         }
     }
@@ -273,9 +336,10 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 // wave order (fixed order: bitwise deterministic) and stores the 16 x 16
 // bf16 tile.  Loads for tiles past the workgroup's share go through a
 // descriptor of zero records, which returns zeros without touching memory.
-template <int D, int NW, int P, bool PK>
+template <int D, int NW, int P, bool PK, bool MX>
 __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 {
+    select_batch(p);
     __shared__ v4f red[2][NW][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -289,12 +353,16 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
     const bool vec = vec_store != 0;
 
     const int lrow = r16 & 7;
-    const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
+    const uint32_t lcol = (uint32_t)(g + 4 * (r16 >> 3)) * 16;
     constexpr bool pk = PK;
     const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.W, 0u);
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(p.w_scale, (uint32_t)((N + 127) >> 7) * (uint32_t)KB * 4u);
+    // Weight scale rows: one per 128 rows (block scale) or per 32 (MX); a
+    // 16-row tile lies in one.
+    constexpr int SH = wscale_shift<MX>();
+    const __amdgpu_buffer_rsrc_t sres =
+        buffer_rsrc(p.w_scale, (uint32_t)((N + (1 << SH) - 1) >> SH) * (uint32_t)KB * 4u);
 
     // This wave's activation blocks and scales, held for the whole kernel
     // (put into the MFMA layout once the first weight loads are issued).
@@ -329,7 +397,7 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
         for (int h = 0; h < 2; ++h)
             woff[h] = pk ? (uint32_t)(lane * 16 + h * 1024)
                          : (uint32_t)min(n0 + 8 * h + lrow, N - 1) * (uint32_t)K + lcol;
-        const int srow = (n0 >> 7) * KB;
+        const int srow = (n0 >> SH) * KB;
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int kb = min(kb0 + j, KB - 1);
@@ -346,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 #pragma unroll
         for (int j = 0; j < D; ++j)
             if (kb0 + j < KB)
-                acc = fma4(mfma_block(w_fragment(wr[j][0], wr[j][1], pk), af[j]), sa[j] * sw[j], acc);
+                acc = block_step<MX>(acc, w_fragment(wr[j][0], wr[j][1], pk), af[j], sw[j], sa[j], g);
         red[i & 1][wave][lane] = acc;
         __syncthreads();
         if (wave == i % NW) {
@@ -399,16 +467,18 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 // output row and take one a_scale per block).  Per block: TPW * NT MFMAs,
 // each followed by one scale FMA per output; the wave partials are summed
 // through LDS in wave order and rounded once.
-template <int TPW, int NT, int D, int NW, bool PK>
+template <int TPW, int NT, int D, int NW, bool PK, bool MX>
 __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
 {
+    static_assert(16 * NT <= (MX ? 32 : 128), "every weight row lies in weight-scale row 0");
+    select_batch(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
     const int m0 = (int)blockIdx.x * (16 * TPW);
     const int r16 = lane & 15, g = lane >> 4;
     const int lrow = r16 & 7;
-    const uint32_t lcol = (uint32_t)(2 * g + (r16 >> 3)) * 16;
+    const uint32_t lcol = (uint32_t)(g + 4 * (r16 >> 3)) * 16;
     constexpr bool pk = PK;
     const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
@@ -431,7 +501,7 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
         asp[t] = p.a_scale + (size_t)min(m0 + 16 * t + r16, M - 1) * KB;
-    // 16 * NT <= 128: every weight row lies in weight block 0.
+    // 16 * NT rows: all in weight-scale row 0 (block scale and MX).
     const float *wsp = p.w_scale;
 
     v4f acc[TPW][NT];
@@ -476,10 +546,9 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const v8i af = fix_row_layout(ar[j][t][0], ar[j][t][1]);
-                    const float sc = sa[j][t] * sw[j];
 #pragma unroll
                     for (int u = 0; u < NT; ++u)
-                        acc[t][u] = fma4(mfma_block(wf[u], af), sc, acc[t][u]);
+                        acc[t][u] = block_step<MX>(acc[t][u], wf[u], af, sw[j], sa[j][t], g);
                 }
             }
         }
@@ -600,21 +669,23 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // LDS tiles are row-major 128-byte rows whose 16-byte chunk c sits at chunk
 // position c ^ chunk_swizzle(row).  A fragment read has lane (g = l/16,
-// p = l%16) read chunk 2g (then 2g+1) of row r0 + p; with this swizzle those
-// 16-byte reads are free of LDS bank conflicts (measured with the LDS bank
-// conflict counter over candidate placements: plain r & 7 still costs 1.33
-// extra cycles per read).  Rows are 16-aligned in every read, so the pattern
-// only needs to be a bijection on each row.
+// p = l%16) read chunk g (then g + 4) of row r0 + p.  The 16 lanes of one
+// read pass share g, so they read one logical chunk c of rows r0..r0+15, at
+// bank offset 32 (p & 1) + 4 (c ^ swizzle(p)); the swizzle makes that a
+// bijection onto the 16 (parity, chunk) pairs, so the 16-byte reads are free
+// of LDS bank conflicts for any c (plain r & 7 measured 1.33 extra cycles per
+// read with the LDS bank conflict counter).  Rows are 16-aligned in every
+// read, so the pattern only needs to be a bijection on each row.
 __device__ __forceinline__ int chunk_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// MFMA operand of this lane: logical chunks 2g and 2g+1 (K bytes 32g..32g+31)
-// of tile row `row`.
+// MFMA operand of this lane: logical chunks g and g + 4 (K bytes 16g..16g+15
+// and 64+16g..64+16g+15) of tile row `row`.
 __device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
 {
     const uint8_t *rp = tile + row * 128;
     const int x = chunk_swizzle(row);
-    const v4i lo = *reinterpret_cast<const v4i *>(rp + (((2 * g) ^ x) << 4));
-    const v4i hi = *reinterpret_cast<const v4i *>(rp + (((2 * g + 1) ^ x) << 4));
+    const v4i lo = *reinterpret_cast<const v4i *>(rp + ((g ^ x) << 4));
+    const v4i hi = *reinterpret_cast<const v4i *>(rp + (((g + 4) ^ x) << 4));
     return cat(lo, hi);
 }
 
@@ -662,7 +733,9 @@ __device__ __forceinline__ v8i lds_w_fragment(const uint8_t *sW, int row, int g,
 //
 // LDS stage: A tile [BM][128] | W tile [BN][128] | scales [64 * waves] floats.
 // Scale slot s < BM holds a_scale of tile row s; slot BM + j holds w_scale of
-// the tile's j-th 128-row weight block.  Tiles are swizzled as described at
+// the tile's j-th weight-scale row (128 weight rows each; MX: 32, and the
+// block's MFMAs take the scale words instead of the FMAs, accumulating in
+// place).  Tiles are swizzled as described at
 // chunk_swizzle().
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
@@ -681,9 +754,10 @@ __device__ __forceinline__ void linear_tile(int L, int tiles_m, int tiles_n, int
     tn = in_group / gsize;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, bool MX>
 __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_store)
 {
+    select_batch(p);
     constexpr int NWAVES = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
@@ -691,7 +765,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     constexpr int STAGE = A_BYTES + W_BYTES + NWAVES * 256;
     constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB copies per wave per block
     constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
-    constexpr int NBW = (BN + 127) / 128;                                    // weight blocks a tile spans
+    constexpr int SH = wscale_shift<MX>();
+    constexpr int NBW = (BN + (1 << SH) - 1) >> SH;                          // weight-scale rows a tile spans
+    constexpr int WSN = MX ? TN : 1;                                         // weight-scale words per wave
     // Copy schedule.  Wave tiles of three or more slices spread a block's
     // copies, CPS per slice, over its first SPREAD slices; those copies run
     // before the block's barrier, so they can only refill the stage freed by
@@ -718,6 +794,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-row weight block");
     static_assert(BN <= 128 ? 128 % BN == 0 : BN % 128 == 0, "tiles start on weight-block boundaries");
+    static_assert(!MX || BN % 32 == 0, "MX: tiles start on 32-row weight-scale boundaries");
     static_assert(BM + NBW <= NWAVES * 64, "scale slots");
     static_assert(STAGES >= 2 && SPREAD >= 1 && SPREAD * CPS >= PER_BLOCK, "copy schedule");
     static_assert(LATE || STAGES > 2 || C_BEFORE == PER_BLOCK, "two stages: next block's copies precede the barrier");
@@ -741,9 +818,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         G *= 2;
     const int r16 = lane & 15, g = lane >> 4;
     const int lrow = lane >> 3, pch = lane & 7;
-    const int NB = (N + 127) >> 7;
+    const int NB = (N + (1 << SH) - 1) >> SH;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
-    const int ws_slot = BM + ((wn * WN) >> 7);   // tiles start on weight-block boundaries
+    // Scale slot of weight fragment u (block scale: one for the wave's columns;
+    // tiles start on weight-scale row boundaries).
+    int ws_slot[WSN];
+#pragma unroll
+    for (int u = 0; u < WSN; ++u)
+        ws_slot[u] = BM + ((wn * WN + 16 * u) >> SH);
     const int arow = wm * WM + r16, wrow = wn * WN + r16;
 
     // Copies.  Lane covers row (lane >> 3) of an 8-row group and physical
@@ -784,7 +866,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         // Lanes past the needed slots repeat the last needed address: one
         // cache line, not one per lane.
         c.s_src = slot < BM ? p.a_scale + (size_t)min(c.m0 + slot, M - 1) * KB
-                            : p.w_scale + (size_t)min((c.n0 >> 7) + min(slot - BM, NBW - 1), NB - 1) * KB;
+                            : p.w_scale + (size_t)min((c.n0 >> SH) + min(slot - BM, NBW - 1), NB - 1) * KB;
         return c;
     };
     // Descriptors of K block kb of a tile: the rows that exist, minus the
@@ -828,7 +910,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     wait_vmcnt<(AHEAD - 1) * PER_BLOCK>();
     __syncthreads();
     v8i wf[TN], af;
-    float sa[TM], ws;
+    float sa[TM], ws[WSN];
     {
         const uint8_t *sA = smem, *sW = smem + A_BYTES;
         const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
@@ -840,7 +922,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 #pragma unroll
         for (int t = 0; t < TM; ++t)
             sa[t] = sS[arow + 16 * t];
-        ws = sS[ws_slot];
+#pragma unroll
+        for (int u = 0; u < WSN; ++u)
+            ws[u] = sS[ws_slot[u]];
     }
 
     // Last slice of the previous block, scaled at the start of the next one
@@ -865,7 +949,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         float s_cur = 0.f;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const float sc_prev = t > 0 ? sa[t - 1] * ws : s_last;
+            const float sc_prev = t > 0 ? sa[t - 1] * ws[0] : s_last;
             if (t == TM - 1) {
                 wait_vmcnt<VM_AT_BARRIER>();   // this wave's copies of the next block have landed
                 __syncthreads();               // ... every wave's; this block's stage is read out
@@ -882,14 +966,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             // Raised wave priority while this slice's MFMAs issue: the matrix
             // core is fed first when both waves of a SIMD have work.
             __builtin_amdgcn_s_setprio(1);
+            if constexpr (MX) {
+                // MX: the block's scales go into the MFMA, which accumulates in place.
 #pragma unroll
-            for (int u = 0; u < TN; ++u)
-                dn[u] = mfma_block(wf[u], af);
+                for (int u = 0; u < TN; ++u)
+                    acc[t][u] = mfma_mx(wf[u], af, acc[t][u], ws[u], sa[t], g);
+            } else {
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    dn[u] = mfma_block(wf[u], af);
+            }
             if (t == TM - 1) {
                 // The next block: its stage is complete (barrier above).  Weight
                 // fragment u is read right after MFMA u has taken the old one.
                 // After the last block these read a stale stage, unused.
-                s_cur = sa[TM - 1] * ws;
+                s_cur = sa[TM - 1] * ws[0];
                 const uint8_t *nA = smem + ((step + 1) % STAGES) * STAGE, *nW = nA + A_BYTES;
                 const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
 #pragma unroll
@@ -899,14 +990,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 #pragma unroll
                 for (int s = 0; s < TM; ++s)
                     sa[s] = nS[arow + 16 * s];
-                ws = nS[ws_slot];
-            }
 #pragma unroll
-            for (int u = 0; u < TN; ++u) {
-                if (t > 0)
-                    acc[t - 1][u] = fma4(d[u], sc_prev, acc[t - 1][u]);
-                else
-                    acc[TM - 1][u] = fma4(d_last[u], sc_prev, acc[TM - 1][u]);
+                for (int u = 0; u < WSN; ++u)
+                    ws[u] = nS[ws_slot[u]];
+            }
+            if constexpr (!MX) {
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    if (t > 0)
+                        acc[t - 1][u] = fma4(d[u], sc_prev, acc[t - 1][u]);
+                    else
+                        acc[TM - 1][u] = fma4(d_last[u], sc_prev, acc[TM - 1][u]);
+                }
             }
             // Issue order: the next slice's activation fragment reads first
             // (most time to land), then each MFMA followed by a share of the
@@ -954,10 +1049,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             block(step, rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), c.s_src, ckb);
         }
 
-        // Tile done: fold in the last slice, round to bf16 and store.
+        // Tile done: fold in the last slice (block scale), round to bf16 and store.
+        if constexpr (!MX) {
 #pragma unroll
-        for (int u = 0; u < TN; ++u)
-            acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
+            for (int u = 0; u < TN; ++u)
+                acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
+        }
         const int n_base = cur.n0 + wn * WN + 4 * g;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
@@ -983,8 +1080,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 
 // Explicit instantiations (emit the host-side launch stubs).
 #define A8W8_PTILE_INST(BM, BN, WGM, WGN, S)                                                  \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false>(Args, int);             \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true>(Args, int);
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, false>(Args, int);      \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, false>(Args, int);       \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, true>(Args, int);       \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, true>(Args, int);
 A8W8_PTILE_INST(256, 256, 2, 4, 2)
 A8W8_PTILE_INST(256, 128, 2, 4, 3)
 A8W8_PTILE_INST(128, 256, 2, 4, 3)
@@ -1068,9 +1167,10 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 //
 // LDS stage: A tile [BM][128] | W tile [BN][128] | activation scales
 // [64 * waves] floats, tiles swizzled as described at chunk_swizzle().
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, bool MX>
 __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
 {
+    select_batch(p);
     constexpr int NWAVES = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
@@ -1118,8 +1218,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     // or past M repeat a valid row and are never read).
     const float *as_src = p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB;
     const int w_stride = PK ? 2048 : 128;   // bytes from one K block of a weight row to the next
-    const int NB = (N + 127) >> 7;
-    const_f32 *wsp = (const_f32 *)(p.w_scale + (size_t)min((n0 + wn * WN) >> 7, NB - 1) * KB);
+    // Weight scales through scalar loads: one row for the wave's columns
+    // (block scale), or the row of each 16-row fragment u (MX).
+    constexpr int SH = wscale_shift<MX>();
+    constexpr int WSN = MX ? TN : 1;
+    const int NB = (N + (1 << SH) - 1) >> SH;
+    const_f32 *wsp[WSN];
+#pragma unroll
+    for (int u = 0; u < WSN; ++u)
+        wsp[u] = (const_f32 *)(p.w_scale + (size_t)min((n0 + wn * WN + 16 * u) >> SH, NB - 1) * KB);
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -1133,24 +1240,48 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     for (int s = 0; s < STAGES - 1; ++s)
         issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
                                            W_BYTES, wave, w_stride);
-    float ws_next = wsp[0];
+    float ws_next[WSN];
+#pragma unroll
+    for (int u = 0; u < WSN; ++u)
+        ws_next[u] = wsp[u][0];
 
     for (int kb = 0; kb < KB; ++kb) {
-        const float ws = ws_next;
+        float ws[WSN];
+#pragma unroll
+        for (int u = 0; u < WSN; ++u)
+            ws[u] = ws_next[u];
         wait_vmcnt<(STAGES - 2) * PER_BLOCK>();   // this wave's copies of block kb have landed
         __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
         const int kn = min(kb + STAGES - 1, KB - 1);
         issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
                                            A_BYTES, W_BYTES, wave, w_stride);
-        ws_next = wsp[min(kb + 1, KB - 1)];
+#pragma unroll
+        for (int u = 0; u < WSN; ++u)
+            ws_next[u] = wsp[u][min(kb + 1, KB - 1)];
 
         const uint8_t *sA = smem + (kb % STAGES) * STAGE;
         const uint8_t *sW = sA + A_BYTES;
         const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
+        if constexpr (MX) {
+            // MX: scales inside the MFMA, accumulated in place.
+            v8i wf[TN];
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u + r16, g, lane);
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                const float sa = sS[wm * WM + 16 * t + r16];
+                const v8i af = lds_fragment(sA, wm * WM + 16 * t + r16, g);
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    acc[t][u] = mfma_mx(wf[u], af, acc[t][u], ws[u], sa, g);
+            }
+            continue;
+        }
         float sc[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t)
-            sc[t] = sS[wm * WM + 16 * t + r16] * ws;
+            sc[t] = sS[wm * WM + 16 * t + r16] * ws[0];
         v8i wf[TN];
 #pragma unroll
         for (int u = 0; u < TN; ++u)
@@ -1190,8 +1321,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 
 
 #define A8W8_TILE_INST(BM, BN, WGM, WGN, S)                                                   \
-    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false>(Args, int);              \
-    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true>(Args, int);
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, false>(Args, int);       \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, false>(Args, int);        \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, true>(Args, int);        \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, true>(Args, int);
 A8W8_TILE_INST(256, 256, 2, 4, 2)
 A8W8_TILE_INST(256, 128, 2, 4, 3)
 A8W8_TILE_INST(128, 256, 2, 4, 3)
@@ -1216,18 +1349,20 @@ using namespace kern;
 // ---------------------------------------------------------------------------
 // Instance table.
 
-// Each instance is compiled twice: for row-layout weights (fn) and for the
-// packed layout (fn_pk).
+// Each instance is compiled four times: fn[2 * mx + wpk], for fp32 block
+// scales (mx 0) or MX scales (mx 1), and row-layout (wpk 0) or packed (wpk 1)
+// weights.
 struct Entry {
     Variant v;
-    const void *fn;
-    const void *fn_pk;
+    const void *fn[4];
     int lds_bytes;
 };
 
-#define FN2(...) reinterpret_cast<const void *>(&__VA_ARGS__, false>), reinterpret_cast<const void *>(&__VA_ARGS__, true>)
+#define FN_ONE(PKV, MXV, ...) reinterpret_cast<const void *>(&__VA_ARGS__, PKV, MXV>)
+#define FN4(...) {FN_ONE(false, false, __VA_ARGS__), FN_ONE(true, false, __VA_ARGS__), \
+                  FN_ONE(false, true, __VA_ARGS__), FN_ONE(true, true, __VA_ARGS__)}
 #define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, "skinny_r" #TPW "_d" #D "_w" #NW}, \
-                            FN2(skinny_kernel<TPW, D, NW), 0}
+                            FN4(skinny_kernel<TPW, D, NW), 0}
 // Persistent tile grids are sized for WPC waves per CU: 8 (two per SIMD) for
 // the instances above 128 VGPRs, 16 for the small ones, or fewer workgroups
 // where their LDS does not fit.
@@ -1237,19 +1372,19 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 }
 #define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   FN2(tile_kernel<BM, BN, WGM, WGN, S), \
+                                   FN4(tile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 #define PTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_PTILE, BM, BN, WGM * WGN, S, 0, \
                                     tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
                                     "ptile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   FN2(ptile_kernel<BM, BN, WGM, WGN, S), \
+                                   FN4(ptile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
 #define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, \
                                "tall_r" #TPW "_n" #NT "_d" #D "_w" #NW}, \
-                              FN2(tall_kernel<TPW, NT, D, NW), 0}
+                              FN4(tall_kernel<TPW, NT, D, NW), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
-                           FN2(pskinny_kernel<D, NW, P), 0}
+                           FN4(pskinny_kernel<D, NW, P), 0}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
@@ -1309,7 +1444,7 @@ hipError_t set_kernel_attributes()
 {
     for (int i = 0; i < kNumEntries; ++i) {
         if (kEntries[i].lds_bytes > 0) {
-            for (const void *fn : {kEntries[i].fn, kEntries[i].fn_pk}) {
+            for (const void *fn : kEntries[i].fn) {
                 hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    kEntries[i].lds_bytes);
                 if (e != hipSuccess)
@@ -1320,15 +1455,16 @@ hipError_t set_kernel_attributes()
     return hipSuccess;
 }
 
-hipError_t launch_variant(int id, const Args &a, int cus, hipStream_t stream)
+hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t stream)
 {
     const Entry &e = kEntries[id];
     const int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
+    // 8-byte stores need every row (and, batched, every batch) 8-byte aligned.
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;
     void *params[] = {&args, &vec};
-    return hipLaunchKernel(a.wpk ? e.fn_pk : e.fn, dim3((unsigned)grid), dim3(e.v.waves * 64), params,
-                           (size_t)e.lds_bytes, stream);
+    return hipLaunchKernel(e.fn[2 * (a.mx ? 1 : 0) + (a.wpk ? 1 : 0)], dim3((unsigned)grid, (unsigned)batch),
+                           dim3(e.v.waves * 64), params, (size_t)e.lds_bytes, stream);
 }
 
 }  // namespace a8w8

@@ -4,11 +4,12 @@
 // Packed layout: rows padded with zeros to N' = 16 * ceil(N / 16); for every
 // 16-row tile t and 128-wide K block kb, 2048 bytes at offset
 // (t * K/128 + kb) * 2048, ordered [h][lane][16 bytes] with lane l (0..63)
-// holding row 16 t + l % 16, bytes 32 (l / 16) + 16 h .. + 16 of the block.
-// That is the operand layout of v_mfma_f32_16x16x128_f8f6f4 (lane l: row
-// l % 16, 32 bytes at 32 (l / 16)), split into two contiguous kilobytes, so a
-// wave loads a whole fragment with two contiguous 16-byte-per-lane loads and
-// no lane exchange -- the "pre-shuffled weights" idea, laid out for this MFMA.
+// holding row 16 t + l % 16, bytes 16 (l / 16) + 64 h .. + 16 of the block.
+// That is the operand layout of v_mfma_f32_16x16x128_f8f6f4 in the
+// instruction's own K order (lane l: row l % 16, 16-byte K chunks l / 16 and
+// l / 16 + 4), split into two contiguous kilobytes, so a wave loads a whole
+// fragment with two contiguous 16-byte-per-lane loads and no lane exchange --
+// the "pre-shuffled weights" idea, laid out for this MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *W, uint8_t 
         const int64_t tile = blk / KB;
         const int kb = (int)(blk - tile * KB);
         const int64_t row = tile * 16 + (lane & 15);
-        const int col = kb * 128 + 32 * (lane >> 4) + 16 * h;
+        const int col = kb * 128 + 16 * (lane >> 4) + 64 * h;
         u32x4p v = {0u, 0u, 0u, 0u};
         if (row < N)
             v = *reinterpret_cast<const u32x4p *>(W + row * K + col);

@@ -48,7 +48,7 @@ extern "C" {
 enum {
     A8W8_OK = 0,
     A8W8_ERR_NULL = 1,    /* a required pointer is NULL                          */
-    A8W8_ERR_SHAPE = 2,   /* M < 0, N < 1, K < 1, K % 128 != 0, M or N > 2^30, K > 2^22 */
+    A8W8_ERR_SHAPE = 2,   /* M < 0, N < 1, K < 1, K % 128 != 0, M or N > 2^30, K > 2^22, batch out of [0, 65535] */
     A8W8_ERR_ALIGN = 3,   /* A or W not 16-byte aligned, a scale or Y not 4-byte aligned */
     A8W8_ERR_ARCH = 4,    /* the current device is not gfx950                    */
     A8W8_ERR_HIP = 5,     /* a HIP runtime call or kernel launch failed          */
@@ -122,7 +122,7 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant,
  * W [N, K] row-major -> Wp of 16 * ceil(N/16) * K bytes.  For every 16-row
  * tile t and 128-wide K block kb, the 2048 bytes at (t * K/128 + kb) * 2048
  * hold, in order h = 0, 1 and lane l = 0..63, the 16 bytes of row 16 t + l%16
- * at columns 128 kb + 32 (l/16) + 16 h .. + 16; rows past N are zero.  Every
+ * at columns 128 kb + 16 (l/16) + 64 h .. + 16; rows past N are zero.  Every
  * kernel then reads a weight fragment as two contiguous 1 KB loads.
  *
  * a8w8_prepack_weights enqueues the conversion (W and Wp device memory,
@@ -141,6 +141,57 @@ int gemm_a8w8_blockscale_packed_run_variant(int32_t variant,
                                             const void *Wp, const float *w_scale,
                                             void *Y, int64_t M, int64_t N, int64_t K,
                                             void *stream);
+
+/*
+ * MX-scaled variant: the mxfp8 GEMM with "32x32" weight-scale blocks (dense,
+ * and batched with b = 8, N = 1024, K = 4096) that the gfx1250 BF16 and MX32
+ * tuned-rows page (ROCm/aiter #7247, Motivation and Technical Details) tunes.
+ * That page gives the block shape and the element type only; the scales are
+ * read as OCP Microscaling (MX) scales, one E8M0 byte each (value
+ * 2^(e - 127); 0xFF is NaN):
+ *
+ *   Y[m,n] = bf16( sum_k e4m3(A[m,k]) * 2^(a_scale[m, k/32] - 127)
+ *                        * e4m3(W[n,k]) * 2^(w_scale[n/32, k/32] - 127) )
+ *
+ * fp32 accumulation (the scaled MFMA applies the powers of two exactly),
+ * one round-to-nearest-even to bf16.  Same kernels, selection (a heuristic
+ * plan: no tuned table is registered for this variant, so plans report
+ * fallback = 1), threading and error rules as gemm_a8w8_blockscale; K % 128
+ * == 0 (whole 128-wide K blocks), and ceil(N/32) * K/128 * 4 < 2^31.
+ *
+ * Buffers (device memory, row-major, caller-owned):
+ *   A        uint8 e4m3fn [batch, M, K]              16-byte aligned
+ *   a_scale  uint8 E8M0   [batch, M, K/32]            4-byte aligned
+ *   W        uint8 e4m3fn [batch, N, K]              16-byte aligned
+ *            (packed entries: batch consecutive a8w8_prepack_weights images
+ *            of 16 * ceil(N/16) * K bytes each)
+ *   w_scale  uint8 E8M0   [batch, ceil(N/32), K/32]   4-byte aligned
+ *   Y        bf16 [batch, M, N]                       2-byte aligned; overwritten
+ * The unbatched entries take batch = 1.  batch == 0 or M == 0 is a no-op;
+ * batch <= 65535.  Batches are independent problems of one shape.
+ */
+int gemm_a8w8_mxscale(const void *A, const void *a_scale,
+                      const void *W, const void *w_scale,
+                      void *Y, int64_t M, int64_t N, int64_t K, void *stream);
+int gemm_a8w8_mxscale_packed(const void *A, const void *a_scale,
+                             const void *Wp, const void *w_scale,
+                             void *Y, int64_t M, int64_t N, int64_t K, void *stream);
+int batched_gemm_a8w8_mxscale(const void *A, const void *a_scale,
+                              const void *W, const void *w_scale, void *Y,
+                              int64_t batch, int64_t M, int64_t N, int64_t K, void *stream);
+int batched_gemm_a8w8_mxscale_packed(const void *A, const void *a_scale,
+                                     const void *Wp, const void *w_scale, void *Y,
+                                     int64_t batch, int64_t M, int64_t N, int64_t K,
+                                     void *stream);
+/* The plan the MX entries launch for (M, N, K) (per batch; host only). */
+int gemm_a8w8_mxscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out);
+/* Run a specific instance on MX operands (for tuning and tests); w_packed
+   selects the packed weight layout.  Returns A8W8_ERR_PLAN as
+   gemm_a8w8_blockscale_run_variant does. */
+int gemm_a8w8_mxscale_run_variant(int32_t variant, const void *A, const void *a_scale,
+                                  const void *W, const void *w_scale, void *Y,
+                                  int64_t batch, int64_t M, int64_t N, int64_t K,
+                                  int32_t w_packed, void *stream);
 
 /* Static name of a compiled instance, e.g. "tile_256x128" (NULL if out of range). */
 const char *gemm_a8w8_variant_name(int32_t variant);

@@ -24,7 +24,7 @@ REGISTERED = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:gemm_)?a8w8_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:batched_)?(?:gemm_)?a8w8_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -191,3 +191,60 @@ def test_unregistered_shape_falls_back_not_fails():
         p = g.gemm_a8w8_blockscale_plan(m, n, 384)
         assert p["fallback"] == 1 and p["kernel_name"] == "tall" and n <= p["bn"], (n, m, p)
         assert p["grid"] == (m + p["bm"] - 1) // p["bm"]
+
+
+# ---------------------------------------------------------------- MX-scaled entries
+
+def _mx(name="gemm_a8w8_mxscale", A=16, a_s=16, W=16, w_s=16, Y=16, batch=None, M=4, N=512, K=1024):
+    f = getattr(g.lib(), name)
+    if batch is None:
+        return f(A, a_s, W, w_s, Y, M, N, K, None)
+    return f(A, a_s, W, w_s, Y, batch, M, N, K, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_a8w8_mxscale", "gemm_a8w8_mxscale_packed"])
+def test_mx_entries_check_arguments(name):
+    assert _mx(name, K=96) == g.A8W8_ERR_SHAPE                   # whole 128-wide K blocks only
+    assert _mx(name, M=-1) == g.A8W8_ERR_SHAPE
+    assert _mx(name, N=0) == g.A8W8_ERR_SHAPE
+    assert _mx(name, A=None) == g.A8W8_ERR_NULL
+    assert _mx(name, w_s=None) == g.A8W8_ERR_NULL
+    assert _mx(name, W=24) == g.A8W8_ERR_ALIGN
+    assert _mx(name, a_s=18) == g.A8W8_ERR_ALIGN
+    assert _mx(name, M=0, A=None, W=None) == g.A8W8_OK
+
+
+@pytest.mark.parametrize("name", ["batched_gemm_a8w8_mxscale", "batched_gemm_a8w8_mxscale_packed"])
+def test_mx_batched_entries_check_arguments(name):
+    assert _mx(name, batch=-1) == g.A8W8_ERR_SHAPE
+    assert _mx(name, batch=65536) == g.A8W8_ERR_SHAPE
+    assert _mx(name, batch=0, A=None, W=None) == g.A8W8_OK     # empty batch: no-op
+    assert _mx(name, batch=8, M=0, A=None) == g.A8W8_OK
+    assert _mx(name, batch=8, K=200) == g.A8W8_ERR_SHAPE
+    assert _mx(name, batch=8, Y=None) == g.A8W8_ERR_NULL
+
+
+def test_mx_weight_scale_rows_limit():
+    # ceil(N/32) * K/128 * 4 must stay below 2^31 (32-bit scale descriptors).
+    assert _mx(N=1 << 30, K=1 << 14) == g.A8W8_ERR_SHAPE
+    assert g.lib().gemm_a8w8_mxscale_plan(16, 1 << 30, 1 << 14, 0, ctypes.byref(g.Plan())) == g.A8W8_ERR_SHAPE
+
+
+def test_mx_run_variant_rejects_like_block_scale():
+    skinny = next(i for i in range(g.gemm_a8w8_num_variants())
+                  if g.gemm_a8w8_describe_variant(i)["kernel_name"] == "skinny")
+    rc = g.lib().gemm_a8w8_mxscale_run_variant(skinny, 16, 16, 16, 16, 16, 1, 17, 512, 1024, 0, None)
+    assert rc == g.A8W8_ERR_PLAN
+    assert g.lib().gemm_a8w8_mxscale_run_variant(-1, 16, 16, 16, 16, 16, 1, 4, 512, 1024, 0, None) == g.A8W8_ERR_PLAN
+
+
+@pytest.mark.parametrize("M,N,K", [(48, 1792, 5120), (768, 5120, 8192), (768, 32768, 1280), (16, 1024, 4096),
+                                   (1, 4608, 5120), (3000, 5120, 2304), (100, 20, 4096)])
+def test_mx_plan_is_a_valid_heuristic_plan(M, N, K):
+    p = g.gemm_a8w8_mxscale_plan(M, N, K)
+    assert p["fallback"] == 1 and p["key_m"] == M
+    assert 0 <= p["variant"] < g.gemm_a8w8_num_variants()
+    if p["kernel_name"] in ("skinny", "pskinny"):
+        assert M <= 16
+    if p["kernel_name"] == "tall":
+        assert N <= p["bn"]

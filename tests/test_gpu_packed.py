@@ -23,15 +23,15 @@ pytestmark = pytest.mark.gpu
 
 def _pack_reference(W: np.ndarray) -> np.ndarray:
     """The packed layout from its definition: per 16-row tile t and K block kb, [h][lane][16 bytes],
-    lane l holding row 16t + l%16, columns 128kb + 32(l/16) + 16h .. +16; rows past N zero."""
+    lane l holding row 16t + l%16, columns 128kb + 16(l/16) + 64h .. +16; rows past N zero."""
     N, K = W.shape
     Np = (N + 15) // 16 * 16
     Wz = np.zeros((Np, K), np.uint8)
     Wz[:N] = W
     T, KB = Np // 16, K // 128
-    # Wz[16t + r, 128kb + 32g + 16h + b] -> packed[t, kb, h, 16g + r, b]
-    v = Wz.reshape(T, 16, KB, 4, 2, 16)                  # t, r, kb, g, h, b
-    return np.ascontiguousarray(v.transpose(0, 2, 4, 3, 1, 5)).reshape(Np, K)
+    # Wz[16t + r, 128kb + 64h + 16g + b] -> packed[t, kb, h, 16g + r, b]
+    v = Wz.reshape(T, 16, KB, 2, 4, 16)                  # t, r, kb, h, g, b
+    return np.ascontiguousarray(v.transpose(0, 2, 3, 4, 1, 5)).reshape(Np, K)
 
 
 @pytest.mark.parametrize("N,K", [(16, 128), (300, 640), (5, 256), (14336, 5120)])
