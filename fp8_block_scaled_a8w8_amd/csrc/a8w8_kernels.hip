@@ -669,38 +669,54 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // LDS tiles are row-major 128-byte rows whose 16-byte chunk c sits at chunk
 // position c ^ chunk_swizzle(row).  A fragment read has lane (g = l/16,
-// p = l%16) read chunk g (then g + 4) of row r0 + p.  The 16 lanes of one
-// read pass share g, so they read one logical chunk c of rows r0..r0+15, at
-// bank offset 32 (p & 1) + 4 (c ^ swizzle(p)); the swizzle makes that a
-// bijection onto the 16 (parity, chunk) pairs, so the 16-byte reads are free
-// of LDS bank conflicts for any c (plain r & 7 measured 1.33 extra cycles per
-// read with the LDS bank conflict counter).  Rows are 16-aligned in every
-// read, so the pattern only needs to be a bijection on each row.
-__device__ __forceinline__ int chunk_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// MFMA operand of this lane: logical chunks g and g + 4 (K bytes 16g..16g+15
-// and 64+16g..64+16g+15) of tile row `row`.
-__device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row, int g)
+// p = l%16) read chunk g (then g + 4) of row r0 + p.  The swizzle XORs the
+// chunk index with a linear function of the row's low four bits (bits 0, 1,
+// 2, 3 contribute 4, 1, 2, 4): the three low bits rotated, then bit 3 into
+// the top.  It was chosen offline as one that leaves these reads free of
+// bank conflicts under every lane-to-pass grouping and bank count (32, 64,
+// 128 four-byte banks) for which the earlier chunk order (2g, 2g+1 with
+// swizzle (r & 7) ^ (r >> 3 & 1)) measured zero conflicts; the LDS bank
+// conflict counter confirms zero for it on gfx950.  Rows are 16-aligned in
+// every read, so the pattern only needs to be a bijection on each row.
+__device__ __forceinline__ int chunk_swizzle(int row)
 {
-    const uint8_t *rp = tile + row * 128;
-    const int x = chunk_swizzle(row);
-    const v4i lo = *reinterpret_cast<const v4i *>(rp + ((g ^ x) << 4));
-    const v4i hi = *reinterpret_cast<const v4i *>(rp + (((g + 4) ^ x) << 4));
+    return (((row & 1) << 2) | ((row >> 1) & 3)) ^ ((row >> 1) & 4);
+}
+
+// Byte offsets, from the first row of a 16-row group, of this lane's two
+// fragment chunks: row l%16, logical chunks g and g + 4 (K bytes 16g..16g+15
+// and 64+16g..64+16g+15).  Computed once per lane, so every read adds only
+// its 16-aligned row base (an immediate offset).
+struct FragOff {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ FragOff frag_offsets(int lane)
+{
+    const int r = lane & 15, g = lane >> 4, x = chunk_swizzle(r);
+    return {(uint32_t)(r * 128 + ((g ^ x) << 4)), (uint32_t)(r * 128 + (((g + 4) ^ x) << 4))};
+}
+
+// MFMA operand of this lane from the 16-row group starting at tile row row0.
+__device__ __forceinline__ v8i lds_fragment(const uint8_t *tile, int row0, FragOff f)
+{
+    const uint8_t *rp = tile + row0 * 128;
+    const v4i lo = *reinterpret_cast<const v4i *>(rp + f.lo);
+    const v4i hi = *reinterpret_cast<const v4i *>(rp + f.hi);
     return cat(lo, hi);
 }
 
 // Weight stages hold either row-layout rows (as above) or, for packed weights,
 // each 16-row tile's 2 KB exactly as stored in memory (operand order): the
 // copies then move whole contiguous kilobytes, and lane l reads bytes 16 l of
-// each half of the tile that holds `row` (its first row plus l % 16).
+// each half of the tile that starts at row0.
 template <bool PK>
-__device__ __forceinline__ v8i lds_w_fragment(const uint8_t *sW, int row, int g, int lane)
+__device__ __forceinline__ v8i lds_w_fragment(const uint8_t *sW, int row0, FragOff f, int lane)
 {
     if constexpr (PK) {
-        const uint8_t *tp = sW + (row >> 4) * 2048 + lane * 16;
+        const uint8_t *tp = sW + (row0 >> 4) * 2048 + lane * 16;
         return cat(*reinterpret_cast<const v4i *>(tp), *reinterpret_cast<const v4i *>(tp + 1024));
     } else {
-        return lds_fragment(sW, row, g);
+        return lds_fragment(sW, row0, f);
     }
 }
 
@@ -826,7 +842,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 #pragma unroll
     for (int u = 0; u < WSN; ++u)
         ws_slot[u] = BM + ((wn * WN + 16 * u) >> SH);
-    const int arow = wm * WM + r16, wrow = wn * WN + r16;
+    const int arow = wm * WM + r16;             // this lane's activation row (scale slots)
+    const int arow0 = wm * WM, wrow0 = wn * WN;  // 16-aligned fragment rows
+    const FragOff fo = frag_offsets(lane);
 
     // Copies.  Lane covers row (lane >> 3) of an 8-row group and physical
     // chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row);
@@ -914,11 +932,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     {
         const uint8_t *sA = smem, *sW = smem + A_BYTES;
         const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
-        wf[0] = lds_w_fragment<PK>(sW, wrow, g, lane);
-        af = lds_fragment(sA, arow, g);
+        wf[0] = lds_w_fragment<PK>(sW, wrow0, fo, lane);
+        af = lds_fragment(sA, arow0, fo);
 #pragma unroll
         for (int u = 1; u < TN; ++u)
-            wf[u] = lds_w_fragment<PK>(sW, wrow + 16 * u, g, lane);
+            wf[u] = lds_w_fragment<PK>(sW, wrow0 + 16 * u, fo, lane);
 #pragma unroll
         for (int t = 0; t < TM; ++t)
             sa[t] = sS[arow + 16 * t];
@@ -961,7 +979,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             }
             v8i af_next = af;
             if (t + 1 < TM)
-                af_next = lds_fragment(sA, arow + 16 * (t + 1), g);
+                af_next = lds_fragment(sA, arow0 + 16 * (t + 1), fo);
             v4f dn[TN];
             // Raised wave priority while this slice's MFMAs issue: the matrix
             // core is fed first when both waves of a SIMD have work.
@@ -985,8 +1003,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
                 const float *nS = reinterpret_cast<const float *>(nW + W_BYTES);
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    wf[u] = lds_w_fragment<PK>(nW, wrow + 16 * u, g, lane);
-                af_next = lds_fragment(nA, arow, g);
+                    wf[u] = lds_w_fragment<PK>(nW, wrow0 + 16 * u, fo, lane);
+                af_next = lds_fragment(nA, arow0, fo);
 #pragma unroll
                 for (int s = 0; s < TM; ++s)
                     sa[s] = nS[arow + 16 * s];
@@ -1194,6 +1212,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     tile_coords((int)blockIdx.x, tiles_m, tiles_n, BM >= 256 ? 2 : 4, tmi, tni);
     const int m0 = tmi * BM, n0 = tni * BN;
     const int r16 = lane & 15, g = lane >> 4;
+    const FragOff fo = frag_offsets(lane);
 
     // Direct-load sources: lane covers row (lane >> 3) of an 8-row group and
     // physical chunk (lane & 7), which holds logical chunk (lane & 7) ^ swizzle(row).
@@ -1267,11 +1286,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
             v8i wf[TN];
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u + r16, g, lane);
+                wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u, fo, lane);
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 const float sa = sS[wm * WM + 16 * t + r16];
-                const v8i af = lds_fragment(sA, wm * WM + 16 * t + r16, g);
+                const v8i af = lds_fragment(sA, wm * WM + 16 * t, fo);
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
                     acc[t][u] = mfma_mx(wf[u], af, acc[t][u], ws[u], sa, g);
@@ -1285,10 +1304,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         v8i wf[TN];
 #pragma unroll
         for (int u = 0; u < TN; ++u)
-            wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u + r16, g, lane);
+            wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u, fo, lane);
         v4f d[2][TN];
         {
-            const v8i af = lds_fragment(sA, wm * WM + r16, g);
+            const v8i af = lds_fragment(sA, wm * WM, fo);
 #pragma unroll
             for (int u = 0; u < TN; ++u)
                 d[0][u] = mfma_block(wf[u], af);
@@ -1296,7 +1315,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             if (t + 1 < TM) {
-                const v8i af = lds_fragment(sA, wm * WM + 16 * (t + 1) + r16, g);
+                const v8i af = lds_fragment(sA, wm * WM + 16 * (t + 1), fo);
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
                     d[(t + 1) & 1][u] = mfma_block(wf[u], af);
