@@ -16,6 +16,10 @@ oracle's own time on the host cores.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--decode-nk N:K] [--decode-ms 1,2,...]   (other decode shapes, e.g. 34816:5120)
        [--workload sweep]                         (the dense-M sweep report)
+       [--no-mx]                                  (skip the MX-scaled points)
+
+The line also reports the MX-scaled variant (E8M0 scales per 1x32 activation
+group and 32x32 weight block) at its page's tuned points, cold weights.
 """
 from __future__ import annotations
 
@@ -156,6 +160,63 @@ def quantize_block(torch, g, inputgen, oracle, dev, replays):
     return out
 
 
+# MX-scaled points: the page's tuned (b, M, N, K) microbenchmark points (gfx1250 BF16 and MX32
+# tuned-rows page, ROCm/aiter #7247, Technical Details), plus its two other dense shapes at M = 768.
+MX_POINTS = [(1, 48, 1792, 5120), (1, 768, 5120, 8192), (1, 768, 32768, 1280), (8, 16, 1024, 4096),
+             (1, 768, 4608, 5120), (1, 768, 5120, 2304)]
+
+
+def mx_bytes(b: int, M: int, N: int, K: int) -> int:
+    """Algorithmic bytes of the MX GEMM: W, w_scale (E8M0 per 32x32), A, a_scale (E8M0 per 1x32), Y."""
+    return b * (N * K + ((N + 31) // 32) * (K // 32) + M * K + M * (K // 32) + 2 * M * N)
+
+
+def mx_block(torch, g, inputgen, oracle, dev, replays):
+    """MX-scaled GEMM at the page's points: parity gate against the oracle on sampled rows (every
+    batch), then cold-weight timing (weights rotated over >= 1 GiB of sign-flipped copies)."""
+    out = {}
+    for b, M, N, K in MX_POINTS:
+        pa = [inputgen.make_mx_activations(M, K, seed=70 + i) for i in range(b)]
+        pw = [inputgen.make_mx_weights(N, K, seed=80 + i) for i in range(b)]
+        stack = (lambda xs: np.stack(xs)) if b > 1 else (lambda xs: xs[0])
+        A, a_s = stack([x[0] for x in pa]), stack([x[1] for x in pa])
+        W0, w_s = stack([x[0] for x in pw]), stack([x[1] for x in pw])
+        dA, da, dw = (torch.from_numpy(x).to(dev) for x in (A, a_s, w_s))
+        R = max(2, math.ceil(ROTATE_BYTES / 2 / (W0.nbytes + w_s.nbytes)))
+        copies = [torch.from_numpy(W0).to(dev)] + \
+            [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
+        fn = g.batched_gemm_a8w8_mxscale if b > 1 else g.gemm_a8w8_mxscale
+        y = fn(dA, da, copies[-1], dw)
+        torch.cuda.synchronize()
+        W_last = inputgen.sign_flip_copy(W0, seed=1000 + R - 1)
+        rows = sorted({0, M // 2, M - 1})
+        worst = 0.0
+        for i in range(b):
+            sl = (lambda x: x[i]) if b > 1 else (lambda x: x)
+            ref = oracle.gemm_mx(sl(A), sl(a_s), sl(W_last), sl(w_s), rows=rows)
+            yh = sl(y)[rows].float().cpu().numpy().astype(np.float64)
+            rel = float(np.linalg.norm(yh - ref) / np.linalg.norm(ref))
+            if rel > 3e-3 or not np.all(np.isfinite(yh)):
+                raise SystemExit(f"parity gate failed (MX b={b} M={M} N={N} K={K}): rel_l2={rel:.3e}")
+            worst = max(worst, rel)
+        yo = torch.empty_like(y)
+        gr = time_graph(torch, [(lambda r=r: fn(dA, da, copies[r], dw, out=yo)) for r in range(R)], 0, 2)
+        us = timed_replays(torch, gr, replays) * 1000.0 / R
+        t_hbm = mx_bytes(b, M, N, K) / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_mfma = b * flops(M, N, K) / (FP8_PEAK_TFLOPS * 1e12) * 1e6
+        plan = g.gemm_a8w8_mxscale_plan(M, N, K)
+        out[f"b{b}_M{M}_N{N}_K{K}"] = {
+            "us_per_call": round(us, 3), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "frac": round(max(t_hbm, t_mfma) / us, 4),
+            "GB_s": round(mx_bytes(b, M, N, K) / (us * 1e-6) / 1e9, 1),
+            "TFLOP_s": round(b * flops(M, N, K) / (us * 1e-6) / 1e12, 1),
+            "plan": plan["name"], "tuned": plan["fallback"] == 0, "weight_copies": R,
+            "parity_rel_l2": round(worst, 6)}
+        del gr, copies
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +231,7 @@ def main():
     ap.add_argument("--decode-nk", default="14336:5120",
                     help="N:K of the decode workload (default: the qkv shape 14336:5120)")
     ap.add_argument("--decode-ms", default="1,2,4,8,16", help="M values the decode workload cycles through")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MX-scaled points")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the run, copy 256 MiB device-to-device three times (traffic calibration)")
     args = ap.parse_args()
@@ -320,6 +382,10 @@ def main():
     quant = quantize_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
     log("quantize:", json.dumps(quant))
 
+    # ------------------------------------------------------------ MX-scaled variant
+    mx = {} if args.no_mx else mx_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
+    log("mx:", json.dumps(mx))
+
     # ------------------------------------------------------------ CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -363,6 +429,7 @@ def main():
         "prepacked_weights": packed,
         "prefill": prefill,
         "quantize": quant,
+        "mx": mx,
         "parity": {"worst_rel_l2": round(gate, 6)},
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": cpu,

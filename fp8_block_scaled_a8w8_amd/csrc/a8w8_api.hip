@@ -184,12 +184,12 @@ struct Choice {
     int fallback;
 };
 
-Choice select_variant(int64_t M, int64_t N, int64_t K, int cus)
+Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx)
 {
     using namespace a8w8_table;
     for (int t = 0; t < kNumShapes; ++t) {
         const ShapeTable &s = kShapes[t];
-        if (s.n != N || s.k != K)
+        if (s.n != N || s.k != K || s.mx != mx)
             continue;
         // smallest key >= M (binary search over the ascending keys)
         int lo = 0, hi = s.count;
@@ -318,7 +318,7 @@ int gemm_impl(const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    const Choice c = o.mx ? Choice{heuristic_variant(M, N, K, cus), M, 1} : select_variant(M, N, K, cus);
+    const Choice c = select_variant(M, N, K, cus, o.mx);
     log_plan(M, N, K, c.variant, c.key_m, c.fallback);
     return launch(c.variant, o, M, N, K, cus, stream);
 }
@@ -399,7 +399,8 @@ int gemm_a8w8_mxscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8
     if (rc != A8W8_OK)
         return rc;
     const int cus = cu_count > 0 ? cu_count : 256;
-    fill_plan(heuristic_variant(M > 0 ? M : 1, N, K, cus), M, N, K, cus, M, 1, out);
+    const Choice c = select_variant(M > 0 ? M : 1, N, K, cus, 1);
+    fill_plan(c.variant, M, N, K, cus, c.key_m, c.fallback, out);
     return A8W8_OK;
 }
 
@@ -411,7 +412,7 @@ int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count,
     if (rc != A8W8_OK)
         return rc;
     const int cus = cu_count > 0 ? cu_count : 256;
-    const Choice c = select_variant(M > 0 ? M : 1, N, K, cus);
+    const Choice c = select_variant(M > 0 ? M : 1, N, K, cus, 0);
     fill_plan(c.variant, M, N, K, cus, c.key_m, c.fallback, out);
     return A8W8_OK;
 }

@@ -17,7 +17,12 @@ Results are appended to tune_results.jsonl as they are measured (an
 interrupted run resumes), and the table is written to tuned_table.json;
 regenerate the header with gen_selector_table.py and rebuild afterwards.
 
-Usage: python -m fp8_block_scaled_a8w8_amd.tune [--shapes N:K,...] [--rounds 3]
+With --mx the MX-scaled variant is tuned instead (E8M0 scales, seeded MX
+operands; --batch b times the batched form with b problems per call), and
+the shapes are stored with "mx": true -- by default the page's MX shapes,
+the dense (N, K) pairs and the batched b = 8, N = 1024, K = 4096 one.
+
+Usage: python -m fp8_block_scaled_a8w8_amd.tune [--shapes N:K,...] [--rounds 3] [--mx [--batch b]]
 """
 from __future__ import annotations
 
@@ -31,12 +36,15 @@ import time
 
 import torch
 
-from . import gemm_a8w8_blockscale_run_variant, variants
+from . import gemm_a8w8_blockscale_run_variant, gemm_a8w8_mxscale_run_variant, variants
 from . import gen_selector_table as gst
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 RESULTS = os.path.join(HERE, "tune_results.jsonl")
 REGISTERED = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6144), (32, 6144), (512, 1024)]
+# MX-scaled shapes of the gfx1250 BF16 and MX32 tuned-rows page (ROCm/aiter #7247,
+# Technical Details): dense (N, K) pairs, and the batched one as N:K:batch.
+REGISTERED_MX = ["1792:5120", "4608:5120", "5120:2304", "5120:8192", "32768:1280", "1024:4096:8"]
 
 
 def key_grid(limit: int = 8192) -> list[int]:
@@ -101,29 +109,57 @@ def time_graph(g, reps: int) -> float:
     return t0.elapsed_time(t1) / reps
 
 
-def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log) -> list[dict]:
+def _operands(N: int, K: int, mx: bool, batch: int):
+    """Seeded operands on the device: activations for M up to 8192, one weight copy, scales."""
     import inputgen
     dev = "cuda:0"
-    A, a_s = inputgen.make_activations(8192, K, seed=0)
-    W0, w_s = inputgen.make_weights(N, K, seed=1)
-    dA = torch.from_numpy(A).to(dev)
-    da = torch.from_numpy(a_s).to(dev)
-    dw = torch.from_numpy(w_s).to(dev)
-    R = max(2, math.ceil(rotate_gib * 2**30 / (W0.nbytes + w_s.nbytes)))
+    if not mx:
+        A, a_s = inputgen.make_activations(8192, K, seed=0)
+        W0, w_s = inputgen.make_weights(N, K, seed=1)
+        return [torch.from_numpy(x).to(dev) for x in (A, a_s)], W0, torch.from_numpy(w_s).to(dev)
+    parts_a = [inputgen.make_mx_activations(8192, K, seed=10 * i) for i in range(batch)]
+    parts_w = [inputgen.make_mx_weights(N, K, seed=10 * i + 1) for i in range(batch)]
+    import numpy as np
+    A = np.stack([p[0] for p in parts_a]) if batch > 1 else parts_a[0][0]
+    a_s = np.stack([p[1] for p in parts_a]) if batch > 1 else parts_a[0][1]
+    W0 = np.stack([p[0] for p in parts_w]) if batch > 1 else parts_w[0][0]
+    w_s = np.stack([p[1] for p in parts_w]) if batch > 1 else parts_w[0][1]
+    return [torch.from_numpy(x).to(dev) for x in (A, a_s)], W0, torch.from_numpy(w_s).to(dev)
+
+
+def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
+               mx: bool = False, batch: int = 1, results_path: str = RESULTS) -> list[dict]:
+    import inputgen
+    dev = "cuda:0"
+    prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
+    if all(f"{prefix}{N}:{K}:{M}" in done for M in key_grid()):
+        return [done[f"{prefix}{N}:{K}:{M}"] for M in key_grid()]      # all measured: no GPU needed
+    (dA, da), W0, dw = _operands(N, K, mx, batch)
+    R = max(2, math.ceil(rotate_gib * 2**30 / (W0.nbytes + dw.numel() * dw.element_size())))
     copies = [torch.from_numpy(W0).to(dev)] + \
         [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
     rows = []
     for M in key_grid():
-        key = f"{N}:{K}:{M}"
+        key = f"{prefix}{N}:{K}:{M}"
         if key in done:
             rows.append(done[key])
             continue
         cands = candidates(M, N, K)
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if mx:
+            lead = (batch,) if batch > 1 else ()
+            Am = (dA[:, :M] if batch > 1 else dA[:M]).contiguous()
+            am = (da[:, :M] if batch > 1 else da[:M]).contiguous()
+            out = torch.empty(lead + (M, N), dtype=torch.bfloat16, device=dev)
+        else:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         graphs = {}
         for v in cands:
-            calls = [(lambda r=r, vid=v["variant"]: gemm_a8w8_blockscale_run_variant(
-                vid, dA[:M], da[:M], copies[r], dw, out=out)) for r in range(R)]
+            if mx:
+                calls = [(lambda r=r, vid=v["variant"]: gemm_a8w8_mxscale_run_variant(
+                    vid, Am, am, copies[r], dw, out=out)) for r in range(R)]
+            else:
+                calls = [(lambda r=r, vid=v["variant"]: gemm_a8w8_blockscale_run_variant(
+                    vid, dA[:M], da[:M], copies[r], dw, out=out)) for r in range(R)]
             graphs[v["variant"]] = graph_for(calls)
         # replays per measurement: about 4 ms of work, at least 2
         probe = time_graph(graphs[cands[0]["variant"]], 1)
@@ -140,9 +176,9 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log) 
                "candidates": {v["name"]: round(med[v["variant"]], 3) for v in cands}}
         rows.append(row)
         done[key] = row
-        with open(RESULTS, "a") as f:
+        with open(results_path, "a") as f:
             f.write(json.dumps({"key": key, "row": row}) + "\n")
-        log(f"N={N} K={K} M={M:5d}: {best['name']:24s} {row['us']:9.2f} us  ({len(cands)} candidates)")
+        log(f"{prefix}N={N} K={K} M={M:5d}: {best['name']:24s} {row['us']:9.2f} us  ({len(cands)} candidates)")
         del graphs, out
     del copies
     torch.cuda.empty_cache()
@@ -151,10 +187,12 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log) 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--shapes", default=",".join(f"{n}:{k}" for n, k in REGISTERED))
+    ap.add_argument("--shapes", default=None, help="N:K[,N:K...] (MX: N:K[:batch])")
+    ap.add_argument("--mx", action="store_true", help="tune the MX-scaled variant")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--fresh", action="store_true", help="ignore earlier results")
+    ap.add_argument("--results", default=RESULTS, help="measurement log to resume from and append to")
     args = ap.parse_args(argv)
     root = os.path.dirname(HERE)
     if root not in sys.path:
@@ -164,21 +202,28 @@ def main(argv=None) -> int:
         print(msg, flush=True)
 
     done = {}
-    if os.path.exists(RESULTS) and not args.fresh:
-        with open(RESULTS) as f:
+    if os.path.exists(args.results) and not args.fresh:
+        with open(args.results) as f:
             for line in f:
                 rec = json.loads(line)
                 done[rec["key"]] = rec["row"]
     table = gst.load()
-    shapes = {(int(s["n"]), int(s["k"])): s for s in table["shapes"]}
-    for item in args.shapes.split(","):
-        N, K = (int(x) for x in item.split(":"))
+    shapes = {(int(s["n"]), int(s["k"]), bool(s.get("mx", False))): s for s in table["shapes"]}
+    default = REGISTERED_MX if args.mx else [f"{n}:{k}" for n, k in REGISTERED]
+    for item in (args.shapes.split(",") if args.shapes else default):
+        f = [int(x) for x in item.split(":")]
+        N, K = f[0], f[1]
+        batch = f[2] if len(f) > 2 else 1
         t = time.time()
-        rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log)
-        shapes[(N, K)] = {"n": N, "k": K, "rows": [
+        rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log, mx=args.mx, batch=batch,
+                          results_path=args.results)
+        entry = {"n": N, "k": K, "rows": [
             {k: r[k] for k in ("key_m", "kernel", "bm", "bn", "waves", "kblocks", "name", "us")} for r in rows]}
-        log(f"tuned N={N} K={K} in {time.time() - t:.1f}s")
-        table = {"shapes": sorted(shapes.values(), key=lambda s: (s["n"], s["k"]))}
+        if args.mx:
+            entry = {"n": N, "k": K, "mx": True, "batch": batch, "rows": entry["rows"]}
+        shapes[(N, K, args.mx)] = entry
+        log(f"tuned {'MX ' if args.mx else ''}N={N} K={K} batch={batch} in {time.time() - t:.1f}s")
+        table = {"shapes": sorted(shapes.values(), key=gst._order)}
         gst.validate(table)
         with open(gst.TABLE_JSON, "w") as f:
             json.dump(table, f, indent=1)

@@ -154,10 +154,11 @@ int gemm_a8w8_blockscale_packed_run_variant(int32_t variant,
  *                        * e4m3(W[n,k]) * 2^(w_scale[n/32, k/32] - 127) )
  *
  * fp32 accumulation (the scaled MFMA applies the powers of two exactly),
- * one round-to-nearest-even to bf16.  Same kernels, selection (a heuristic
- * plan: no tuned table is registered for this variant, so plans report
- * fallback = 1), threading and error rules as gemm_a8w8_blockscale; K % 128
- * == 0 (whole 128-wide K blocks), and ceil(N/32) * K/128 * 4 < 2^31.
+ * one round-to-nearest-even to bf16.  Same kernels, threading and error
+ * rules as gemm_a8w8_blockscale; the exact-M selector has its own tables for
+ * this variant (the page's shapes), other (N, K) get the heuristic plan
+ * (fallback = 1).  K % 128 == 0 (whole 128-wide K blocks), and
+ * ceil(N/32) * K/128 * 4 < 2^31.
  *
  * Buffers (device memory, row-major, caller-owned):
  *   A        uint8 e4m3fn [batch, M, K]              16-byte aligned

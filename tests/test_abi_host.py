@@ -162,8 +162,8 @@ def test_table_validation_rejects_bad_tables():
         gst.validate(bad)
 
 
-def _table_shapes():
-    return [(int(s["n"]), int(s["k"])) for s in gst.load()["shapes"]]
+def _table_shapes(mx=False):
+    return [(int(s["n"]), int(s["k"])) for s in gst.load()["shapes"] if bool(s.get("mx", False)) == mx]
 
 
 @pytest.mark.parametrize("N,K", REGISTERED)
@@ -238,9 +238,35 @@ def test_mx_run_variant_rejects_like_block_scale():
     assert g.lib().gemm_a8w8_mxscale_run_variant(-1, 16, 16, 16, 16, 16, 1, 4, 512, 1024, 0, None) == g.A8W8_ERR_PLAN
 
 
-@pytest.mark.parametrize("M,N,K", [(48, 1792, 5120), (768, 5120, 8192), (768, 32768, 1280), (16, 1024, 4096),
-                                   (1, 4608, 5120), (3000, 5120, 2304), (100, 20, 4096)])
-def test_mx_plan_is_a_valid_heuristic_plan(M, N, K):
+# The page's MX shapes (dense, and the batched N=1024, K=4096 one).
+REGISTERED_MX = [(1792, 5120), (4608, 5120), (5120, 2304), (5120, 8192), (32768, 1280), (1024, 4096)]
+
+
+@pytest.mark.parametrize("N,K", REGISTERED_MX)
+def test_mx_every_m_has_a_tuned_plan_within_125_percent(N, K):
+    assert (N, K) in _table_shapes(mx=True)
+    for M in range(1, 8193):
+        p = g.gemm_a8w8_mxscale_plan(M, N, K)
+        assert p["fallback"] == 0, (M, p)
+        assert M <= p["key_m"] <= 1.25 * M, (M, p)
+        if M <= 16:
+            assert p["key_m"] == M
+        if p["kernel_name"] in ("skinny", "pskinny"):
+            assert M <= 16
+
+
+def test_mx_and_block_scale_tables_are_separate():
+    # A block-scale table does not serve the MX variant (and the reverse).
+    for N, K in _table_shapes(mx=False):
+        if (N, K) not in REGISTERED_MX:
+            assert g.gemm_a8w8_mxscale_plan(100, N, K)["fallback"] == 1
+    for N, K in REGISTERED_MX:
+        if (N, K) not in _table_shapes(mx=False):
+            assert g.gemm_a8w8_blockscale_plan(100, N, K)["fallback"] == 1
+
+
+@pytest.mark.parametrize("M,N,K", [(48, 1000, 5120), (3000, 5000, 2304), (100, 20, 4096), (7, 640, 1024)])
+def test_mx_unregistered_shape_gets_a_valid_heuristic_plan(M, N, K):
     p = g.gemm_a8w8_mxscale_plan(M, N, K)
     assert p["fallback"] == 1 and p["key_m"] == M
     assert 0 <= p["variant"] < g.gemm_a8w8_num_variants()
