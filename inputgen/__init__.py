@@ -37,6 +37,7 @@ __all__ = [
     "quantize_blocks_128x128", "make_activations", "make_weights",
     "sign_flip_copy", "random_m_values",
     "MX_GROUP", "E4M3_EMAX", "quantize_mx", "make_mx_activations", "make_mx_weights",
+    "quantize_per_row", "make_rowwise_activations", "make_rowwise_weights",
 ]
 
 
@@ -162,3 +163,28 @@ def make_mx_activations(M: int, K: int, seed: int = 0, std: float = 1.0):
 def make_mx_weights(N: int, K: int, seed: int = 1, std: float = 0.02):
     """MX weight operand: (W uint8 [N, K], w_scale uint8 E8M0 [ceil(N/32), K/32])."""
     return quantize_mx(normal_bf16(N, K, std, seed), MX_GROUP)
+
+
+# ---------------------------------------------------------------------------
+# Row-wise operands (per-token activations, per-channel weights): one fp32
+# scale per row over all of K, s = fp32(amax / 448), codes as for the block
+# recipe (the reading of the per-token a8w8 path the pages name).
+
+def quantize_per_row(x: torch.Tensor) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise fp32 [R, K] with one scale per row -> (uint8 [R, K], float32 [R])."""
+    amax = x.abs().amax(dim=1)
+    s = (amax / FP8_MAX).to(torch.float32)
+    safe = torch.where(s > 0, s, torch.ones_like(s))
+    y = (x / safe[:, None]).clamp(-FP8_MAX, FP8_MAX)
+    y = torch.where((s > 0)[:, None], y, torch.zeros_like(y))
+    return _encode_e4m3fn(y).numpy().copy(), s.numpy().copy()
+
+
+def make_rowwise_activations(M: int, K: int, seed: int = 0, std: float = 1.0):
+    """Per-token activation operand: (A uint8 [M, K], a_scale float32 [M])."""
+    return quantize_per_row(normal_bf16(M, K, std, seed))
+
+
+def make_rowwise_weights(N: int, K: int, seed: int = 1, std: float = 0.02):
+    """Per-channel weight operand: (W uint8 [N, K], w_scale float32 [N])."""
+    return quantize_per_row(normal_bf16(N, K, std, seed))

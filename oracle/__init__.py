@@ -1,5 +1,6 @@
-"""CPU fp64 oracle for the a8w8 block-scale GEMM, its MX-scaled variant and
-its activation quantisation step -- TEST INFRASTRUCTURE ONLY.
+"""CPU fp64 oracle for the a8w8 block-scale GEMM, its MX-scaled and row-wise
+(per-token / per-channel) variants and its activation quantisation step --
+TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never does, and the
@@ -15,7 +16,10 @@ of the same quotients, zero groups, the group maximum, the half-spacing
 error bound; for ``gemm_mx``: the E8M0 format definition, exact rational
 brute force, one-group and one-block power-of-two changes that move exactly
 their own K range and rows, a unit-scale numpy matmul special case, and the
-reduction to ``gemm`` when every 32-wide scale of a 128-wide block agrees).
+reduction to ``gemm`` when every 32-wide scale of a 128-wide block agrees;
+for ``gemm_rowwise``: exact rational brute force, exact power-of-two scaling
+of one row and one column, zero scales, a unit-scale numpy matmul case and
+the reduction to ``gemm`` with power-of-two scales).
 """
 from __future__ import annotations
 
@@ -56,6 +60,9 @@ def _load():
             [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.a8w8_oracle_e8m0_value.restype = ctypes.c_double
         lib.a8w8_oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.a8w8_oracle_gemm_rowwise.restype = ctypes.c_int
+        lib.a8w8_oracle_gemm_rowwise.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + \
+            [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.a8w8_oracle_gemm_mx.restype = ctypes.c_int
         lib.a8w8_oracle_gemm_mx.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + \
             [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -213,3 +220,34 @@ def gemm_mx_batched(A, a_scale, W, w_scale, rows=None) -> np.ndarray:
     dimension; ``rows`` (optional) selects the same rows of every batch."""
     return np.stack([gemm_mx(A[i], a_scale[i], W[i], w_scale[i], rows=rows)
                      for i in range(A.shape[0])])
+
+
+def gemm_rowwise(A: np.ndarray, a_scale: np.ndarray, W: np.ndarray, w_scale: np.ndarray,
+                 rows=None) -> np.ndarray:
+    """Row-wise scaled Y (float64) = a_scale[m] * w_scale[n] * (dec(A) . dec(W)^T)[m, n].
+
+    The per-token a8w8 path (one fp32 scale per activation row, one per weight
+    row / output channel), read as the plain row-wise scaled product.
+    A uint8 [M,K]; a_scale float32 [M]; W uint8 [N,K]; w_scale float32 [N].
+    """
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.float32).reshape(-1)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32).reshape(-1)
+    M, K = A.shape
+    N, K2 = W.shape
+    if K2 != K:
+        raise ValueError("A and W disagree on K")
+    if a_scale.size != M or w_scale.size != N:
+        raise ValueError("row-wise scales must be [M] and [N]")
+    if rows is None:
+        n_rows, rows_ptr = M, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows, rows_ptr = rows_arr.size, rows_arr.ctypes.data
+    Y = np.empty((n_rows, N), dtype=np.float64)
+    rc = _load().a8w8_oracle_gemm_rowwise(A.ctypes.data, a_scale.ctypes.data, W.ctypes.data,
+                                          w_scale.ctypes.data, M, N, K, rows_ptr, n_rows, Y.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("a8w8_oracle_gemm_rowwise failed with code %d" % rc)
+    return Y

@@ -242,3 +242,54 @@ int a8w8_oracle_gemm_mx(const uint8_t *A, const uint8_t *a_scale,
     free(Ad);
     return bad ? -2 : 0;
 }
+
+/*
+ * Row-wise ("per-token") variant: one fp32 scale per activation row and one
+ * per weight row (output channel), the non-block-scale a8w8 path that the
+ * "Why aiter#5069's measured -25% kernel win moved serving throughput by
+ * 0.0%" page describes as fed by a per-token fp8 setting (unreachable for its
+ * block-quantised checkpoint).  The pages give no formula; the reading here
+ * is the plain row-wise scaled product:
+ *
+ *   Y[m,n] = a_scale[m] * w_scale[n] * sum_k e4m3fn(A[m,k]) * e4m3fn(W[n,k])
+ *
+ * (fp64; the sum over k ascending, then the two scales, not rounded).
+ * Layouts: A uint8 [M,K]; a_scale float [M]; W uint8 [N,K]; w_scale float [N];
+ * Y double [n_rows, N] for the requested rows (all M when rows == NULL).
+ */
+int a8w8_oracle_gemm_rowwise(const uint8_t *A, const float *a_scale,
+                             const uint8_t *W, const float *w_scale,
+                             int64_t M, int64_t N, int64_t K,
+                             const int64_t *rows, int64_t n_rows, double *Y)
+{
+    double table[256];
+    int64_t r, n;
+
+    if (M < 0 || N < 0 || K < 0 || n_rows < 0)
+        return -1;
+    if (rows == NULL && n_rows != M)
+        return -1;
+    if (n_rows == 0 || N == 0)
+        return 0;
+    if (!A || !a_scale || !W || !w_scale || !Y)
+        return -1;
+    for (r = 0; r < n_rows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        if (m < 0 || m >= M)
+            return -1;
+    }
+    for (int c = 0; c < 256; ++c)
+        table[c] = a8w8_oracle_e4m3fn_value((uint8_t)c);
+
+#pragma omp parallel for schedule(dynamic, 16)
+    for (n = 0; n < N; ++n) {
+        for (int64_t rr = 0; rr < n_rows; ++rr) {
+            int64_t m = rows ? rows[rr] : rr;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += table[A[m * K + k]] * table[W[n * K + k]];
+            Y[rr * N + n] = acc * (double)a_scale[m] * (double)w_scale[n];
+        }
+    }
+    return 0;
+}
