@@ -16,10 +16,12 @@ oracle's own time on the host cores.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--decode-nk N:K] [--decode-ms 1,2,...]   (other decode shapes, e.g. 34816:5120)
        [--workload sweep]                         (the dense-M sweep report)
-       [--no-mx]                                  (skip the MX-scaled points)
+       [--no-mx]                                  (skip the MX-scaled and row-wise points)
 
 The line also reports the MX-scaled variant (E8M0 scales per 1x32 activation
-group and 32x32 weight block) at its page's tuned points, cold weights.
+group and 32x32 weight block) at its page's tuned points, cold weights, and
+the row-wise (per-token / per-channel) variant on the decode and prefill
+shapes.
 """
 from __future__ import annotations
 
@@ -217,6 +219,55 @@ def mx_block(torch, g, inputgen, oracle, dev, replays):
     return out
 
 
+def rowwise_bytes(M: int, N: int, K: int) -> int:
+    """Algorithmic bytes of the row-wise GEMM: W, A, one fp32 scale per row of each, Y."""
+    return N * K + 4 * N + M * K + 4 * M + 2 * M * N
+
+
+def rowwise_block(torch, g, inputgen, oracle, dev, replays):
+    """Row-wise (per-token / per-channel) GEMM: the decode qkv shape (M cycling 1..16, cold
+    weights over >= 1 GiB) and one prefill point, each behind an oracle parity gate."""
+    N, K, Ms = 14336, 5120, (1, 2, 4, 8, 16)
+    A, a_s = inputgen.make_rowwise_activations(16, K, seed=90)
+    W0, w_s = inputgen.make_rowwise_weights(N, K, seed=91)
+    dA, da, dw = (torch.from_numpy(x).to(dev) for x in (A, a_s, w_s))
+    R = max(len(Ms), math.ceil(ROTATE_BYTES / 2 / W0.nbytes) // len(Ms) * len(Ms))
+    copies = [torch.from_numpy(W0).to(dev)] + \
+        [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
+    ref = oracle.gemm_rowwise(A, a_s, W0, w_s)
+    for M in Ms:
+        yh = g.gemm_a8w8_rowwise(dA[:M], da[:M], copies[0], dw).float().cpu().numpy().astype(np.float64)
+        rel = float(np.linalg.norm(yh - ref[:M]) / np.linalg.norm(ref[:M]))
+        if rel > 3e-3 or not np.all(np.isfinite(yh)):
+            raise SystemExit(f"parity gate failed (row-wise M={M}): rel_l2={rel:.3e}")
+    outs = [torch.empty((Ms[r % len(Ms)], N), dtype=torch.bfloat16, device=dev) for r in range(R)]
+    gr = time_graph(torch, [(lambda r=r: g.gemm_a8w8_rowwise(dA[:Ms[r % len(Ms)]], da[:Ms[r % len(Ms)]],
+                                                             copies[r], dw, out=outs[r])) for r in range(R)], 0, 2)
+    us = timed_replays(torch, gr, replays) * 1000.0 / R
+    bytes_mean = sum(rowwise_bytes(Ms[r % len(Ms)], N, K) for r in range(R)) / R
+    out = {"decode": {"us_per_call": round(us, 3), "workload": f"M in {{1,2,4,8,16}}, N={N}, K={K}, cold W "
+                      f"({R} copies)", "hbm_frac": round(bytes_mean / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del gr, copies, outs
+    Mp = 8192
+    Ap, ap_ = inputgen.make_rowwise_activations(Mp, K, seed=92)
+    dAp, dap = torch.from_numpy(Ap).to(dev), torch.from_numpy(ap_).to(dev)
+    dW0 = torch.from_numpy(W0).to(dev)
+    y = g.gemm_a8w8_rowwise(dAp, dap, dW0, dw)
+    rows = [0, 4095, 8191]
+    yh = y[rows].float().cpu().numpy().astype(np.float64)
+    rp = oracle.gemm_rowwise(Ap, ap_, W0, w_s, rows=rows)
+    rel = float(np.linalg.norm(yh - rp) / np.linalg.norm(rp))
+    if rel > 3e-3:
+        raise SystemExit(f"parity gate failed (row-wise prefill): rel_l2={rel:.3e}")
+    gp = time_graph(torch, [lambda: g.gemm_a8w8_rowwise(dAp, dap, dW0, dw, out=y)] * 4, 0, 2)
+    ms = timed_replays(torch, gp, 10) / 4
+    tf = flops(Mp, N, K) / (ms * 1e-3) / 1e12
+    out[f"prefill_M{Mp}_N{N}_K{K}"] = {"us_per_call": round(ms * 1000, 2), "TFLOP_s": round(tf, 1),
+                                        "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
+    del gp
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,7 +282,7 @@ def main():
     ap.add_argument("--decode-nk", default="14336:5120",
                     help="N:K of the decode workload (default: the qkv shape 14336:5120)")
     ap.add_argument("--decode-ms", default="1,2,4,8,16", help="M values the decode workload cycles through")
-    ap.add_argument("--no-mx", action="store_true", help="skip the MX-scaled points")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MX-scaled and row-wise points")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the run, copy 256 MiB device-to-device three times (traffic calibration)")
     args = ap.parse_args()
@@ -386,6 +437,10 @@ def main():
     mx = {} if args.no_mx else mx_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
     log("mx:", json.dumps(mx))
 
+    # ------------------------------------------------------------ row-wise (per-token) variant
+    rowwise = {} if args.no_mx else rowwise_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
+    log("rowwise:", json.dumps(rowwise))
+
     # ------------------------------------------------------------ CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -430,6 +485,7 @@ def main():
         "prefill": prefill,
         "quantize": quant,
         "mx": mx,
+        "rowwise": rowwise,
         "parity": {"worst_rel_l2": round(gate, 6)},
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": cpu,

@@ -13,7 +13,8 @@ Y bfloat16 [M,N].
 The MX-scaled variant (``gemm_a8w8_mxscale`` and its batched and packed
 forms) takes E8M0 scale bytes instead: a_scale uint8 [M,K/32] (one per row
 per 32-wide K group), w_scale uint8 [ceil(N/32),K/32] (one per 32x32 block),
-value 2^(e-127).
+value 2^(e-127).  The row-wise variant (``gemm_a8w8_rowwise``) takes one fp32
+scale per activation row (a_scale [M]) and per weight row (w_scale [N]).
 """
 from __future__ import annotations
 
@@ -53,6 +54,9 @@ EXPORTED = (
     "batched_gemm_a8w8_mxscale_packed",
     "gemm_a8w8_mxscale_plan",
     "gemm_a8w8_mxscale_run_variant",
+    "gemm_a8w8_rowwise",
+    "gemm_a8w8_rowwise_packed",
+    "gemm_a8w8_rowwise_run_variant",
 )
 
 
@@ -119,6 +123,11 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [vp] * 5 + [i64] * 4 + [vp]
         L.gemm_a8w8_mxscale_plan.restype = ctypes.c_int
         L.gemm_a8w8_mxscale_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        for name in ("gemm_a8w8_rowwise", "gemm_a8w8_rowwise_packed"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [vp] * 5 + [i64] * 3 + [vp]
+        L.gemm_a8w8_rowwise_run_variant.restype = ctypes.c_int
+        L.gemm_a8w8_rowwise_run_variant.argtypes = [i32] + [vp] * 5 + [i64] * 3 + [i32, vp]
         L.gemm_a8w8_mxscale_run_variant.restype = ctypes.c_int
         L.gemm_a8w8_mxscale_run_variant.argtypes = [i32] + [vp] * 5 + [i64] * 4 + [i32, vp]
         _lib = L
@@ -393,4 +402,64 @@ def gemm_a8w8_mxscale_run_variant(variant: int, A, a_scale, W, w_scale, out=None
                                              1 if packed_n is not None else 0, _stream_handle(stream))
     if rc != A8W8_OK:
         raise A8W8Error(rc, f"gemm_a8w8_mxscale_run_variant({variant})")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Row-wise variant (fp32 scale per activation row and per weight row)
+
+def _check_rowwise(A, a_scale, W, w_scale, out, N=None):
+    for name, t in (("A", A), ("W", W)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8) or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D float8_e4m3fn (or uint8) tensor")
+    M, K = A.shape
+    rows, K2 = W.shape
+    if N is None:
+        N = rows
+    elif rows != packed_rows(N):
+        raise ValueError(f"packed weights for N={N} have {packed_rows(N)} rows, got {rows}")
+    if K2 != K or K % 128:
+        raise ValueError("A and W must agree on K, a multiple of 128")
+    if a_scale.dtype != torch.float32 or w_scale.dtype != torch.float32 or \
+            tuple(a_scale.shape) != (M,) or tuple(w_scale.shape) != (N,):
+        raise ValueError(f"row-wise scales must be float32 [{M}] and [{N}]")
+    for name, t in (("A", A), ("a_scale", a_scale), ("W", W), ("w_scale", w_scale)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [M,N] tensor")
+    return M, N, K, out
+
+
+def gemm_a8w8_rowwise(A, a_scale, W, w_scale, out=None, stream=None) -> torch.Tensor:
+    """Row-wise scaled Y = a_scale[m] * w_scale[n] * (A . W^T) (per-token / per-channel); bf16 [M,N]."""
+    M, N, K, out = _check_rowwise(A, a_scale, W, w_scale, out)
+    rc = lib().gemm_a8w8_rowwise(A.data_ptr(), a_scale.data_ptr(), W.data_ptr(), w_scale.data_ptr(),
+                                 out.data_ptr(), M, N, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_rowwise")
+    return out
+
+
+def gemm_a8w8_rowwise_packed(A, a_scale, Wp, w_scale, N: int, out=None, stream=None) -> torch.Tensor:
+    """gemm_a8w8_rowwise with W in the packed layout (prepack_weights)."""
+    M, N, K, out = _check_rowwise(A, a_scale, Wp, w_scale, out, N)
+    rc = lib().gemm_a8w8_rowwise_packed(A.data_ptr(), a_scale.data_ptr(), Wp.data_ptr(), w_scale.data_ptr(),
+                                        out.data_ptr(), M, N, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_rowwise_packed")
+    return out
+
+
+def gemm_a8w8_rowwise_run_variant(variant: int, A, a_scale, W, w_scale, out=None, stream=None,
+                                  packed_n: int | None = None) -> torch.Tensor:
+    """Row-wise GEMM with a fixed kernel instance; packed W when packed_n is given."""
+    M, N, K, out = _check_rowwise(A, a_scale, W, w_scale, out, packed_n)
+    rc = lib().gemm_a8w8_rowwise_run_variant(variant, A.data_ptr(), a_scale.data_ptr(), W.data_ptr(),
+                                             w_scale.data_ptr(), out.data_ptr(), M, N, K,
+                                             1 if packed_n is not None else 0, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, f"gemm_a8w8_rowwise_run_variant({variant})")
     return out

@@ -253,20 +253,21 @@ struct Operands {
     void *Y;
     int64_t batch;
     int wpk;   // W in the packed layout
-    int mx;    // MX (E8M0) scales instead of fp32 block scales
+    int sm;    // scale kind: 0 fp32 block scales, 1 MX (E8M0), 2 row-wise fp32
 };
 
 // Elements of each array per batch (scale arrays in 32-bit words: an MX row of
-// K/32 bytes is K/128 words, the same count as a row of fp32 block scales).
+// K/32 bytes is K/128 words, the same count as a row of fp32 block scales;
+// row-wise scales are one word per row).
 void batch_strides(const Operands &o, int64_t M, int64_t N, int64_t K, Args &a)
 {
     const int64_t KB = K / 128;
     const int64_t w_rows = o.wpk ? (N + 15) / 16 * 16 : N;
-    const int64_t s_rows = o.mx ? (N + 31) / 32 : (N + 127) / 128;
+    const int64_t s_rows = o.sm == 1 ? (N + 31) / 32 : (N + 127) / 128;
     a.bs_a = M * K;
-    a.bs_as = M * KB;
+    a.bs_as = o.sm == 2 ? M : M * KB;
     a.bs_w = w_rows * K;
-    a.bs_ws = s_rows * KB;
+    a.bs_ws = o.sm == 2 ? N : s_rows * KB;
     a.bs_y = M * N;
 }
 
@@ -282,7 +283,7 @@ int launch(int id, const Operands &o, int64_t M, int64_t N, int64_t K, int cus, 
     a.N = (int32_t)N;
     a.K = (int32_t)K;
     a.wpk = o.wpk;
-    a.mx = o.mx;
+    a.sm = o.sm;
     batch_strides(o, M, N, K, a);
     if (a8w8::launch_variant(id, a, (int)o.batch, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
         return A8W8_ERR_HIP;
@@ -299,7 +300,7 @@ int check_call(const Operands &o, int64_t M, int64_t N, int64_t K)
         return A8W8_ERR_SHAPE;
     // MX weight-scale rows (one per 32 weight rows): the pskinny kernel's
     // descriptor spans them in 32 bits, the kernels index them in 31.
-    if (o.mx && (N + 31) / 32 * (K / 128) * 4 >= ((int64_t)1 << 31))
+    if (o.sm == 1 && (N + 31) / 32 * (K / 128) * 4 >= ((int64_t)1 << 31))
         return A8W8_ERR_SHAPE;
     return A8W8_OK;
 }
@@ -318,7 +319,9 @@ int gemm_impl(const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    const Choice c = select_variant(M, N, K, cus, o.mx);
+    // Row-wise calls use the block-scale tables: same kernels and loads, less
+    // scale work per block.
+    const Choice c = select_variant(M, N, K, cus, o.sm == 1 ? 1 : 0);
     log_plan(M, N, K, c.variant, c.key_m, c.fallback);
     return launch(c.variant, o, M, N, K, cus, stream);
 }
@@ -389,6 +392,25 @@ int gemm_a8w8_mxscale_run_variant(int32_t variant, const void *A, const void *a_
                                   int32_t w_packed, void *stream)
 {
     return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, batch, w_packed ? 1 : 0, 1}, M, N, K, stream);
+}
+
+int gemm_a8w8_rowwise(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
+                      int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl({A, a_scale, W, w_scale, Y, 1, 0, 2}, M, N, K, stream);
+}
+
+int gemm_a8w8_rowwise_packed(const void *A, const float *a_scale, const void *Wp, const float *w_scale, void *Y,
+                             int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return gemm_impl({A, a_scale, Wp, w_scale, Y, 1, 1, 2}, M, N, K, stream);
+}
+
+int gemm_a8w8_rowwise_run_variant(int32_t variant, const void *A, const float *a_scale, const void *W,
+                                  const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K, int32_t w_packed,
+                                  void *stream)
+{
+    return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, 1, w_packed ? 1 : 0, 2}, M, N, K, stream);
 }
 
 int gemm_a8w8_mxscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)

@@ -26,7 +26,8 @@ struct Args {
     uint16_t *Y;
     int32_t M, N, K;
     int32_t wpk;       // 1: W is in the packed (fragment-order) layout, see packed_block
-    int32_t mx;        // 1: MX scales (E8M0 bytes: 1 x 32 activation groups, 32 x 32 weight blocks)
+    int32_t sm;        // scale kind: 0 fp32 per 1 x 128 / 128 x 128 blocks; 1 MX (E8M0 bytes per
+                       // 1 x 32 / 32 x 32); 2 row-wise (fp32 per activation row, per weight row)
     // Batched calls: gridDim.y batches; batch z reads A + z * bs_a, a_scale + z * bs_as,
     // W + z * bs_w, w_scale + z * bs_ws and writes Y + z * bs_y (elements of each array).
     int64_t bs_a, bs_as, bs_w, bs_ws, bs_y;

@@ -91,20 +91,79 @@ __device__ __forceinline__ v4f mfma_mx(v8i w, v8i a, v4f acc, float w_word, floa
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, acc, 0, 0, 0, ws, 0, as);
 }
 
+// Scale kinds (compile-time SM of every kernel):
+//   SM_BLOCK   fp32 scales per 1 x 128 activation group and 128 x 128 weight block;
+//   SM_MX      E8M0 scales per 1 x 32 activation group and 32 x 32 weight block;
+//   SM_ROWWISE fp32 scale per activation row and per weight row (output
+//              channel): the MFMAs accumulate the unscaled dot over all of K
+//              and the epilogue multiplies by a_scale[m] * w_scale[n].
+constexpr int SM_BLOCK = 0, SM_MX = 1, SM_ROWWISE = 2;
+
 // One K block into the accumulator: block scale (the fp32 product of the two
-// scales, one FMA per output) or MX (E8M0 scales inside the MFMA).
-template <bool MX>
+// scales, one FMA per output), MX (E8M0 scales inside the MFMA) or row-wise
+// (unscaled, in place).
+template <int SM>
 __device__ __forceinline__ v4f block_step(v4f acc, v8i w, v8i a, float sw, float sa, int g)
 {
-    if constexpr (MX)
+    if constexpr (SM == SM_MX) {
         return mfma_mx(w, a, acc, sw, sa, g);
-    else
+    } else if constexpr (SM == SM_ROWWISE) {
+        // zero scale operands select the unscaled instruction
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, acc, 0, 0, 0, 0, 0, 0);
+    } else {
         return fma4(mfma_block(w, a), sa * sw, acc);
+    }
 }
 
-// Weight rows covered by one scale row: 128 (block scale) or 32 (MX).
-template <bool MX>
-constexpr int wscale_shift() { return MX ? 5 : 7; }
+// Weight rows covered by one per-block scale row: 128 (block scale) or 32 (MX).
+template <int SM>
+constexpr int wscale_shift() { return SM == SM_MX ? 5 : 7; }
+
+// Row-wise kind: a lane's outputs for row m, columns n..n+3 times
+// a_scale[m] * w_scale[n + i] (as (v * a) * w), before rounding.  m < M.
+template <int SM>
+__device__ __forceinline__ v4f rowwise_scale(v4f v, const Args &p, int m, int n)
+{
+    if constexpr (SM == SM_ROWWISE) {
+        const float sa = p.a_scale[m];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (n + i < p.N)
+                v[i] = (v[i] * sa) * p.w_scale[n + i];
+    }
+    return v;
+}
+
+// The same scales fetched ahead of time (the weight-streaming kernels load
+// them before their K loop, so the epilogue waits for no memory): row m's
+// a_scale (0 past M) and w_scale of columns n..n+3 (0 past N).
+struct RowScales {
+    float a, w[4];
+};
+template <int SM>
+__device__ __forceinline__ RowScales rowwise_fetch(const Args &p, int m, int n)
+{
+    RowScales r = {0.f, {0.f, 0.f, 0.f, 0.f}};
+    if constexpr (SM == SM_ROWWISE) {
+        if (m < p.M)
+            r.a = p.a_scale[m];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (n + i < p.N)
+                r.w[i] = p.w_scale[n + i];
+    }
+    return r;
+}
+template <int SM>
+__device__ __forceinline__ v4f rowwise_apply(v4f v, const RowScales &r)
+{
+    if constexpr (SM == SM_ROWWISE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = (v[i] * r.a) * r.w[i];
+    }
+    return v;
+}
 
 // Batched launches: batch blockIdx.y works on its own slice of every array.
 __device__ __forceinline__ void select_batch(Args &p)
@@ -199,7 +258,7 @@ __device__ __forceinline__ uint32_t w_rows(const Args &p)
     return PK ? (uint32_t)((p.N + 15) & ~15) : (uint32_t)p.N;
 }
 
-template <int TPW, int D, int NW, bool PK, bool MX>
+template <int TPW, int D, int NW, bool PK, int SM>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 {
     select_batch(p);
@@ -239,7 +298,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     const float *asp = p.a_scale + (size_t)(mval ? r16 : 0) * KB;
     // Weight scale rows.  Block scale: RG divides 128, so the row group lies in
     // one 128-row block.  MX: tiles 2i and 2i+1 lie in one 32-row block (RG is
-    // 16 or a multiple of 32); tiles past N read the last block.
+    // 16 or a multiple of 32); tiles past N read the last block.  Row-wise: no
+    // per-block scales.
+    constexpr bool MX = SM == SM_MX, PER_BLOCK_SCALES = SM != SM_ROWWISE;
     constexpr int WS = MX ? (TPW + 1) / 2 : 1;
     const float *wsp[WS];
 #pragma unroll
@@ -251,10 +312,18 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     for (int t = 0; t < TPW; ++t)
         acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+    // Row-wise: the scales of the outputs this lane stores (wave t stores tile t).
+    static_assert(NW == 1 || TPW <= NW, "each wave stores at most one tile");
+    constexpr int RS = NW > 1 ? 1 : TPW;
+    RowScales rs[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+        rs[i] = rowwise_fetch<SM>(p, r16, n0 + 16 * (NW > 1 ? wave : i) + 4 * g);
+
     for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
         v4i ar[D][2];
         v4i wr[D][TPW][2];
-        float sa[D], sw[D][WS];
+        float sa[D] = {}, sw[D][WS] = {};
         // Issue every load of the pass before consuming any of them.
 #pragma unroll
         for (int j = 0; j < D; ++j) {
@@ -270,10 +339,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[h], koff, 0);
-            sa[j] = asp[kb];
+            if constexpr (PER_BLOCK_SCALES) {
+                sa[j] = asp[kb];
 #pragma unroll
-            for (int i = 0; i < WS; ++i)
-                sw[j][i] = wsp[i][kb];
+                for (int i = 0; i < WS; ++i)
+                    sw[j][i] = wsp[i][kb];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -282,7 +353,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
                 const v8i af = fix_row_layout(ar[j][0], ar[j][1]);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
-                    acc[t] = block_step<MX>(acc[t], w_fragment(wr[j][t][0], wr[j][t][1], pk), af,
+                    acc[t] = block_step<SM>(acc[t], w_fragment(wr[j][t][0], wr[j][t][1], pk), af,
                                             sw[j][MX ? t >> 1 : 0], sa[j], g);
             }
         }
@@ -306,13 +377,13 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
                 v[3] += o[3];
             }
             if (mval)
-                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, v);
+                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, rowwise_apply<SM>(v, rs[0]));
         }
     } else {
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
             if (mval)
-                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, acc[t]);
+                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, rowwise_apply<SM>(acc[t], rs[t]));
     }
 }
 
@@ -336,7 +407,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 // wave order (fixed order: bitwise deterministic) and stores the 16 x 16
 // bf16 tile.  Loads for tiles past the workgroup's share go through a
 // descriptor of zero records, which returns zeros without touching memory.
-template <int D, int NW, int P, bool PK, bool MX>
+template <int D, int NW, int P, bool PK, int SM>
 __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 {
     select_batch(p);
@@ -360,7 +431,8 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
     // Weight scale rows: one per 128 rows (block scale) or per 32 (MX); a
     // 16-row tile lies in one.
-    constexpr int SH = wscale_shift<MX>();
+    constexpr int SH = wscale_shift<SM>();
+    constexpr bool PER_BLOCK_SCALES = SM != SM_ROWWISE;
     const __amdgpu_buffer_rsrc_t sres =
         buffer_rsrc(p.w_scale, (uint32_t)((N + (1 << SH) - 1) >> SH) * (uint32_t)KB * 4u);
 
@@ -368,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
     // (put into the MFMA layout once the first weight loads are issued).
     v4i araw[D][2];
     v8i af[D];
-    float sa[D];
+    float sa[D] = {};
     {
         const float *asp = p.a_scale + (size_t)(mval ? r16 : 0) * KB;
         uint32_t aoff[2];
@@ -383,12 +455,17 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 araw[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ares, (int)aoff[h], kb * 128, 0);
-            sa[j] = asp[kb];
+            if constexpr (PER_BLOCK_SCALES)
+                sa[j] = asp[kb];
         }
     }
 
+    // Row-wise: this lane's a_scale once, the w_scale of its four columns with each tile.
+    const RowScales rs_a = rowwise_fetch<SM>(p, r16, N);
+    const __amdgpu_buffer_rsrc_t rwres = buffer_rsrc(p.w_scale, SM == SM_ROWWISE ? (uint32_t)N * 4u : 0u);
+
     // Issue the weight and w_scale loads of this workgroup's tile i.
-    auto load_tile = [&](int i, v4i (&wr)[D][2], float (&sw)[D]) {
+    auto load_tile = [&](int i, v4i (&wr)[D][2], float (&sw)[D], RowScales &rw) {
         const bool live = i < mine;
         const int n0 = (b + (live ? i : 0) * G) * 16;
         const __amdgpu_buffer_rsrc_t r = live ? wres : none;
@@ -405,16 +482,27 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 wr[j][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[h], wso, 2 /* nt */);
-            sw[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, 0, (srow + kb) * 4, 0));
+            if constexpr (PER_BLOCK_SCALES)
+                sw[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, 0, (srow + kb) * 4, 0));
+            else
+                sw[j] = 0.f;
+        }
+        if constexpr (SM == SM_ROWWISE) {
+            // columns past N (and tiles past the share) read zeros through the descriptors
+            const __amdgpu_buffer_rsrc_t sr = live ? rwres : none;
+            rw.a = rs_a.a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rw.w[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (n0 + 4 * g + e) * 4, 0, 0));
         }
     };
     // Multiply tile i, reduce it over the waves and store it.
-    auto finish_tile = [&](int i, const v4i (&wr)[D][2], const float (&sw)[D]) {
+    auto finish_tile = [&](int i, const v4i (&wr)[D][2], const float (&sw)[D], const RowScales &rw) {
         v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < D; ++j)
             if (kb0 + j < KB)
-                acc = block_step<MX>(acc, w_fragment(wr[j][0], wr[j][1], pk), af[j], sw[j], sa[j], g);
+                acc = block_step<SM>(acc, w_fragment(wr[j][0], wr[j][1], pk), af[j], sw[j], sa[j], g);
         red[i & 1][wave][lane] = acc;
         __syncthreads();
         if (wave == i % NW) {
@@ -428,7 +516,7 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
                 v[3] += o[3];
             }
             if (mval)
-                store4(p.Y, (int64_t)r16 * N, (b + i * G) * 16 + 4 * g, N, vec, v);
+                store4(p.Y, (int64_t)r16 * N, (b + i * G) * 16 + 4 * g, N, vec, rowwise_apply<SM>(v, rw));
         }
     };
 
@@ -436,9 +524,10 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
     // tile i is finished.
     v4i wr[P][D][2];
     float sw[P][D];
+    RowScales rsw[P];
 #pragma unroll
     for (int q = 0; q + 1 < P; ++q)
-        load_tile(q, wr[q], sw[q]);
+        load_tile(q, wr[q], sw[q], rsw[q]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < D; ++j)
@@ -448,9 +537,9 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
     do {
 #pragma unroll
         for (int q = 0; q < P; ++q) {
-            load_tile(i + q + P - 1, wr[(q + P - 1) % P], sw[(q + P - 1) % P]);
+            load_tile(i + q + P - 1, wr[(q + P - 1) % P], sw[(q + P - 1) % P], rsw[(q + P - 1) % P]);
             if (i + q < mine)
-                finish_tile(i + q, wr[q], sw[q]);
+                finish_tile(i + q, wr[q], sw[q], rsw[q]);
         }
         i += P;
     } while (i < mine);
@@ -467,10 +556,11 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 // output row and take one a_scale per block).  Per block: TPW * NT MFMAs,
 // each followed by one scale FMA per output; the wave partials are summed
 // through LDS in wave order and rounded once.
-template <int TPW, int NT, int D, int NW, bool PK, bool MX>
+template <int TPW, int NT, int D, int NW, bool PK, int SM>
 __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
 {
-    static_assert(16 * NT <= (MX ? 32 : 128), "every weight row lies in weight-scale row 0");
+    static_assert(16 * NT <= (SM == SM_MX ? 32 : 128), "every weight row lies in weight-scale row 0");
+    constexpr bool PER_BLOCK_SCALES = SM != SM_ROWWISE;
     select_batch(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -511,9 +601,13 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
         for (int u = 0; u < NT; ++u)
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+    // Row-wise: the scales of the output tile this wave stores (tile i = wave).
+    static_assert(TPW * NT <= NW, "each wave stores at most one output tile");
+    const RowScales rs = rowwise_fetch<SM>(p, m0 + 16 * (wave / NT) + r16, 16 * (wave % NT) + 4 * g);
+
     for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
         v4i wr[D][NT][2], ar[D][TPW][2];
-        float sa[D][TPW], sw[D];
+        float sa[D][TPW] = {}, sw[D] = {};
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int kb = min(kb_begin + j, KB - 1);   // blocks past the end load a valid block, skipped below
@@ -530,10 +624,12 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
                 for (int h = 0; h < 2; ++h)
                     wr[j][u][h] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[u][h], wso, 0);
             }
+            if constexpr (PER_BLOCK_SCALES) {
 #pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                sa[j][t] = asp[t][kb];
-            sw[j] = wsp[kb];
+                for (int t = 0; t < TPW; ++t)
+                    sa[j][t] = asp[t][kb];
+                sw[j] = wsp[kb];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -548,7 +644,7 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
                     const v8i af = fix_row_layout(ar[j][t][0], ar[j][t][1]);
 #pragma unroll
                     for (int u = 0; u < NT; ++u)
-                        acc[t][u] = block_step<MX>(acc[t][u], wf[u], af, sw[j], sa[j][t], g);
+                        acc[t][u] = block_step<SM>(acc[t][u], wf[u], af, sw[j], sa[j][t], g);
                 }
             }
         }
@@ -573,7 +669,7 @@ __global__ __launch_bounds__(NW * 64) void tall_kernel(Args p, int vec_store)
         }
         const int m = m0 + 16 * (i / NT) + r16;
         if (m < M)
-            store4(p.Y, (int64_t)m * N, 16 * (i % NT) + 4 * g, N, vec_store != 0, v);
+            store4(p.Y, (int64_t)m * N, 16 * (i % NT) + 4 * g, N, vec_store != 0, rowwise_apply<SM>(v, rs));
     }
 }
 
@@ -626,10 +722,10 @@ __device__ __forceinline__ v4i tile_rsrc(const uint8_t *base, uint32_t bytes)
 // Issue the copies of one K block into the LDS stage at byte address `stage`:
 // A_LOADS 16-byte copies of activation rows, W_LOADS of weight rows (ra and rw
 // describe the block's tile rows, see tile_kernel), and one 4-byte copy of
-// scale values.  Every wave issues exactly A_LOADS + W_LOADS + 1
-// vector-memory instructions per block, which is what the counted waits in
-// the main loop rely on.
-template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES>
+// scale values (SC: kinds with per-block scales).  Every wave issues exactly
+// A_LOADS + W_LOADS + SC vector-memory instructions per block, which is what
+// the counted waits in the main loop rely on.
+template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES, bool SC>
 __device__ __forceinline__ void issue_tile_loads(v4i ra, v4i rw, const uint32_t (&a_off)[A_LOADS],
                                                  const uint32_t (&w_off)[W_LOADS], const float *s_src, int kb,
                                                  uint32_t stage, int wave)
@@ -640,12 +736,13 @@ __device__ __forceinline__ void issue_tile_loads(v4i ra, v4i rw, const uint32_t 
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i)
         lds_copy16(rw, w_off[i], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + i) * 1024));
-    lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
+    if constexpr (SC)
+        lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
 }
 
-// Copy number j (0 <= j < A_LOADS + W_LOADS + 1) of one block, in the order
+// Copy number j (0 <= j < A_LOADS + W_LOADS + SC) of one block, in the order
 // issue_tile_loads uses.
-template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES>
+template <int A_LOADS, int W_LOADS, int A_BYTES, int W_BYTES, bool SC>
 __device__ __forceinline__ void issue_one(int j, v4i ra, v4i rw, const uint32_t (&a_off)[A_LOADS],
                                           const uint32_t (&w_off)[W_LOADS], const float *s_src, int kb,
                                           uint32_t stage, int wave)
@@ -654,7 +751,7 @@ __device__ __forceinline__ void issue_one(int j, v4i ra, v4i rw, const uint32_t 
         lds_copy16(ra, a_off[j], stage + (uint32_t)(wave * A_LOADS + j) * 1024u);
     else if (j < A_LOADS + W_LOADS)
         lds_copy16(rw, w_off[j - A_LOADS], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + j - A_LOADS) * 1024));
-    else
+    else if constexpr (SC)
         lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
 }
 
@@ -770,7 +867,7 @@ __device__ __forceinline__ void linear_tile(int L, int tiles_m, int tiles_n, int
     tn = in_group / gsize;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, bool MX>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, int SM>
 __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_store)
 {
     select_batch(p);
@@ -780,8 +877,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
     constexpr int STAGE = A_BYTES + W_BYTES + NWAVES * 256;
     constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB copies per wave per block
-    constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
-    constexpr int SH = wscale_shift<MX>();
+    constexpr bool MX = SM == SM_MX, SC = SM != SM_ROWWISE;                  // SC: per-block scale copies
+    constexpr int PER_BLOCK = A_LOADS + W_LOADS + (SC ? 1 : 0);              // vector-memory ops per block
+    constexpr int SH = wscale_shift<SM>();
     constexpr int NBW = (BN + (1 << SH) - 1) >> SH;                          // weight-scale rows a tile spans
     constexpr int WSN = MX ? TN : 1;                                         // weight-scale words per wave
     // Copy schedule.  Wave tiles of three or more slices spread a block's
@@ -883,8 +981,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         c.n0 = tn * BN;
         // Lanes past the needed slots repeat the last needed address: one
         // cache line, not one per lane.
-        c.s_src = slot < BM ? p.a_scale + (size_t)min(c.m0 + slot, M - 1) * KB
-                            : p.w_scale + (size_t)min((c.n0 >> SH) + min(slot - BM, NBW - 1), NB - 1) * KB;
+        c.s_src = !SC         ? p.a_scale
+                  : slot < BM ? p.a_scale + (size_t)min(c.m0 + slot, M - 1) * KB
+                              : p.w_scale + (size_t)min((c.n0 >> SH) + min(slot - BM, NBW - 1), NB - 1) * KB;
         return c;
     };
     // Descriptors of K block kb of a tile: the rows that exist, minus the
@@ -922,13 +1021,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         const int q = min(s, steps - 1);
         const CopyTile c = copy_tile(q / KB);
         const int ckb = q % KB;
-        issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), a_off, w_off,
+        issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES, SC>(rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), a_off, w_off,
                                                             c.s_src, ckb, lds0 + (uint32_t)(s * STAGE), wave);
     }
     wait_vmcnt<(AHEAD - 1) * PER_BLOCK>();
     __syncthreads();
     v8i wf[TN], af;
-    float sa[TM], ws[WSN];
+    float sa[TM] = {}, ws[WSN] = {};
     {
         const uint8_t *sA = smem, *sW = smem + A_BYTES;
         const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
@@ -937,12 +1036,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 #pragma unroll
         for (int u = 1; u < TN; ++u)
             wf[u] = lds_w_fragment<PK>(sW, wrow0 + 16 * u, fo, lane);
+        if constexpr (SC) {
 #pragma unroll
-        for (int t = 0; t < TM; ++t)
-            sa[t] = sS[arow + 16 * t];
+            for (int t = 0; t < TM; ++t)
+                sa[t] = sS[arow + 16 * t];
 #pragma unroll
-        for (int u = 0; u < WSN; ++u)
-            ws[u] = sS[ws_slot[u]];
+            for (int u = 0; u < WSN; ++u)
+                ws[u] = sS[ws_slot[u]];
+        }
     }
 
     // Last slice of the previous block, scaled at the start of the next one
@@ -975,7 +1076,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             if (!LATE && t < SPREAD) {
 #pragma unroll
                 for (int j = t * CPS; j < (t + 1) * CPS && j < PER_BLOCK; ++j)
-                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
+                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES, SC>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
             }
             v8i af_next = af;
             if (t + 1 < TM)
@@ -984,11 +1085,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             // Raised wave priority while this slice's MFMAs issue: the matrix
             // core is fed first when both waves of a SIMD have work.
             __builtin_amdgcn_s_setprio(1);
-            if constexpr (MX) {
-                // MX: the block's scales go into the MFMA, which accumulates in place.
+            if constexpr (SM != SM_BLOCK) {
+                // MX: the block's scales go into the MFMA; row-wise: no per-block
+                // scale.  Either way the MFMA accumulates in place.
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    acc[t][u] = mfma_mx(wf[u], af, acc[t][u], ws[u], sa[t], g);
+                    acc[t][u] = block_step<SM>(acc[t][u], wf[u], af, ws[WSN > 1 ? u : 0], sa[t], g);
             } else {
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
@@ -1005,14 +1107,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
                 for (int u = 0; u < TN; ++u)
                     wf[u] = lds_w_fragment<PK>(nW, wrow0 + 16 * u, fo, lane);
                 af_next = lds_fragment(nA, arow0, fo);
+                if constexpr (SC) {
 #pragma unroll
-                for (int s = 0; s < TM; ++s)
-                    sa[s] = nS[arow + 16 * s];
+                    for (int s = 0; s < TM; ++s)
+                        sa[s] = nS[arow + 16 * s];
 #pragma unroll
-                for (int u = 0; u < WSN; ++u)
-                    ws[u] = nS[ws_slot[u]];
+                    for (int u = 0; u < WSN; ++u)
+                        ws[u] = nS[ws_slot[u]];
+                }
             }
-            if constexpr (!MX) {
+            if constexpr (SM == SM_BLOCK) {
 #pragma unroll
                 for (int u = 0; u < TN; ++u) {
                     if (t > 0)
@@ -1038,7 +1142,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             if (LATE && t == TM - 1) {
 #pragma unroll
                 for (int j = 0; j < PER_BLOCK; ++j)
-                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
+                    issue_one<A_LOADS, W_LOADS, A_BYTES, W_BYTES, SC>(j, ra, rw, a_off, w_off, s_src, ckb, cstage, wave);
             }
 #pragma unroll
             for (int u = 0; u < TN; ++u)
@@ -1068,7 +1172,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         }
 
         // Tile done: fold in the last slice (block scale), round to bf16 and store.
-        if constexpr (!MX) {
+        if constexpr (SM == SM_BLOCK) {
 #pragma unroll
             for (int u = 0; u < TN; ++u)
                 acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
@@ -1080,7 +1184,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             if (m < M) {
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    store4(p.Y, (int64_t)m * N, n_base + 16 * u, N, vec_store != 0, acc[t][u]);
+                    store4(p.Y, (int64_t)m * N, n_base + 16 * u, N, vec_store != 0,
+                           rowwise_scale<SM>(acc[t][u], p, m, n_base + 16 * u));
             }
         }
 #pragma unroll
@@ -1098,10 +1203,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 
 // Explicit instantiations (emit the host-side launch stubs).
 #define A8W8_PTILE_INST(BM, BN, WGM, WGN, S)                                                  \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, false>(Args, int);      \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, false>(Args, int);       \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, true>(Args, int);       \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, true>(Args, int);
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, 0>(Args, int);          \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, 0>(Args, int);           \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, 1>(Args, int);          \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, 1>(Args, int);           \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, 2>(Args, int);          \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, 2>(Args, int);
 A8W8_PTILE_INST(256, 256, 2, 4, 2)
 A8W8_PTILE_INST(256, 128, 2, 4, 3)
 A8W8_PTILE_INST(128, 256, 2, 4, 3)
@@ -1136,7 +1243,7 @@ __device__ __forceinline__ void dma4_at(const void *src, const void *lds_dst)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
 }
 
-template <int A_LOADS, int W_LOADS>
+template <int A_LOADS, int W_LOADS, bool SC>
 __device__ __forceinline__ void issue_block_copies(const uint8_t *const (&a_src)[A_LOADS],
                                                  const uint8_t *const (&w_src)[W_LOADS], const float *as_src,
                                                  int kb, uint8_t *stage, int a_bytes, int w_bytes, int wave,
@@ -1148,7 +1255,8 @@ __device__ __forceinline__ void issue_block_copies(const uint8_t *const (&a_src)
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i)
         dma16_at(w_src[i] + (size_t)kb * w_block_stride, stage + a_bytes + (wave * W_LOADS + i) * 1024);
-    dma4_at(as_src + kb, stage + a_bytes + w_bytes + wave * 256);
+    if constexpr (SC)
+        dma4_at(as_src + kb, stage + a_bytes + w_bytes + wave * 256);
 }
 
 
@@ -1185,7 +1293,7 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 //
 // LDS stage: A tile [BM][128] | W tile [BN][128] | activation scales
 // [64 * waves] floats, tiles swizzled as described at chunk_swizzle().
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, bool MX>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, int SM>
 __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_store)
 {
     select_batch(p);
@@ -1195,7 +1303,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
     constexpr int STAGE = A_BYTES + W_BYTES + NWAVES * 256;
     constexpr int A_LOADS = BM / (8 * NWAVES), W_LOADS = BN / (8 * NWAVES);   // 1 KB loads per wave per block
-    constexpr int PER_BLOCK = A_LOADS + W_LOADS + 1;                         // vector-memory ops per block
+    constexpr bool SC = SM != SM_ROWWISE;                                    // per-block scale copies
+    constexpr int PER_BLOCK = A_LOADS + W_LOADS + (SC ? 1 : 0);              // vector-memory ops per block
     static_assert(A_LOADS >= 1 && W_LOADS >= 1 && BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0,
                   "each wave copies whole 8-row groups of both tiles");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is made of 16 x 16 MFMA outputs");
@@ -1235,12 +1344,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     }
     // Activation scales: wave w copies tile rows 64w + lane (rows past the tile
     // or past M repeat a valid row and are never read).
-    const float *as_src = p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB;
+    const float *as_src = SC ? p.a_scale + (size_t)min(m0 + min(wave * 64 + lane, BM - 1), M - 1) * KB : p.a_scale;
     const int w_stride = PK ? 2048 : 128;   // bytes from one K block of a weight row to the next
     // Weight scales through scalar loads: one row for the wave's columns
     // (block scale), or the row of each 16-row fragment u (MX).
-    constexpr int SH = wscale_shift<MX>();
-    constexpr int WSN = MX ? TN : 1;
+    constexpr int SH = wscale_shift<SM>();
+    constexpr int WSN = SM == SM_MX ? TN : 1;
     const int NB = (N + (1 << SH) - 1) >> SH;
     const_f32 *wsp[WSN];
 #pragma unroll
@@ -1257,12 +1366,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat the last block).
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-        issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
+        issue_block_copies<A_LOADS, W_LOADS, SC>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
                                            W_BYTES, wave, w_stride);
-    float ws_next[WSN];
+    float ws_next[WSN] = {};
+    if constexpr (SC) {
 #pragma unroll
-    for (int u = 0; u < WSN; ++u)
-        ws_next[u] = wsp[u][0];
+        for (int u = 0; u < WSN; ++u)
+            ws_next[u] = wsp[u][0];
+    }
 
     for (int kb = 0; kb < KB; ++kb) {
         float ws[WSN];
@@ -1272,28 +1383,31 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         wait_vmcnt<(STAGES - 2) * PER_BLOCK>();   // this wave's copies of block kb have landed
         __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
         const int kn = min(kb + STAGES - 1, KB - 1);
-        issue_block_copies<A_LOADS, W_LOADS>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
+        issue_block_copies<A_LOADS, W_LOADS, SC>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
                                            A_BYTES, W_BYTES, wave, w_stride);
+        if constexpr (SC) {
 #pragma unroll
-        for (int u = 0; u < WSN; ++u)
-            ws_next[u] = wsp[u][min(kb + 1, KB - 1)];
+            for (int u = 0; u < WSN; ++u)
+                ws_next[u] = wsp[u][min(kb + 1, KB - 1)];
+        }
 
         const uint8_t *sA = smem + (kb % STAGES) * STAGE;
         const uint8_t *sW = sA + A_BYTES;
         const float *sS = reinterpret_cast<const float *>(sW + W_BYTES);
-        if constexpr (MX) {
-            // MX: scales inside the MFMA, accumulated in place.
+        if constexpr (SM != SM_BLOCK) {
+            // MX: scales inside the MFMA; row-wise: none per block.  The MFMA
+            // accumulates in place.
             v8i wf[TN];
 #pragma unroll
             for (int u = 0; u < TN; ++u)
                 wf[u] = lds_w_fragment<PK>(sW, wn * WN + 16 * u, fo, lane);
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                const float sa = sS[wm * WM + 16 * t + r16];
+                const float sa = SC ? sS[wm * WM + 16 * t + r16] : 0.f;
                 const v8i af = lds_fragment(sA, wm * WM + 16 * t, fo);
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    acc[t][u] = mfma_mx(wf[u], af, acc[t][u], ws[u], sa, g);
+                    acc[t][u] = block_step<SM>(acc[t][u], wf[u], af, ws[WSN > 1 ? u : 0], sa, g);
             }
             continue;
         }
@@ -1333,17 +1447,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         if (m < M) {
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                store4(p.Y, (int64_t)m * N, n0 + wn * WN + 16 * u + 4 * g, N, vec_store != 0, acc[t][u]);
+                store4(p.Y, (int64_t)m * N, n0 + wn * WN + 16 * u + 4 * g, N, vec_store != 0,
+                       rowwise_scale<SM>(acc[t][u], p, m, n0 + wn * WN + 16 * u + 4 * g));
         }
     }
 }
 
 
 #define A8W8_TILE_INST(BM, BN, WGM, WGN, S)                                                   \
-    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, false>(Args, int);       \
-    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, false>(Args, int);        \
-    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, true>(Args, int);        \
-    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, true>(Args, int);
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, 0>(Args, int);           \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, 0>(Args, int);            \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, 1>(Args, int);           \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, 1>(Args, int);            \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, false, 2>(Args, int);           \
+    template __global__ void tile_kernel<BM, BN, WGM, WGN, S, true, 2>(Args, int);
 A8W8_TILE_INST(256, 256, 2, 4, 2)
 A8W8_TILE_INST(256, 128, 2, 4, 3)
 A8W8_TILE_INST(128, 256, 2, 4, 3)
@@ -1368,20 +1485,21 @@ using namespace kern;
 // ---------------------------------------------------------------------------
 // Instance table.
 
-// Each instance is compiled four times: fn[2 * mx + wpk], for fp32 block
-// scales (mx 0) or MX scales (mx 1), and row-layout (wpk 0) or packed (wpk 1)
+// Each instance is compiled six times: fn[2 * sm + wpk], for each scale kind
+// sm (SM_BLOCK, SM_MX, SM_ROWWISE) and row-layout (wpk 0) or packed (wpk 1)
 // weights.
 struct Entry {
     Variant v;
-    const void *fn[4];
+    const void *fn[6];
     int lds_bytes;
 };
 
-#define FN_ONE(PKV, MXV, ...) reinterpret_cast<const void *>(&__VA_ARGS__, PKV, MXV>)
-#define FN4(...) {FN_ONE(false, false, __VA_ARGS__), FN_ONE(true, false, __VA_ARGS__), \
-                  FN_ONE(false, true, __VA_ARGS__), FN_ONE(true, true, __VA_ARGS__)}
+#define FN_ONE(PKV, SMV, ...) reinterpret_cast<const void *>(&__VA_ARGS__, PKV, SMV>)
+#define FN6(...) {FN_ONE(false, 0, __VA_ARGS__), FN_ONE(true, 0, __VA_ARGS__), \
+                  FN_ONE(false, 1, __VA_ARGS__), FN_ONE(true, 1, __VA_ARGS__), \
+                  FN_ONE(false, 2, __VA_ARGS__), FN_ONE(true, 2, __VA_ARGS__)}
 #define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, "skinny_r" #TPW "_d" #D "_w" #NW}, \
-                            FN4(skinny_kernel<TPW, D, NW), 0}
+                            FN6(skinny_kernel<TPW, D, NW), 0}
 // Persistent tile grids are sized for WPC waves per CU: 8 (two per SIMD) for
 // the instances above 128 VGPRs, 16 for the small ones, or fewer workgroups
 // where their LDS does not fit.
@@ -1391,19 +1509,19 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 }
 #define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   FN4(tile_kernel<BM, BN, WGM, WGN, S), \
+                                   FN6(tile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 #define PTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_PTILE, BM, BN, WGM * WGN, S, 0, \
                                     tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
                                     "ptile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   FN4(ptile_kernel<BM, BN, WGM, WGN, S), \
+                                   FN6(ptile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
 #define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, \
                                "tall_r" #TPW "_n" #NT "_d" #D "_w" #NW}, \
-                              FN4(tall_kernel<TPW, NT, D, NW), 0}
+                              FN6(tall_kernel<TPW, NT, D, NW), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
-                           FN4(pskinny_kernel<D, NW, P), 0}
+                           FN6(pskinny_kernel<D, NW, P), 0}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
@@ -1482,7 +1600,7 @@ hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;
     void *params[] = {&args, &vec};
-    return hipLaunchKernel(e.fn[2 * (a.mx ? 1 : 0) + (a.wpk ? 1 : 0)], dim3((unsigned)grid, (unsigned)batch),
+    return hipLaunchKernel(e.fn[2 * a.sm + (a.wpk ? 1 : 0)], dim3((unsigned)grid, (unsigned)batch),
                            dim3(e.v.waves * 64), params, (size_t)e.lds_bytes, stream);
 }
 

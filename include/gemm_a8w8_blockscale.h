@@ -194,6 +194,36 @@ int gemm_a8w8_mxscale_run_variant(int32_t variant, const void *A, const void *a_
                                   int64_t batch, int64_t M, int64_t N, int64_t K,
                                   int32_t w_packed, void *stream);
 
+/*
+ * Row-wise ("per-token") variant: one fp32 scale per activation row (token)
+ * and one per weight row (output channel) -- the non-block-scale a8w8 path
+ * that the "Why aiter#5069's measured -25% kernel win moved serving
+ * throughput by 0.0%" page describes as fed by a per-token fp8 setting
+ * (its unreachable-half paragraph).  The pages give no formula; the reading
+ * here is the plain row-wise scaled product
+ *
+ *   Y[m,n] = bf16( (sum_k e4m3(A[m,k]) * e4m3(W[n,k])) * a_scale[m] * w_scale[n] )
+ *
+ * with the dot accumulated in fp32 over all of K and the two scales applied
+ * once, in that order, before the round to nearest even.  Buffers as for
+ * gemm_a8w8_blockscale except a_scale float32 [M] and w_scale float32 [N]
+ * (4-byte aligned).  The _packed form reads a8w8_prepack_weights output.  Same
+ * kernels and selection tables as the block-scale entries, same threading and
+ * error rules; bitwise reproducible.
+ */
+int gemm_a8w8_rowwise(const void *A, const float *a_scale,
+                      const void *W, const float *w_scale,
+                      void *Y, int64_t M, int64_t N, int64_t K, void *stream);
+int gemm_a8w8_rowwise_packed(const void *A, const float *a_scale,
+                             const void *Wp, const float *w_scale,
+                             void *Y, int64_t M, int64_t N, int64_t K, void *stream);
+/* Run a specific instance on row-wise operands (tuning and tests); w_packed
+   selects the packed weight layout. */
+int gemm_a8w8_rowwise_run_variant(int32_t variant, const void *A, const float *a_scale,
+                                  const void *W, const float *w_scale, void *Y,
+                                  int64_t M, int64_t N, int64_t K, int32_t w_packed,
+                                  void *stream);
+
 /* Static name of a compiled instance, e.g. "tile_256x128" (NULL if out of range). */
 const char *gemm_a8w8_variant_name(int32_t variant);
 

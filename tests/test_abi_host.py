@@ -274,3 +274,29 @@ def test_mx_unregistered_shape_gets_a_valid_heuristic_plan(M, N, K):
         assert M <= 16
     if p["kernel_name"] == "tall":
         assert N <= p["bn"]
+
+
+# ---------------------------------------------------------------- row-wise entries
+
+def _rw(name="gemm_a8w8_rowwise", A=16, a_s=16, W=16, w_s=16, Y=16, M=4, N=512, K=1024):
+    return getattr(g.lib(), name)(A, a_s, W, w_s, Y, M, N, K, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_a8w8_rowwise", "gemm_a8w8_rowwise_packed"])
+def test_rowwise_entries_check_arguments(name):
+    assert _rw(name, K=100) == g.A8W8_ERR_SHAPE
+    assert _rw(name, N=0) == g.A8W8_ERR_SHAPE
+    assert _rw(name, M=-3) == g.A8W8_ERR_SHAPE
+    assert _rw(name, a_s=None) == g.A8W8_ERR_NULL
+    assert _rw(name, Y=None) == g.A8W8_ERR_NULL
+    assert _rw(name, A=8) == g.A8W8_ERR_ALIGN
+    assert _rw(name, w_s=6) == g.A8W8_ERR_ALIGN
+    assert _rw(name, M=0, A=None, a_s=None) == g.A8W8_OK
+
+
+def test_rowwise_run_variant_rejects_like_block_scale():
+    skinny = next(i for i in range(g.gemm_a8w8_num_variants())
+                  if g.gemm_a8w8_describe_variant(i)["kernel_name"] == "skinny")
+    L = g.lib()
+    assert L.gemm_a8w8_rowwise_run_variant(skinny, 16, 16, 16, 16, 16, 17, 512, 1024, 0, None) == g.A8W8_ERR_PLAN
+    assert L.gemm_a8w8_rowwise_run_variant(10 ** 6, 16, 16, 16, 16, 16, 4, 512, 1024, 0, None) == g.A8W8_ERR_PLAN
