@@ -71,10 +71,11 @@ class Plan(ctypes.Structure):
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("kblocks", ctypes.c_int32),
                 ("kpasses", ctypes.c_int32), ("fallback", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("key_m", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("key_m", ctypes.c_int64),
+                ("splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
         d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
         return d
 

@@ -15,13 +15,16 @@
 // recommends after its build-time lookup raised instead (its Gate 1).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <set>
 #include <tuple>
+#include <utility>
 
 #include "a8w8_internal.h"
 #include "a8w8_selector_table.h"
@@ -38,6 +41,8 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 // Batches are the grid's y dimension.
 constexpr int64_t kMaxBatch = 65535;
+// Largest split-K workspace (fp32 partial tiles) one stream may hold.
+constexpr int64_t kMaxWorkspace = (int64_t)128 << 20;
 
 // Per-device state: 0 = not yet checked, 1 = gfx950 ready, 2 = unsupported.
 std::atomic<int> g_dev_state[kMaxDevices];
@@ -109,6 +114,9 @@ bool skinny_fits(int64_t N, int64_t K)
 bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
 {
     const Variant &v = a8w8::variant(id);
+    // Split K: at least two K blocks per split, and a workspace within the cap.
+    if (v.splits > 1 && (K / 128 < 2 * (int64_t)v.splits || a8w8::variant_workspace_bytes(id, M, N) > kMaxWorkspace))
+        return false;
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return M <= v.max_m && skinny_fits(N, K);
     if (v.kernel == A8W8_KERNEL_PSKINNY)
@@ -118,15 +126,75 @@ bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
     return true;
 }
 
-int find_variant(int kernel, int bm, int bn, int waves, int kblocks)
+int find_variant(int kernel, int bm, int bn, int waves, int kblocks, int splits = 1)
 {
     for (int i = 0; i < a8w8::num_variants(); ++i) {
         const Variant &v = a8w8::variant(i);
         if (v.kernel == kernel && v.bm == bm && v.bn == bn && (waves == 0 || v.waves == waves) &&
-            (kblocks == 0 || v.kblocks == kblocks))
+            (kblocks == 0 || v.kblocks == kblocks) && v.splits == splits)
             return i;
     }
     return -1;
+}
+
+// The same instance without split K.
+int unsplit_twin(int id)
+{
+    const Variant &v = a8w8::variant(id);
+    return v.splits > 1 ? find_variant(v.kernel, v.bm, v.bn, v.waves, v.kblocks, 1) : id;
+}
+
+// Split-K workspace of one (device, stream): fp32 partial tiles and the
+// per-tile counters, which start at zero and are reset by the last split of
+// each tile.  One per stream, so calls on different streams never share one;
+// calls on one stream run in order.
+struct Workspace {
+    float *buf = nullptr;
+    int64_t bytes = 0;
+    int32_t *cnt = nullptr;
+    int64_t counters = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+// The calling stream's workspace with room for `bytes` and `counters`,
+// allocated (or grown) here -- only while the stream is not capturing a
+// graph.  Growing waits for the stream's earlier work (it may still use the
+// old buffers).  Returns false when no suitable workspace can be had; the
+// caller then runs the unsplit instance.
+bool stream_workspace(int dev, hipStream_t stream, int64_t bytes, int64_t counters, float **ws, int32_t **cnt)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    if (w.bytes < bytes || w.counters < counters) {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone)
+            return false;
+        if (w.buf || w.cnt) {
+            if (hipStreamSynchronize(stream) != hipSuccess)
+                return false;
+            (void)hipFree(w.buf);
+            (void)hipFree(w.cnt);
+            w = Workspace{};
+        }
+        const int64_t nb = std::max<int64_t>(bytes, (int64_t)8 << 20);
+        const int64_t nc = std::max<int64_t>(counters, (int64_t)1 << 14);
+        void *b = nullptr, *c = nullptr;
+        if (hipMalloc(&b, (size_t)nb) != hipSuccess || hipMalloc(&c, (size_t)nc * 4) != hipSuccess ||
+            hipMemsetAsync(c, 0, (size_t)nc * 4, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(b);
+            (void)hipFree(c);
+            return false;
+        }
+        w.buf = static_cast<float *>(b);
+        w.bytes = nb;
+        w.cnt = static_cast<int32_t *>(c);
+        w.counters = nc;
+    }
+    *ws = w.buf;
+    *cnt = w.cnt;
+    return true;
 }
 
 // Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
@@ -201,7 +269,7 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx)
                 hi = mid;
         }
         if (lo < s.count) {
-            const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo], s.kblocks[lo]);
+            const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo], s.kblocks[lo], s.splits[lo]);
             if (v >= 0 && variant_accepts(v, M, N, K))
                 return {v, s.key_m[lo], 0};
         }
@@ -224,6 +292,7 @@ void fill_plan(int id, int64_t M, int64_t N, int64_t K, int cus, int64_t key_m, 
     out->grid = M > 0 ? a8w8::variant_grid(id, M, N, K, cus) : 0;
     out->key_m = key_m;
     out->fallback = fallback;
+    out->splits = v.splits;
 }
 
 // GEMM_A8W8_LOG=1: one stderr line per distinct (M, N, K) with the plan used.
@@ -274,6 +343,19 @@ void batch_strides(const Operands &o, int64_t M, int64_t N, int64_t K, Args &a)
 int launch(int id, const Operands &o, int64_t M, int64_t N, int64_t K, int cus, void *stream)
 {
     Args a;
+    a.splits = 1;
+    a.ws = nullptr;
+    a.cnt = nullptr;
+    if (a8w8::variant(id).splits > 1) {
+        int dev = 0;
+        const int64_t bytes = o.batch * a8w8::variant_workspace_bytes(id, M, N);
+        const int64_t counters = o.batch * a8w8::variant_counters(id, M, N);
+        if (hipGetDevice(&dev) == hipSuccess && bytes <= kMaxWorkspace &&
+            stream_workspace(dev, static_cast<hipStream_t>(stream), bytes, counters, &a.ws, &a.cnt))
+            a.splits = a8w8::variant(id).splits;
+        else
+            id = unsplit_twin(id);
+    }
     a.A = static_cast<const uint8_t *>(o.A);
     a.a_scale = static_cast<const float *>(o.a_scale);
     a.W = static_cast<const uint8_t *>(o.W);

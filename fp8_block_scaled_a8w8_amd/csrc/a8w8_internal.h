@@ -14,6 +14,7 @@ struct Variant {
     int32_t kblocks;   // K blocks each wave loads (skinny, pskinny), LDS ring depth (tile)
     int32_t max_m;     // largest M the instance accepts (skinny, pskinny: 16), 0 = any
     int32_t per_cu;    // ptile, pskinny: workgroups per CU the persistent grid is sized for
+    int32_t splits;    // tile: workgroups per output tile, each taking 1/splits of K (1: no split)
     const char *name;
 };
 
@@ -31,10 +32,19 @@ struct Args {
     // Batched calls: gridDim.y batches; batch z reads A + z * bs_a, a_scale + z * bs_as,
     // W + z * bs_w, w_scale + z * bs_ws and writes Y + z * bs_y (elements of each array).
     int64_t bs_a, bs_as, bs_w, bs_ws, bs_y;
+    // Split K (tile kernel): splits per tile; the calling stream's workspace for the
+    // fp32 partial tiles [batch][tile][split][BM * BN] and one zeroed counter per
+    // [batch][tile] (the last split of a tile resets it).
+    int32_t splits;
+    float *ws;
+    int32_t *cnt;
 };
 
 int num_variants();
 const Variant &variant(int id);
+// Workspace a split-K instance needs per batch: fp32 partial bytes and counters.
+int64_t variant_workspace_bytes(int id, int64_t M, int64_t N);
+int64_t variant_counters(int id, int64_t M, int64_t N);
 // Workgroups the instance launches for (M, N, K) on a device with `cus`
 // compute units (ptile, pskinny: min(tiles, cus * per_cu), each workgroup
 // looping over its share of the tiles), and the passes over K one wave makes

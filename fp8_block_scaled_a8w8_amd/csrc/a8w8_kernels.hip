@@ -1260,17 +1260,20 @@ __device__ __forceinline__ void issue_block_copies(const uint8_t *const (&a_src)
 }
 
 
-// Tile index of workgroup `b` among T tiles: workgroups are dispatched to the
-// 8 XCDs round-robin (b % 8), so each XCD is given a contiguous range of tile
-// ids; inside it, tiles run in groups of G tile-rows, column by column, so the
-// workgroups that are resident together on one XCD share A rows and W rows in
-// that XCD's L2.  A bijection on [0, T): results do not depend on it.
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int G, int &tm, int &tn)
+// Work item of workgroup `b` among T items (T = the grid): workgroups are
+// dispatched to the 8 XCDs round-robin (b % 8), so each XCD is given a
+// contiguous range of item ids.  group_tile then runs tiles in groups of G
+// tile-rows, column by column, so the workgroups that are resident together
+// on one XCD share A rows and W rows in that XCD's L2.  Both are bijections:
+// results do not depend on them.
+__device__ __forceinline__ int xcd_item(int b, int T)
 {
-    const int T = tiles_m * tiles_n;
     const int xcd = b & 7, local = b >> 3;
     const int q = T >> 3, r = T & 7;
-    const int t = xcd * q + min(xcd, r) + local;
+    return xcd * q + min(xcd, r) + local;
+}
+__device__ __forceinline__ void group_tile(int t, int tiles_m, int tiles_n, int G, int &tm, int &tn)
+{
     const int per_group = G * tiles_n;
     const int group = t / per_group;
     const int first_m = group * G;
@@ -1281,6 +1284,17 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 }
 
 
+// Split K (p.splits = S > 1, for shapes with too few output tiles to fill the
+// chip): the grid holds S workgroups per tile -- work item t = S * tile + s,
+// XCD-contiguous as above, so a tile's splits mostly share one L2 -- and split
+// s walks K blocks [s KB / S, (s + 1) KB / S).  Each writes its fp32 partial
+// tile to the stream's workspace (lane-contiguous, 1 KB per wave fragment),
+// makes it visible at device scope and counts itself in the tile's counter;
+// the last of the S to arrive sums the S partials in split order 0, 1, ...
+// (a fixed order whatever the arrival order, so the result is bitwise
+// reproducible), rounds and stores the tile, and resets the counter to zero
+// for the next call.  Nothing waits on another workgroup.
+//
 // Tile kernel.  A workgroup of WGM x WGN waves owns a BM x BN output tile and
 // walks K one 128-wide scale block at a time through a STAGES-deep ring of LDS
 // buffers: block kb+STAGES-1 is copied global -> LDS (direct-to-LDS loads, no
@@ -1317,9 +1331,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     const int wm = wave / WGN, wn = wave % WGN;
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int S = p.splits;                                  // 1 <= S <= KB
+    const int item = xcd_item((int)blockIdx.x, tiles_m * tiles_n * S);
+    const int tile_lin = item / S, split = item - tile_lin * S;
     int tmi, tni;
-    tile_coords((int)blockIdx.x, tiles_m, tiles_n, BM >= 256 ? 2 : 4, tmi, tni);
+    group_tile(tile_lin, tiles_m, tiles_n, BM >= 256 ? 2 : 4, tmi, tni);
     const int m0 = tmi * BM, n0 = tni * BN;
+    const int kb_lo = split * KB / S, nkb = (split + 1) * KB / S - kb_lo;   // this split's K blocks
     const int r16 = lane & 15, g = lane >> 4;
     const FragOff fo = frag_offsets(lane);
 
@@ -1363,32 +1381,33 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         for (int u = 0; u < TN; ++u)
             acc[t][u] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: blocks 0 .. STAGES-2 in flight (indices past the end repeat the last block).
+    // Prologue: blocks 0 .. STAGES-2 of the split in flight (indices past its
+    // end repeat its last block).
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        issue_block_copies<A_LOADS, W_LOADS, SC>(a_src, w_src, as_src, min(s, KB - 1), smem + s * STAGE, A_BYTES,
-                                           W_BYTES, wave, w_stride);
+    for (int st = 0; st < STAGES - 1; ++st)
+        issue_block_copies<A_LOADS, W_LOADS, SC>(a_src, w_src, as_src, kb_lo + min(st, nkb - 1), smem + st * STAGE,
+                                           A_BYTES, W_BYTES, wave, w_stride);
     float ws_next[WSN] = {};
     if constexpr (SC) {
 #pragma unroll
         for (int u = 0; u < WSN; ++u)
-            ws_next[u] = wsp[u][0];
+            ws_next[u] = wsp[u][kb_lo];
     }
 
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < nkb; ++kb) {
         float ws[WSN];
 #pragma unroll
         for (int u = 0; u < WSN; ++u)
             ws[u] = ws_next[u];
         wait_vmcnt<(STAGES - 2) * PER_BLOCK>();   // this wave's copies of block kb have landed
         __syncthreads();                          // ... every wave's, and stage (kb-1) % STAGES is free
-        const int kn = min(kb + STAGES - 1, KB - 1);
+        const int kn = kb_lo + min(kb + STAGES - 1, nkb - 1);
         issue_block_copies<A_LOADS, W_LOADS, SC>(a_src, w_src, as_src, kn, smem + ((kb + STAGES - 1) % STAGES) * STAGE,
                                            A_BYTES, W_BYTES, wave, w_stride);
         if constexpr (SC) {
 #pragma unroll
             for (int u = 0; u < WSN; ++u)
-                ws_next[u] = wsp[u][min(kb + 1, KB - 1)];
+                ws_next[u] = wsp[u][kb_lo + min(kb + 1, nkb - 1)];
         }
 
         const uint8_t *sA = smem + (kb % STAGES) * STAGE;
@@ -1440,6 +1459,46 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         }
     }
     wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
+
+    if (S > 1) {
+        // Partial tile of split s: [tile][s][wave][t][u][lane] v4f in this batch's workspace.
+        constexpr int TILE_V4 = BM * BN / 4, WAVE_V4 = TM * TN * 64;
+        const size_t tile_g = (size_t)blockIdx.y * tiles_m * tiles_n + tile_lin;
+        v4f *part = reinterpret_cast<v4f *>(p.ws) + tile_g * S * TILE_V4 + wave * WAVE_V4 + lane;
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                part[(size_t)split * TILE_V4 + (t * TN + u) * 64] = acc[t][u];
+        __shared__ int last;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this wave's partial is visible device-wide
+        __syncthreads();                                      // ... and every wave's
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(p.cnt + tile_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        if (!last)
+            return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every split's partial
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                acc[t][u] = part[(t * TN + u) * 64];
+        for (int s2 = 1; s2 < S; ++s2) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    const v4f o = part[(size_t)s2 * TILE_V4 + (t * TN + u) * 64];
+                    acc[t][u][0] += o[0];
+                    acc[t][u][1] += o[1];
+                    acc[t][u][2] += o[2];
+                    acc[t][u][3] += o[3];
+                }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(p.cnt + tile_g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
@@ -1498,7 +1557,7 @@ struct Entry {
 #define FN6(...) {FN_ONE(false, 0, __VA_ARGS__), FN_ONE(true, 0, __VA_ARGS__), \
                   FN_ONE(false, 1, __VA_ARGS__), FN_ONE(true, 1, __VA_ARGS__), \
                   FN_ONE(false, 2, __VA_ARGS__), FN_ONE(true, 2, __VA_ARGS__)}
-#define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, "skinny_r" #TPW "_d" #D "_w" #NW}, \
+#define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, 1, "skinny_r" #TPW "_d" #D "_w" #NW}, \
                             FN6(skinny_kernel<TPW, D, NW), 0}
 // Persistent tile grids are sized for WPC waves per CU: 8 (two per SIMD) for
 // the instances above 128 VGPRs, 16 for the small ones, or fewer workgroups
@@ -1507,20 +1566,25 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 {
     return cmin(163840 / lds_bytes, wpc / waves) > 0 ? cmin(163840 / lds_bytes, wpc / waves) : 1;
 }
-#define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, \
+#define TILE(BM, BN, WGM, WGN, S) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, 1, \
                                     "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
                                    FN6(tile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
+// The same kernel with K split over SPLIT workgroups per tile (name suffix _k<SPLIT>).
+#define TILE_SK(BM, BN, WGM, WGN, S, SPLIT) {{A8W8_KERNEL_TILE, BM, BN, WGM * WGN, S, 0, 0, SPLIT, \
+                                    "tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S "_k" #SPLIT}, \
+                                   FN6(tile_kernel<BM, BN, WGM, WGN, S), \
+                                   S * ((BM + BN) * 128 + WGM * WGN * 256)}
 #define PTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_PTILE, BM, BN, WGM * WGN, S, 0, \
-                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), \
+                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), 1, \
                                     "ptile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
                                    FN6(ptile_kernel<BM, BN, WGM, WGN, S), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
-#define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, \
+#define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, 1, \
                                "tall_r" #TPW "_n" #NT "_d" #D "_w" #NW}, \
                               FN6(tall_kernel<TPW, NT, D, NW), 0}
-#define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
+#define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
                            FN6(pskinny_kernel<D, NW, P), 0}
 
 const Entry kEntries[] = {
@@ -1535,6 +1599,14 @@ const Entry kEntries[] = {
     PSKINNY(5, 8, 2), PSKINNY(4, 10, 3), PSKINNY(6, 8, 2),
     TALL(1, 2, 3, 8), TALL(2, 2, 3, 8), TALL(4, 2, 3, 8), TALL(2, 2, 6, 8), TALL(1, 2, 6, 8), TALL(1, 2, 3, 16),
     TALL(1, 1, 3, 8), TALL(2, 1, 3, 8), TALL(4, 1, 3, 8),
+    TILE_SK(256, 256, 2, 4, 2, 2), TILE_SK(256, 128, 2, 4, 3, 2), TILE_SK(256, 128, 2, 4, 3, 4),
+    TILE_SK(128, 256, 2, 4, 3, 2), TILE_SK(128, 256, 2, 4, 3, 4), TILE_SK(128, 128, 2, 2, 4, 2),
+    TILE_SK(128, 128, 2, 2, 4, 4), TILE_SK(128, 128, 2, 2, 4, 8), TILE_SK(128, 64, 2, 2, 3, 2),
+    TILE_SK(128, 64, 2, 2, 3, 4), TILE_SK(64, 128, 2, 2, 3, 2), TILE_SK(64, 128, 2, 2, 3, 4),
+    TILE_SK(64, 128, 2, 2, 3, 8), TILE_SK(64, 64, 2, 2, 3, 2), TILE_SK(64, 64, 2, 2, 3, 4),
+    TILE_SK(64, 64, 2, 2, 3, 8), TILE_SK(32, 128, 1, 4, 3, 4), TILE_SK(32, 128, 1, 4, 3, 8),
+    TILE_SK(32, 64, 2, 2, 3, 4), TILE_SK(32, 64, 2, 2, 3, 8), TILE_SK(64, 32, 2, 2, 3, 4),
+    TILE_SK(64, 32, 2, 2, 3, 8), TILE_SK(32, 32, 2, 2, 3, 4), TILE_SK(32, 32, 2, 2, 3, 8),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -1561,7 +1633,7 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
     }
     const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
     if (v.kernel == A8W8_KERNEL_TILE)
-        return tiles;
+        return tiles * v.splits;
     const int64_t slots = (int64_t)(cus > 0 ? cus : 1) * v.per_cu;
     return tiles < slots ? tiles : slots;
 }
@@ -1572,9 +1644,26 @@ int64_t variant_passes(int id, int64_t K)
     if (v.kernel == A8W8_KERNEL_PSKINNY)
         return 1;
     if (v.kernel != A8W8_KERNEL_SKINNY && v.kernel != A8W8_KERNEL_TALL)
-        return K / 128;
+        return (K / 128 + v.splits - 1) / v.splits;
     const int64_t per_pass = (int64_t)v.waves * v.kblocks;
     return (K / 128 + per_pass - 1) / per_pass;
+}
+
+int64_t variant_workspace_bytes(int id, int64_t M, int64_t N)
+{
+    const Variant &v = kEntries[id].v;
+    if (v.splits <= 1)
+        return 0;
+    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    return tiles * v.splits * v.bm * v.bn * 4;
+}
+
+int64_t variant_counters(int id, int64_t M, int64_t N)
+{
+    const Variant &v = kEntries[id].v;
+    if (v.splits <= 1)
+        return 0;
+    return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
 }
 
 hipError_t set_kernel_attributes()

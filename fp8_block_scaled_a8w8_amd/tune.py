@@ -76,6 +76,12 @@ def candidates(M: int, N: int, K: int) -> list[dict]:
             continue
         if M >= 1024 and N >= 1024 and v["bm"] * v["bn"] < 128 * 128:
             continue
+        if v["splits"] > 1:
+            # split K only where the unsplit tiles leave CUs idle, with >= 2 blocks per split
+            tiles = -(-M // v["bm"]) * -(-N // v["bn"])
+            if tiles >= 2 * 256 or K // 128 < 2 * v["splits"] or tiles * v["splits"] > 8 * 256 or \
+                    tiles * v["splits"] * v["bm"] * v["bn"] * 4 > (128 << 20):
+                continue
         out.append(v)
     return out
 
@@ -171,7 +177,7 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
         med = {vid: statistics.median(ts) for vid, ts in times.items()}
         best = min(cands, key=lambda v: med[v["variant"]])
         row = {"key_m": M, "kernel": best["kernel_name"], "bm": best["bm"], "bn": best["bn"],
-               "waves": best["waves"], "kblocks": best["kblocks"], "name": best["name"],
+               "waves": best["waves"], "kblocks": best["kblocks"], "splits": best["splits"], "name": best["name"],
                "us": round(med[best["variant"]], 3),
                "candidates": {v["name"]: round(med[v["variant"]], 3) for v in cands}}
         rows.append(row)
@@ -218,7 +224,8 @@ def main(argv=None) -> int:
         rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log, mx=args.mx, batch=batch,
                           results_path=args.results)
         entry = {"n": N, "k": K, "rows": [
-            {k: r[k] for k in ("key_m", "kernel", "bm", "bn", "waves", "kblocks", "name", "us")} for r in rows]}
+            {k: r.get(k, 1) for k in ("key_m", "kernel", "bm", "bn", "waves", "kblocks", "splits", "name", "us")}
+            for r in rows]}
         if args.mx:
             entry = {"n": N, "k": K, "mx": True, "batch": batch, "rows": entry["rows"]}
         shapes[(N, K, args.mx)] = entry

@@ -28,12 +28,20 @@
  * Y must not overlap any input.
  *
  * Threading / asynchrony: calls only enqueue one kernel on `stream` (a
- * hipStream_t of the current device; NULL = the null stream) and return; they
- * never synchronise the host, allocate device memory or issue memsets, so they
- * may be captured into a HIP graph.  Each output element is reduced in a fixed
- * order inside one workgroup, so results are bitwise reproducible.  The first
- * call on a device reads its properties (architecture, compute units) once.
- * Calls are re-entrant; the selector table is immutable.
+ * hipStream_t of the current device; NULL = the null stream) and return.
+ * Plans that split K over several workgroups per output tile (shapes with
+ * few tiles; plan.splits > 1) use a workspace the library keeps per (device,
+ * stream): the first such call on a stream allocates it (at most 128 MB, and
+ * a zero fill of its counters on that stream), a larger later one waits for
+ * the stream and replaces it; it is never allocated while the stream is
+ * capturing a graph -- a split plan without a large enough workspace then
+ * runs unsplit.  Otherwise calls never synchronise the host, allocate device
+ * memory or issue memsets, so they may be captured into a HIP graph (run one
+ * call eagerly on the stream first to keep the split plan).  Each output
+ * element is reduced in a fixed order (split partials in split order), so
+ * results are bitwise reproducible.  The first call on a device reads its
+ * properties (architecture, compute units) once.  Calls are re-entrant; the
+ * selector table is immutable.
  */
 #ifndef GEMM_A8W8_BLOCKSCALE_H
 #define GEMM_A8W8_BLOCKSCALE_H
@@ -79,6 +87,8 @@ typedef struct {
     int64_t grid;       /* workgroups launched for this shape (tile: persistent, at most  */
                         /* a few per CU, each looping over its share of the output tiles) */
     int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
+    int32_t splits;     /* tile: workgroups per output tile, each taking 1/splits of K (1: none) */
+    int32_t reserved;
 } a8w8_plan;
 
 /*

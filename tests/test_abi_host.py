@@ -300,3 +300,28 @@ def test_rowwise_run_variant_rejects_like_block_scale():
     L = g.lib()
     assert L.gemm_a8w8_rowwise_run_variant(skinny, 16, 16, 16, 16, 16, 17, 512, 1024, 0, None) == g.A8W8_ERR_PLAN
     assert L.gemm_a8w8_rowwise_run_variant(10 ** 6, 16, 16, 16, 16, 16, 4, 512, 1024, 0, None) == g.A8W8_ERR_PLAN
+
+
+# ---------------------------------------------------------------- split-K instances
+
+def test_split_instances_need_two_k_blocks_per_split():
+    L = g.lib()
+    for v in g.variants():
+        if v["splits"] > 1:
+            small_k = 128 * (2 * v["splits"] - 1)
+            assert L.gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, 64, 512, small_k,
+                                                      None) == g.A8W8_ERR_PLAN, v["name"]
+            d = g.gemm_a8w8_describe_variant(v["variant"], 100, 1000, 128 * 4 * v["splits"])
+            assert d["kpasses"] == 4
+
+
+def test_split_instances_beyond_the_workspace_cap_are_rejected():
+    v = next(v for v in g.variants() if v["splits"] == 8)
+    # 8 splits x (M x N) fp32 partials far above 128 MB
+    rc = g.lib().gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, 8192, 8192, 4096, None)
+    assert rc == g.A8W8_ERR_PLAN
+
+
+def test_plans_report_splits():
+    for M, N, K in ((1, 14336, 5120), (8192, 14336, 5120)):
+        assert g.gemm_a8w8_blockscale_plan(M, N, K)["splits"] >= 1

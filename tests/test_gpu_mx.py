@@ -64,13 +64,13 @@ def _shape_for(v, cus):
     return tiles_m * v["bm"] - v["bm"] // 2 - 3, N
 
 
-@pytest.mark.parametrize("variant", range(64))
+@pytest.mark.parametrize("variant", range(96))
 def test_every_instance_mx(variant):
     if variant >= g.gemm_a8w8_num_variants():
         pytest.skip("no such instance")
     v = g.gemm_a8w8_describe_variant(variant)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    K = 640
+    K = max(640, 256 * v["splits"])   # split-K instances need >= 2 K blocks per split
     M, N = _shape_for(v, cus)
     A, a, W, w = _mx_operands(M, N, K, seed=1000 + variant)
     dA, da, dW, dw = _dev(A, a, W, w)
@@ -167,7 +167,8 @@ def test_integer_case_bitwise():
     ref = bf16_round(oracle.gemm_mx(A, a, W, w))
     for vid in range(g.gemm_a8w8_num_variants()):
         v = g.gemm_a8w8_describe_variant(vid)
-        if v["kernel_name"] in ("skinny", "pskinny") or (v["kernel_name"] == "tall" and v["bn"] < N):
+        if v["kernel_name"] in ("skinny", "pskinny") or (v["kernel_name"] == "tall" and v["bn"] < N) \
+                or K // 128 < 2 * v["splits"]:
             continue
         y = y_host(g.gemm_a8w8_mxscale_run_variant(vid, dA, da, dW, dw))
         assert np.array_equal(y, ref), v["name"]

@@ -57,13 +57,13 @@ def _shape_for(v, cus):
     return tiles_m * v["bm"] - v["bm"] // 2 - 3, N
 
 
-@pytest.mark.parametrize("variant", range(64))
+@pytest.mark.parametrize("variant", range(96))
 def test_every_instance_packed_equals_row_major(variant):
     if variant >= g.gemm_a8w8_num_variants():
         pytest.skip("no such instance")
     v = g.gemm_a8w8_describe_variant(variant)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    K = 640
+    K = max(640, 256 * v["splits"])   # split-K instances need >= 2 K blocks per split
     M, N = _shape_for(v, cus)
     A, a_s = inputgen.make_activations(M, K, seed=M)
     W, w_s = inputgen.make_weights(N, K, seed=N)
