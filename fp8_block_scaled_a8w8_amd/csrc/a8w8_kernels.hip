@@ -1288,8 +1288,8 @@ __device__ __forceinline__ void group_tile(int t, int tiles_m, int tiles_n, int 
 // chip): the grid holds S workgroups per tile -- work item t = S * tile + s,
 // XCD-contiguous as above, so a tile's splits mostly share one L2 -- and split
 // s walks K blocks [s KB / S, (s + 1) KB / S).  Each writes its fp32 partial
-// tile to the stream's workspace (lane-contiguous, 1 KB per wave fragment),
-// makes it visible at device scope and counts itself in the tile's counter;
+// tile to the stream's workspace with device-scope stores, waits for them to
+// complete and counts itself in the tile's counter;
 // the last of the S to arrive sums the S partials in split order 0, 1, ...
 // (a fixed order whatever the arrival order, so the result is bitwise
 // reproducible), rounds and stores the tile, and resets the counter to zero
@@ -1461,40 +1461,48 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
 
     if (S > 1) {
-        // Partial tile of split s: [tile][s][wave][t][u][lane] v4f in this batch's workspace.
-        constexpr int TILE_V4 = BM * BN / 4, WAVE_V4 = TM * TN * 64;
+        // Partial tile of split s: [tile][s][wave][t][u][component][lane] fp32 in this
+        // batch's workspace, so each dword store covers 256 contiguous bytes.  The
+        // partials are written and read with device-scope (agent) accesses, which
+        // are coherent across the XCDs' L2s by themselves: no cache-wide writeback
+        // or invalidate, which would cost every other tile its cached operands.
+        constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 256;
         const size_t tile_g = (size_t)blockIdx.y * tiles_m * tiles_n + tile_lin;
-        v4f *part = reinterpret_cast<v4f *>(p.ws) + tile_g * S * TILE_V4 + wave * WAVE_V4 + lane;
+        float *part = p.ws + tile_g * S * TILE_F + wave * WAVE_F + lane;
 #pragma unroll
         for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                part[(size_t)split * TILE_V4 + (t * TN + u) * 64] = acc[t][u];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    __hip_atomic_store(part + (size_t)split * TILE_F + ((t * TN + u) * 4 + c) * 64, acc[t][u][c],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __shared__ int last;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this wave's partial is visible device-wide
-        __syncthreads();                                      // ... and every wave's
+        wait_vmcnt<0>();                                     // this wave's partial stores are complete
+        __syncthreads();                                     // ... and every wave's
         if (threadIdx.x == 0)
             last = __hip_atomic_fetch_add(p.cnt + tile_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
         __syncthreads();
         if (!last)
             return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every split's partial
+        // The last split: every other split counted itself after its stores completed.
 #pragma unroll
         for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                acc[t][u] = part[(t * TN + u) * 64];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[t][u][c] = __hip_atomic_load(part + ((t * TN + u) * 4 + c) * 64, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         for (int s2 = 1; s2 < S; ++s2) {
 #pragma unroll
             for (int t = 0; t < TM; ++t)
 #pragma unroll
-                for (int u = 0; u < TN; ++u) {
-                    const v4f o = part[(size_t)s2 * TILE_V4 + (t * TN + u) * 64];
-                    acc[t][u][0] += o[0];
-                    acc[t][u][1] += o[1];
-                    acc[t][u][2] += o[2];
-                    acc[t][u][3] += o[3];
-                }
+                for (int u = 0; u < TN; ++u)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[t][u][c] += __hip_atomic_load(part + (size_t)s2 * TILE_F + ((t * TN + u) * 4 + c) * 64,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (threadIdx.x == 0)
             __hip_atomic_store(p.cnt + tile_g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -7,8 +7,9 @@ fastest one becomes the table row for that key.  A request M is later served
 by the smallest key >= M, so no M runs an instance tuned for more than 1.25 M.
 
 Timing follows the cold-weight method: each call reads its own copy of W
-(copies totalling >= --rotate-gib, default 1 GiB, four times the 256 MB MALL;
-copies are sign-flipped versions of one seeded W), R calls are captured in
+(copies totalling >= --rotate-gib, default 1 GiB, four times the 256 MB MALL,
+at most --max-copies of them; copies are sign-flipped versions of one seeded
+W), R calls are captured in
 one HIP graph, the graph is replayed, and the per-call time is the median of
 --rounds interleaved rounds over all candidates (the pages' own tuner read
 one resident weight copy, which mis-picked instances for decode).
@@ -134,7 +135,7 @@ def _operands(N: int, K: int, mx: bool, batch: int):
 
 
 def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
-               mx: bool = False, batch: int = 1, results_path: str = RESULTS) -> list[dict]:
+               mx: bool = False, batch: int = 1, results_path: str = RESULTS, max_copies: int = 256) -> list[dict]:
     import inputgen
     dev = "cuda:0"
     prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
@@ -142,6 +143,7 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
         return [done[f"{prefix}{N}:{K}:{M}"] for M in key_grid()]      # all measured: no GPU needed
     (dA, da), W0, dw = _operands(N, K, mx, batch)
     R = max(2, math.ceil(rotate_gib * 2**30 / (W0.nbytes + dw.numel() * dw.element_size())))
+    R = min(R, max_copies)          # tiny weights: bounded graphs (the activations dominate the traffic there)
     copies = [torch.from_numpy(W0).to(dev)] + \
         [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
     rows = []
@@ -197,6 +199,7 @@ def main(argv=None) -> int:
     ap.add_argument("--mx", action="store_true", help="tune the MX-scaled variant")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--max-copies", type=int, default=256, help="at most this many weight copies per graph")
     ap.add_argument("--fresh", action="store_true", help="ignore earlier results")
     ap.add_argument("--results", default=RESULTS, help="measurement log to resume from and append to")
     args = ap.parse_args(argv)
@@ -222,7 +225,7 @@ def main(argv=None) -> int:
         batch = f[2] if len(f) > 2 else 1
         t = time.time()
         rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log, mx=args.mx, batch=batch,
-                          results_path=args.results)
+                          results_path=args.results, max_copies=args.max_copies)
         entry = {"n": N, "k": K, "rows": [
             {k: r.get(k, 1) for k in ("key_m", "kernel", "bm", "bn", "waves", "kblocks", "splits", "name", "us")}
             for r in rows]}
