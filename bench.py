@@ -100,9 +100,17 @@ def parity_gate(g, oracle, A, a_s, W_host, w_s, dA, da, dW, dw, Ms, what):
     return worst
 
 
+_SIDE_STREAM = None
+
+
 def time_graph(torch, calls, replays, warmup):
-    """Capture `calls` (list of zero-arg callables) into one HIP graph; return (ms per replay, list)."""
-    s = torch.cuda.Stream()
+    """Capture `calls` (list of zero-arg callables) into one HIP graph (after one eager pass on the
+    capture stream, which also gives split-K plans their per-stream workspace); returns the graph.
+    One side stream serves every capture, so the library keeps one workspace for all of them."""
+    global _SIDE_STREAM
+    if _SIDE_STREAM is None:
+        _SIDE_STREAM = torch.cuda.Stream()
+    s = _SIDE_STREAM
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for c in calls:

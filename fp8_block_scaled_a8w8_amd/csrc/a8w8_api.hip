@@ -158,10 +158,10 @@ std::mutex g_ws_mutex;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
 // The calling stream's workspace with room for `bytes` and `counters`,
-// allocated (or grown) here -- only while the stream is not capturing a
-// graph.  Growing waits for the stream's earlier work (it may still use the
-// old buffers).  Returns false when no suitable workspace can be had; the
-// caller then runs the unsplit instance.
+// allocated (or replaced by a larger one) here -- only while the stream is not
+// capturing a graph.  A replaced workspace is retired, never freed: graphs
+// captured earlier keep using it.  Returns false when no suitable workspace
+// can be had; the caller then runs the unsplit instance.
 bool stream_workspace(int dev, hipStream_t stream, int64_t bytes, int64_t counters, float **ws, int32_t **cnt)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -170,25 +170,18 @@ bool stream_workspace(int dev, hipStream_t stream, int64_t bytes, int64_t counte
         hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone)
             return false;
-        if (w.buf || w.cnt) {
-            if (hipStreamSynchronize(stream) != hipSuccess)
-                return false;
-            (void)hipFree(w.buf);
-            (void)hipFree(w.cnt);
-            w = Workspace{};
-        }
-        const int64_t nb = std::max<int64_t>(bytes, (int64_t)8 << 20);
-        const int64_t nc = std::max<int64_t>(counters, (int64_t)1 << 14);
+        const int64_t nb = std::max<int64_t>(std::max<int64_t>(bytes, 2 * w.bytes), (int64_t)32 << 20);
+        const int64_t nc = std::max<int64_t>(std::max<int64_t>(counters, 2 * w.counters), (int64_t)1 << 15);
         void *b = nullptr, *c = nullptr;
-        if (hipMalloc(&b, (size_t)nb) != hipSuccess || hipMalloc(&c, (size_t)nc * 4) != hipSuccess ||
+        if (hipMalloc(&b, (size_t)std::min(nb, kMaxWorkspace)) != hipSuccess || hipMalloc(&c, (size_t)nc * 4) != hipSuccess ||
             hipMemsetAsync(c, 0, (size_t)nc * 4, stream) != hipSuccess) {
             (void)hipGetLastError();
             (void)hipFree(b);
             (void)hipFree(c);
             return false;
         }
-        w.buf = static_cast<float *>(b);
-        w.bytes = nb;
+        w.buf = static_cast<float *>(b);          // the previous buffers (if any) stay allocated
+        w.bytes = std::min(nb, kMaxWorkspace);
         w.cnt = static_cast<int32_t *>(c);
         w.counters = nc;
     }

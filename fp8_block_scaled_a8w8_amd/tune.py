@@ -48,11 +48,15 @@ REGISTERED = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6
 REGISTERED_MX = ["1792:5120", "4608:5120", "5120:2304", "5120:8192", "32768:1280", "1024:4096:8"]
 
 
-def key_grid(limit: int = 8192) -> list[int]:
+# The M values the MX page times (M = 16, 48, 768) get exact keys in the MX tables.
+MX_EXTRA_KEYS = (48, 768)
+
+
+def key_grid(limit: int = 8192, extra=()) -> list[int]:
     keys = list(range(1, 17))
     while keys[-1] < limit:
         keys.append(min(limit, int(math.floor(1.25 * (keys[-1] + 1)))))
-    return keys
+    return sorted(set(keys) | set(extra))
 
 
 def candidates(M: int, N: int, K: int) -> list[dict]:
@@ -87,8 +91,15 @@ def candidates(M: int, N: int, K: int) -> list[dict]:
     return out
 
 
+_SIDE_STREAM = None
+
+
 def graph_for(calls):
-    s = torch.cuda.Stream()
+    # One side stream for every capture: split-K plans keep one workspace per stream.
+    global _SIDE_STREAM
+    if _SIDE_STREAM is None:
+        _SIDE_STREAM = torch.cuda.Stream()
+    s = _SIDE_STREAM
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for c in calls:
@@ -139,15 +150,16 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
     import inputgen
     dev = "cuda:0"
     prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
-    if all(f"{prefix}{N}:{K}:{M}" in done for M in key_grid()):
-        return [done[f"{prefix}{N}:{K}:{M}"] for M in key_grid()]      # all measured: no GPU needed
+    grid = key_grid(extra=MX_EXTRA_KEYS if mx else ())
+    if all(f"{prefix}{N}:{K}:{M}" in done for M in grid):
+        return [done[f"{prefix}{N}:{K}:{M}"] for M in grid]      # all measured: no GPU needed
     (dA, da), W0, dw = _operands(N, K, mx, batch)
     R = max(2, math.ceil(rotate_gib * 2**30 / (W0.nbytes + dw.numel() * dw.element_size())))
     R = min(R, max_copies)          # tiny weights: bounded graphs (the activations dominate the traffic there)
     copies = [torch.from_numpy(W0).to(dev)] + \
         [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
     rows = []
-    for M in key_grid():
+    for M in grid:
         key = f"{prefix}{N}:{K}:{M}"
         if key in done:
             rows.append(done[key])

@@ -31,13 +31,17 @@
  * hipStream_t of the current device; NULL = the null stream) and return.
  * Plans that split K over several workgroups per output tile (shapes with
  * few tiles; plan.splits > 1) use a workspace the library keeps per (device,
- * stream): the first such call on a stream allocates it (at most 128 MB, and
- * a zero fill of its counters on that stream), a larger later one waits for
- * the stream and replaces it; it is never allocated while the stream is
- * capturing a graph -- a split plan without a large enough workspace then
- * runs unsplit.  Otherwise calls never synchronise the host, allocate device
- * memory or issue memsets, so they may be captured into a HIP graph (run one
- * call eagerly on the stream first to keep the split plan).  Each output
+ * stream) for the life of the process: the first such call on a stream
+ * allocates it (32 to 128 MB, plus a zero fill of its counters on that
+ * stream), a later one that needs more allocates a larger one (the old one
+ * stays allocated, for graphs captured with it); none is allocated while
+ * the stream is capturing a graph -- a split plan without a large enough
+ * workspace then runs unsplit.  A captured graph uses the workspace of the
+ * stream it was captured on: do not run it concurrently with other work
+ * captured or enqueued on that stream.  Otherwise calls never synchronise
+ * the host, allocate device memory or issue memsets, so they may be captured
+ * into a HIP graph (run one call eagerly on the stream first to keep the
+ * split plan).  Each output
  * element is reduced in a fixed order (split partials in split order), so
  * results are bitwise reproducible.  The first call on a device reads its
  * properties (architecture, compute units) once.  Calls are re-entrant; the
