@@ -1,8 +1,9 @@
 """Tune the exact-M selector table on one MI355X.
 
 For every registered (N, K) and every key M -- each M from 1 to 16, then a
-grid whose consecutive keys satisfy key_{i+1} <= 1.25 * (key_i + 1) up to
-8192 -- every compiled kernel instance that accepts M is timed, and the
+grid whose consecutive keys satisfy key_{i+1} = floor(1.125 * (key_i + 1)) up
+to 8192 (the selector allows 1.25) -- every compiled kernel instance that
+accepts M is timed, and the
 fastest one becomes the table row for that key.  A request M is later served
 by the smallest key >= M, so no M runs an instance tuned for more than 1.25 M.
 
@@ -52,10 +53,16 @@ REGISTERED_MX = ["1792:5120", "4608:5120", "5120:2304", "5120:8192", "32768:1280
 MX_EXTRA_KEYS = (48, 768)
 
 
+# Above M = 16 consecutive keys grow by 1.125 (half the 1.25 the selector allows): the
+# best instance can change sharply inside one 1.25x interval of the mid-M band
+# (tile-count quantisation), so the finer grid serves every M with a row tuned closer to it.
+KEY_RATIO = 1.125
+
+
 def key_grid(limit: int = 8192, extra=()) -> list[int]:
     keys = list(range(1, 17))
     while keys[-1] < limit:
-        keys.append(min(limit, int(math.floor(1.25 * (keys[-1] + 1)))))
+        keys.append(min(limit, int(math.floor(KEY_RATIO * (keys[-1] + 1)))))
     return sorted(set(keys) | set(extra))
 
 
