@@ -1693,6 +1693,10 @@ hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t
 {
     const Entry &e = kEntries[id];
     const int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
+    // The kernels number workgroups and tiles in 32 bits (and the x dimension of a
+    // grid is limited to 2^31 - 1): refuse, never truncate, a larger grid.
+    if (grid < 1 || grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
     // 8-byte stores need every row (and, batched, every batch) 8-byte aligned.
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;
