@@ -197,3 +197,13 @@ def test_empty_calls_are_no_ops():
     y = torch.full((0, N), 1.0, dtype=torch.bfloat16, device=DEV)
     g.gemm_a8w8_mxscale(dA[:0], da[:0], dW, dw, out=y)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 1000, 3072), (100, 1000, 3072), (1500, 640, 1024), (300, 24, 2048)])
+def test_unregistered_shapes_use_the_heuristic_plan(M, N, K):
+    plan = g.gemm_a8w8_mxscale_plan(M, N, K)
+    assert plan["fallback"] == 1
+    A, a, W, w = _mx_operands(M, N, K, seed=M + N)
+    y = g.gemm_a8w8_mxscale(*_dev(A, a, W, w))
+    rows = _rows(M)
+    assert_parity(y_host(y)[rows], oracle.gemm_mx(A, a, W, w, rows=rows), f"mx heuristic {plan['name']}")

@@ -113,3 +113,12 @@ def test_zero_scales_give_zero_rows_and_columns():
         assert np.all(y[3] == 0) and np.all(y[:, 17] == 0)
         ref = oracle.gemm_rowwise(A[:Ms], a[:Ms], W, w)
         assert_parity(y, ref, f"rowwise zero scales M={Ms}")
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 1000, 3072), (100, 1000, 3072), (1500, 640, 1024), (300, 24, 2048)])
+def test_unregistered_shapes_use_the_heuristic_plan(M, N, K):
+    assert g.gemm_a8w8_blockscale_plan(M, N, K)["fallback"] == 1
+    A, a, W, w = _operands(M, N, K, seed=M + N)
+    y = g.gemm_a8w8_rowwise(*_dev(A, a, W, w))
+    rows = _rows(M)
+    assert_parity(y_host(y)[rows], oracle.gemm_rowwise(A, a, W, w, rows=rows), "rowwise heuristic")
