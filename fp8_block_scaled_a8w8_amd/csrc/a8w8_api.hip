@@ -196,7 +196,8 @@ bool stream_workspace(int dev, hipStream_t stream, int64_t bytes, int64_t counte
 // K in one pass with the fewest blocks per wave.  Above, for N <= 32: the
 // tall kernel (16-row activation groups, 16 waves; 32-row groups from
 // M = 4096).  Otherwise the largest tile that still gives every compute unit
-// at least two workgroups, else the smallest.
+// at least two workgroups, else the smallest, with K split when even that
+// leaves compute units idle.
 int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
 {
     if (M <= 16 && skinny_fits(N, K)) {
@@ -236,7 +237,24 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
         if (tiles >= 2 * (int64_t)cus)
             return find_variant(A8W8_KERNEL_TILE, bm, bn, 0, 0);
     }
-    return find_variant(A8W8_KERNEL_TILE, 32, 32, 0, 0);
+    // Fewer tiles than two per CU even at 32 x 32: split K over S workgroups per tile,
+    // the smallest S (2, 4, 8) that gives every CU a workgroup, keeping >= 4 K blocks
+    // per split (the tuned tables pick split plans in this regime).
+    const int base = find_variant(A8W8_KERNEL_TILE, 32, 32, 0, 0);
+    const Variant &bv = a8w8::variant(base);
+    const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
+    int best = base;
+    for (int s : {2, 4, 8}) {
+        if (K / 128 < 4 * (int64_t)s)
+            break;
+        const int sid = find_variant(A8W8_KERNEL_TILE, 32, 32, bv.waves, bv.kblocks, s);
+        if (sid < 0 || !variant_accepts(sid, M, N, K))
+            continue;
+        best = sid;
+        if (tiles * s >= cus)
+            break;
+    }
+    return best;
 }
 
 struct Choice {
