@@ -25,24 +25,19 @@ namespace kern {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// e4m3fn byte of a finite fp32 value y, rounded to nearest with ties to
-// even, magnitudes above 448 saturating to 448 (so the clamp to [-448, 448]
-// costs one integer minimum).  Bias 7, 3 mantissa bits; below 2^-6 the values
-// are the multiples of 2^-9 (codes 0..7; 8 = 2^-6 is the smallest normal); the
-// largest finite value 448 is code 0x7E.  Branch-free: both encodings are
-// formed and one is selected.
-//   normal:    round the fp32 bits to 3 mantissa bits (add 0x7FFFF plus the
-//              kept LSB, then shift: ties go to the even kept value, a carry
-//              moves into the exponent), then rebias the exponent 127 -> 7.
-//   subnormal: |y| * 2^9 is exact; round it to an integer, ties to even.
-__device__ __forceinline__ uint32_t e4m3fn_rne_sat(float y)
+// e4m3fn bytes of finite fp32 values, rounded to nearest with ties to even,
+// magnitudes above 448 saturating to 448: clamp to [-448, 448] (one med3) and
+// convert with gfx950's v_cvt_pk_fp8_f32, two values per instruction.  On
+// [-448, 448] the conversion is exactly the e4m3fn round-to-nearest-even
+// encoding (bias 7, 3 mantissa bits, multiples of 2^-9 below 2^-6, sign of
+// -0 kept): a device check compared it with a bit-level software encoder for
+// every fp32 value in [0, 448] and its negative, with no difference.
+__device__ __forceinline__ uint32_t e4m3fn_pack4(float q0, float q1, float q2, float q3)
 {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t a = u & 0x7fffffffu;
-    const uint32_t normal = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    const uint32_t code = a < 0x3c800000u ? sub : normal;
-    return ((u >> 24) & 0x80u) | (code < 0x7eu ? code : 0x7eu);
+    const float c0 = __builtin_amdgcn_fmed3f(q0, -448.0f, 448.0f), c1 = __builtin_amdgcn_fmed3f(q1, -448.0f, 448.0f);
+    const float c2 = __builtin_amdgcn_fmed3f(q2, -448.0f, 448.0f), c3 = __builtin_amdgcn_fmed3f(q3, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, lo, true);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -65,20 +60,12 @@ __device__ __forceinline__ float div_rn(float x, float s, float r)
 
 __device__ __forceinline__ uint32_t pack4(const float *x, float s, float r)
 {
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        c |= e4m3fn_rne_sat(div_rn(x[i], s, r)) << (8 * i);
-    return c;
+    return e4m3fn_pack4(div_rn(x[0], s, r), div_rn(x[1], s, r), div_rn(x[2], s, r), div_rn(x[3], s, r));
 }
 
 __device__ __forceinline__ uint32_t pack4_ieee(const float *x, float s)
 {
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        c |= e4m3fn_rne_sat(x[i] / s) << (8 * i);
-    return c;
+    return e4m3fn_pack4(x[0] / s, x[1] / s, x[2] / s, x[3] / s);
 }
 
 // One lane converts 8 consecutive values (16 bytes) of a group; the 16 lanes
