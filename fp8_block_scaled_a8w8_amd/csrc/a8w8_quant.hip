@@ -131,9 +131,13 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t *X, uin
 hipError_t launch_quant_1x128(const void *X, void *A, float *a_scale, int64_t groups, int cus, hipStream_t stream)
 {
     // Small problems: one group per lane group (more workgroups in flight);
-    // large ones: the capped grid walks kGroupsPerTrip groups per trip.
+    // large ones: a capped grid walks kGroupsPerTrip groups per trip.  The cap
+    // grows with the problem -- 8, 16 or 32 workgroups per CU below 16, 64
+    // and above 64 workgroups' worth of groups per CU -- the fastest of the
+    // three measured at M = 1024 .. 16384 (K = 5120) and M = 8192, K = 7168.
     const int64_t wgs = (groups + 15) / 16;
-    const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * 8;
+    const int64_t c = cus > 0 ? cus : 256;
+    const int64_t cap = c * (wgs >= 64 * c ? 32 : wgs >= 16 * c ? 16 : 8);
     const unsigned grid = (unsigned)(wgs < cap ? wgs : cap);
     hipLaunchKernelGGL(kern::quant_1x128_kernel, dim3(grid), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(X), static_cast<uint8_t *>(A), a_scale, groups);
