@@ -137,13 +137,6 @@ int find_variant(int kernel, int bm, int bn, int waves, int kblocks, int splits 
     return -1;
 }
 
-// The same instance without split K.
-int unsplit_twin(int id)
-{
-    const Variant &v = a8w8::variant(id);
-    return v.splits > 1 ? find_variant(v.kernel, v.bm, v.bn, v.waves, v.kblocks, 1) : id;
-}
-
 // Split-K workspace of one (device, stream): fp32 partial tiles and the
 // per-tile counters, which start at zero and are reset by the last split of
 // each tile.  One per stream, so calls on different streams never share one;
@@ -205,7 +198,7 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
         int64_t best_key = 0;
         for (int i = 0; i < a8w8::num_variants(); ++i) {
             const Variant &v = a8w8::variant(i);
-            if (v.kernel != A8W8_KERNEL_SKINNY)
+            if (v.kernel != A8W8_KERNEL_SKINNY || v.splits > 1)
                 continue;
             const int64_t groups = (N + v.bn - 1) / v.bn;
             const int64_t passes = a8w8::variant_passes(i, K);
@@ -364,8 +357,7 @@ int launch(int id, const Operands &o, int64_t M, int64_t N, int64_t K, int cus, 
         if (hipGetDevice(&dev) == hipSuccess && bytes <= kMaxWorkspace &&
             stream_workspace(dev, static_cast<hipStream_t>(stream), bytes, counters, &a.ws, &a.cnt))
             a.splits = a8w8::variant(id).splits;
-        else
-            id = unsplit_twin(id);
+        // else the instance runs unsplit: one workgroup per tile, no workspace.
     }
     a.A = static_cast<const uint8_t *>(o.A);
     a.a_scale = static_cast<const float *>(o.a_scale);

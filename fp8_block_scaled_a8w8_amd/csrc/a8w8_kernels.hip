@@ -236,6 +236,15 @@ __device__ __forceinline__ v8i fix_row_layout(v4i v0, v4i v1)
     return cat(a, b);
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    // s_waitcnt immediate (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Packed weights (the optional offline layout a8w8_prepack_weights writes):
 // rows padded with zeros to a multiple of 16; for every 16-row tile t and K
 // block kb, 2 KB in MFMA operand order, [h][lane][16 bytes], lane l holding
@@ -258,14 +267,21 @@ __device__ __forceinline__ uint32_t w_rows(const Args &p)
     return PK ? (uint32_t)((p.N + 15) & ~15) : (uint32_t)p.N;
 }
 
-template <int TPW, int D, int NW, bool PK, int SM>
+template <int TPW, int D, int NW, bool SK, bool PK, int SM>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
 {
     select_batch(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
-    const int n0 = (int)blockIdx.x * (16 * TPW);
+    // Split K (SK instances, p.splits = S > 1): workgroup i takes row group
+    // i / S and the K blocks [s KB / S, (s + 1) KB / S) of split s = i % S; the
+    // partial sums meet in the fixed-order reduction at the end.  Other
+    // instances fold S = 1 at compile time.
+    const int S = SK ? p.splits : 1;
+    const int tile = (int)blockIdx.x / S, split = (int)blockIdx.x - tile * S;
+    const int kb_lo = split * KB / S, kb_hi = (split + 1) * KB / S;
+    const int n0 = tile * (16 * TPW);
     const int r16 = lane & 15, g = lane >> 4;
     const bool mval = r16 < M;
 
@@ -320,14 +336,14 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
     for (int i = 0; i < RS; ++i)
         rs[i] = rowwise_fetch<SM>(p, r16, n0 + 16 * (NW > 1 ? wave : i) + 4 * g);
 
-    for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
+    for (int kb_begin = kb_lo + wave * D; kb_begin < kb_hi; kb_begin += NW * D) {
         v4i ar[D][2];
         v4i wr[D][TPW][2];
         float sa[D] = {}, sw[D][WS] = {};
         // Issue every load of the pass before consuming any of them.
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            const int kb = min(kb_begin + j, KB - 1);   // blocks past the end load a valid block, skipped below
+            const int kb = min(kb_begin + j, kb_hi - 1);   // blocks past the range load a valid block, skipped below
             const int koff = kb * 128;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            if (kb_begin + j < KB) {
+            if (kb_begin + j < kb_hi) {
                 const v8i af = fix_row_layout(ar[j][0], ar[j][1]);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
@@ -359,31 +375,83 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Args p, int vec_store)
         }
     }
 
-    const bool vec = vec_store != 0;
+    // Each wave's share of the output: with several waves, wave t (t < TPW) sums
+    // tile t over the waves in wave order; a single wave holds every tile.
+    constexpr int NV = NW > 1 ? 1 : TPW;
+    const bool own = NW == 1 || wave < TPW;
+    v4f out[NV];
     if constexpr (NW > 1) {
         __shared__ v4f red[NW][TPW][64];
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
             red[wave][t][lane] = acc[t];
         __syncthreads();
-        for (int t = wave; t < TPW; t += NW) {
-            v4f v = red[0][t][lane];
+        if (own) {
+            out[0] = red[0][wave][lane];
 #pragma unroll
             for (int w = 1; w < NW; ++w) {
-                const v4f o = red[w][t][lane];
-                v[0] += o[0];
-                v[1] += o[1];
-                v[2] += o[2];
-                v[3] += o[3];
+                const v4f o = red[w][wave][lane];
+                out[0][0] += o[0];
+                out[0][1] += o[1];
+                out[0][2] += o[2];
+                out[0][3] += o[3];
             }
-            if (mval)
-                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, rowwise_apply<SM>(v, rs[0]));
         }
     } else {
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-            if (mval)
-                store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, rowwise_apply<SM>(acc[t], rs[t]));
+            out[t] = acc[t];
+    }
+
+    if (S > 1) {
+        // Partial row group of split s: [group][s][tile][component][lane] fp32 in
+        // this batch's workspace, written and read with device-scope accesses;
+        // the last split to count itself sums the S partials in split order and
+        // stores the result (the protocol of the split tile kernel below).
+        constexpr int GROUP_F = 256 * TPW;
+        const size_t group_g = (size_t)blockIdx.y * (gridDim.x / S) + tile;
+        float *part = p.ws + group_g * S * GROUP_F + lane;
+        if (own) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    __hip_atomic_store(part + (size_t)split * GROUP_F + ((NW > 1 ? wave : i) * 4 + c) * 64,
+                                       out[i][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __shared__ int last;
+        wait_vmcnt<0>();                                     // this wave's partial stores are complete
+        __syncthreads();                                     // ... and every wave's
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(p.cnt + group_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        if (!last)
+            return;
+        if (own) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const float *q = part + ((NW > 1 ? wave : i) * 4) * 64;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    out[i][c] = __hip_atomic_load(q + c * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int s2 = 1; s2 < S; ++s2)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        out[i][c] += __hip_atomic_load(q + (size_t)s2 * GROUP_F + c * 64, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(p.cnt + group_g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    const bool vec = vec_store != 0;
+    if (own && mval) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int t = NW > 1 ? wave : i;
+            store4(p.Y, (int64_t)r16 * N, n0 + 16 * t + 4 * g, N, vec, rowwise_apply<SM>(out[i], rs[i]));
+        }
     }
 }
 
@@ -753,15 +821,6 @@ __device__ __forceinline__ void issue_one(int j, v4i ra, v4i rw, const uint32_t 
         lds_copy16(rw, w_off[j - A_LOADS], stage + (uint32_t)(A_BYTES + (wave * W_LOADS + j - A_LOADS) * 1024));
     else if constexpr (SC)
         lds_copy4(s_src + kb, stage + (uint32_t)(A_BYTES + W_BYTES + wave * 256));
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    // s_waitcnt immediate (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // LDS tiles are row-major 128-byte rows whose 16-byte chunk c sits at chunk
@@ -1566,7 +1625,11 @@ struct Entry {
                   FN_ONE(false, 1, __VA_ARGS__), FN_ONE(true, 1, __VA_ARGS__), \
                   FN_ONE(false, 2, __VA_ARGS__), FN_ONE(true, 2, __VA_ARGS__)}
 #define SKINNY(TPW, D, NW) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, 1, "skinny_r" #TPW "_d" #D "_w" #NW}, \
-                            FN6(skinny_kernel<TPW, D, NW), 0}
+                            FN6(skinny_kernel<TPW, D, NW, false), 0}
+// The same kernel with K split over SPLIT workgroups per row group (name suffix _k<SPLIT>).
+#define SKINNY_SK(TPW, D, NW, SPLIT) {{A8W8_KERNEL_SKINNY, 16, 16 * TPW, NW, D, 16, 0, SPLIT, \
+                                       "skinny_r" #TPW "_d" #D "_w" #NW "_k" #SPLIT}, \
+                                      FN6(skinny_kernel<TPW, D, NW, true), 0}
 // Persistent tile grids are sized for WPC waves per CU: 8 (two per SIMD) for
 // the instances above 128 VGPRs, 16 for the small ones, or fewer workgroups
 // where their LDS does not fit.
@@ -1615,6 +1678,8 @@ const Entry kEntries[] = {
     TILE_SK(64, 64, 2, 2, 3, 8), TILE_SK(32, 128, 1, 4, 3, 4), TILE_SK(32, 128, 1, 4, 3, 8),
     TILE_SK(32, 64, 2, 2, 3, 4), TILE_SK(32, 64, 2, 2, 3, 8), TILE_SK(64, 32, 2, 2, 3, 4),
     TILE_SK(64, 32, 2, 2, 3, 8), TILE_SK(32, 32, 2, 2, 3, 4), TILE_SK(32, 32, 2, 2, 3, 8),
+    SKINNY_SK(1, 3, 4, 4), SKINNY_SK(1, 3, 8, 2), SKINNY_SK(2, 3, 8, 2), SKINNY_SK(4, 3, 4, 4),
+    SKINNY_SK(2, 5, 4, 2), SKINNY_SK(4, 5, 4, 2), SKINNY_SK(1, 5, 2, 4), SKINNY_SK(2, 4, 8, 2),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -1629,7 +1694,7 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
     (void)K;
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_SKINNY)
-        return (N + v.bn - 1) / v.bn;
+        return (N + v.bn - 1) / v.bn * v.splits;
     if (v.kernel == A8W8_KERNEL_TALL)
         return (M + v.bm - 1) / v.bm;
     if (v.kernel == A8W8_KERNEL_PSKINNY) {
@@ -1653,8 +1718,8 @@ int64_t variant_passes(int id, int64_t K)
         return 1;
     if (v.kernel != A8W8_KERNEL_SKINNY && v.kernel != A8W8_KERNEL_TALL)
         return (K / 128 + v.splits - 1) / v.splits;
-    const int64_t per_pass = (int64_t)v.waves * v.kblocks;
-    return (K / 128 + per_pass - 1) / per_pass;
+    const int64_t per_pass = (int64_t)v.waves * v.kblocks, per_split = (K / 128 + v.splits - 1) / v.splits;
+    return (per_split + per_pass - 1) / per_pass;
 }
 
 int64_t variant_workspace_bytes(int id, int64_t M, int64_t N)
@@ -1692,7 +1757,11 @@ hipError_t set_kernel_attributes()
 hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t stream)
 {
     const Entry &e = kEntries[id];
-    const int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
+    // A split instance run with fewer splits (a.splits, 1 when no workspace
+    // could be had) launches that many workgroups per tile.
+    int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
+    if (e.v.splits > 1)
+        grid = grid / e.v.splits * a.splits;
     // The kernels number workgroups and tiles in 32 bits (and the x dimension of a
     // grid is limited to 2^31 - 1): refuse, never truncate, a larger grid.
     if (grid < 1 || grid > 0x7fffffff)

@@ -70,7 +70,10 @@ def candidates(M: int, N: int, K: int) -> list[dict]:
     out = []
     for v in variants():
         if v["kernel_name"] == "skinny":
-            if M <= 16:
+            groups = -(-N // v["bn"])
+            # split K only where the unsplit row groups leave CUs idle, with >= 2 blocks per split
+            if M <= 16 and (v["splits"] == 1 or (groups < 2 * 256 and K // 128 >= 2 * v["splits"]
+                                                 and groups * v["splits"] <= 8 * 256)):
                 out.append(v)
             continue
         if v["kernel_name"] == "pskinny":

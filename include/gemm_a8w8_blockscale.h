@@ -91,7 +91,7 @@ typedef struct {
     int64_t grid;       /* workgroups launched for this shape (tile: persistent, at most  */
                         /* a few per CU, each looping over its share of the output tiles) */
     int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
-    int32_t splits;     /* tile: workgroups per output tile, each taking 1/splits of K (1: none) */
+    int32_t splits;     /* tile, skinny: workgroups per output tile, each taking 1/splits of K (1: none) */
     int32_t reserved;
 } a8w8_plan;
 

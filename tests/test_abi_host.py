@@ -309,10 +309,13 @@ def test_split_instances_need_two_k_blocks_per_split():
     for v in g.variants():
         if v["splits"] > 1:
             small_k = 128 * (2 * v["splits"] - 1)
-            assert L.gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, 64, 512, small_k,
+            M = 16 if v["kernel_name"] == "skinny" else 64
+            assert L.gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, M, 512, small_k,
                                                       None) == g.A8W8_ERR_PLAN, v["name"]
-            d = g.gemm_a8w8_describe_variant(v["variant"], 100, 1000, 128 * 4 * v["splits"])
-            assert d["kpasses"] == 4
+            d = g.gemm_a8w8_describe_variant(v["variant"], M, 1000, 128 * 4 * v["splits"])
+            per_pass = v["waves"] * v["kblocks"] if v["kernel_name"] == "skinny" else 1
+            assert d["kpasses"] == -(-4 // per_pass), v["name"]
+            assert d["grid"] == -(-M // v["bm"]) * -(-1000 // v["bn"]) * v["splits"], v["name"]
 
 
 def test_split_instances_beyond_the_workspace_cap_are_rejected():

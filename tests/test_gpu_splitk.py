@@ -1,13 +1,14 @@
-"""GPU tests of split-K plans (tile kernel, several workgroups per output
-tile, fp32 partials in the stream's workspace, the last split of a tile sums
-them in split order and resets the tile's counter).
+"""GPU tests of split-K plans (tile and skinny kernels, several workgroups
+per output tile, fp32 partials in the stream's workspace, the last split of a
+tile sums them in split order and resets the tile's counter).
 
 Checked: every split instance against the oracle and against its unsplit
-twin (both within tolerance), bitwise run-to-run determinism over repeated
-calls (the counters must come back to zero), all three scale kinds, batched
-calls, a captured HIP graph replayed between eager calls, a call captured on
-a stream that has no workspace yet (it must run unsplit: bitwise equal to the
-unsplit instance), and two streams running split plans at once.
+twin where one is registered (both within tolerance), bitwise run-to-run
+determinism over repeated calls (the counters must come back to zero), all
+three scale kinds, batched calls, a captured HIP graph replayed between eager
+calls, a call captured on a stream that has no workspace yet (it must run
+unsplit: bitwise equal to the unsplit instance), and two streams running
+split plans at once.
 """
 from __future__ import annotations
 
@@ -33,32 +34,45 @@ def _split_ids():
 
 
 def _twin(v):
+    """The registered unsplit instance of the same kernel and shape, or None."""
     for u in g.variants():
         if (u["kernel_name"], u["bm"], u["bn"], u["waves"], u["kblocks"], u["splits"]) == \
                 (v["kernel_name"], v["bm"], v["bn"], v["waves"], v["kblocks"], 1):
             return u["variant"]
-    raise AssertionError(f"no unsplit twin for {v['name']}")
+    return None
+
+
+def _split_shape(v, K_extra=384):
+    """A ragged shape for a split instance: K blocks do not divide evenly over the splits."""
+    K = 256 * v["splits"] + K_extra
+    if v["kernel_name"] == "skinny":
+        return 11, 2 * v["bn"] + 40, K
+    return 2 * v["bm"] + 7, 2 * v["bn"] + 40, K
 
 
 def test_split_instances_exist_and_describe_themselves():
     ids = _split_ids()
-    assert len(ids) >= 20
+    kinds = [g.gemm_a8w8_describe_variant(i)["kernel_name"] for i in ids]
+    assert kinds.count("tile") >= 20 and kinds.count("skinny") >= 6
     for vid in ids:
-        v = g.gemm_a8w8_describe_variant(vid, 300, 500, 4096)
-        assert v["kernel_name"] == "tile" and v["name"].endswith(f"_k{v['splits']}")
-        tiles = -(-300 // v["bm"]) * -(-500 // v["bn"])
+        M = 16 if g.gemm_a8w8_describe_variant(vid)["kernel_name"] == "skinny" else 300
+        v = g.gemm_a8w8_describe_variant(vid, M, 500, 4096)
+        assert v["name"].endswith(f"_k{v['splits']}")
+        tiles = -(-M // v["bm"]) * -(-500 // v["bn"])
         assert v["grid"] == tiles * v["splits"]
+    for v in g.variants():
+        if v["splits"] > 1 and v["kernel_name"] == "tile":
+            assert _twin(v) is not None, v["name"]
 
 
-@pytest.mark.parametrize("vid_index", range(32))
+@pytest.mark.parametrize("vid_index", range(40))
 def test_every_split_instance_block_scale(vid_index):
     ids = _split_ids()
     if vid_index >= len(ids):
         pytest.skip("no such split instance")
     vid = ids[vid_index]
     v = g.gemm_a8w8_describe_variant(vid)
-    K = 256 * v["splits"] + 384                      # ragged: K blocks do not divide evenly
-    M, N = 2 * v["bm"] + 7, 2 * v["bn"] + 40
+    M, N, K = _split_shape(v)
     A, a = inputgen.make_activations(M, K, seed=vid)
     W, w = inputgen.make_weights(N, K, seed=vid + 1)
     dA, da, dW, dw = _dev(A, a, W, w)
@@ -70,16 +84,17 @@ def test_every_split_instance_block_scale(vid_index):
         assert np.array_equal(y_bits(y2), y1b), f"{v['name']} not reproducible"
     ref = oracle.gemm(A, a, W, w)
     assert_parity(y_host(y1), ref, f"{v['name']}")
-    yu = g.gemm_a8w8_blockscale_run_variant(_twin(v), dA, da, dW, dw)
-    assert_parity(y_host(yu), ref, f"{v['name']} twin")
+    if _twin(v) is not None:
+        yu = g.gemm_a8w8_blockscale_run_variant(_twin(v), dA, da, dW, dw)
+        assert_parity(y_host(yu), ref, f"{v['name']} twin")
 
 
 @pytest.mark.parametrize("kind", ["mx", "rowwise"])
 def test_split_instances_other_scale_kinds(kind):
-    for vid in _split_ids()[::3]:
+    ids = _split_ids()
+    for vid in ids[::3] + [i for i in ids if g.gemm_a8w8_describe_variant(i)["kernel_name"] == "skinny"]:
         v = g.gemm_a8w8_describe_variant(vid)
-        K = 256 * v["splits"] + 128
-        M, N = v["bm"] + 9, 2 * v["bn"] + 24
+        M, N, K = _split_shape(v, 128)
         if kind == "mx":
             A, a = inputgen.make_mx_activations(M, K, seed=vid)
             W, w = inputgen.make_mx_weights(N, K, seed=vid + 1)
@@ -94,10 +109,16 @@ def test_split_instances_other_scale_kinds(kind):
     say(f"split instances, {kind} scales: ok")
 
 
-def test_split_batched_mx():
-    vid = next(i for i in _split_ids() if g.gemm_a8w8_describe_variant(i)["splits"] == 4)
+def _first_split(kernel, splits):
+    return next(i for i in _split_ids() if (g.gemm_a8w8_describe_variant(i)["kernel_name"],
+                                            g.gemm_a8w8_describe_variant(i)["splits"]) == (kernel, splits))
+
+
+@pytest.mark.parametrize("kernel", ["tile", "skinny"])
+def test_split_batched_mx(kernel):
+    vid = _first_split(kernel, 4)
     v = g.gemm_a8w8_describe_variant(vid)
-    b, M, N, K = 3, v["bm"] + 5, v["bn"] * 2 + 8, 2048
+    b, M, N, K = 3, (v["bm"] + 5 if kernel == "tile" else 13), v["bn"] * 2 + 8, 2048
     parts = [(inputgen.make_mx_activations(M, K, seed=10 + i), inputgen.make_mx_weights(N, K, seed=20 + i))
              for i in range(b)]
     A = np.stack([p[0][0] for p in parts])
@@ -109,17 +130,18 @@ def test_split_batched_mx():
         assert_parity(y[i], oracle.gemm_mx(A[i], a[i], W[i], w[i]), f"batch {i}")
 
 
-def _graph_case():
-    vid = next(i for i in _split_ids() if g.gemm_a8w8_describe_variant(i)["splits"] == 4)
+def _graph_case(kernel):
+    vid = _first_split(kernel, 4)
     v = g.gemm_a8w8_describe_variant(vid)
-    M, N, K = 2 * v["bm"] + 3, 3 * v["bn"], 4096
+    M, N, K = (2 * v["bm"] + 3 if kernel == "tile" else 7), 3 * v["bn"], 4096
     A, a = inputgen.make_activations(M, K, seed=3)
     W, w = inputgen.make_weights(N, K, seed=4)
     return vid, v, A, a, W, w
 
 
-def test_split_plan_in_a_captured_graph():
-    vid, v, A, a, W, w = _graph_case()
+@pytest.mark.parametrize("kernel", ["tile", "skinny"])
+def test_split_plan_in_a_captured_graph(kernel):
+    vid, v, A, a, W, w = _graph_case(kernel)
     dA, da, dW, dw = _dev(A, a, W, w)
     s = torch.cuda.Stream()
     out = torch.empty((A.shape[0], W.shape[0]), dtype=torch.bfloat16, device=DEV)
@@ -141,23 +163,30 @@ def test_split_plan_in_a_captured_graph():
     assert_parity(y_host(out), oracle.gemm(A, a, W, w), "graph replay")
 
 
-def test_capture_without_workspace_runs_unsplit():
-    vid, v, A, a, W, w = _graph_case()
+@pytest.mark.parametrize("kernel", ["tile", "skinny"])
+def test_capture_without_workspace_runs_unsplit(kernel):
+    vid, v, A, a, W, w = _graph_case(kernel)
     dA, da, dW, dw = _dev(A, a, W, w)
-    twin = g.gemm_a8w8_blockscale_run_variant(_twin(v), dA, da, dW, dw)
+    if _twin(v) is None:
+        twin = None
+    else:
+        twin = g.gemm_a8w8_blockscale_run_variant(_twin(v), dA, da, dW, dw)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()                          # fresh stream: no workspace yet
-    out = torch.empty_like(twin)
+    out = torch.empty((A.shape[0], W.shape[0]), dtype=torch.bfloat16, device=DEV)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
         g.gemm_a8w8_blockscale_run_variant(vid, dA, da, dW, dw, out=out)
     graph.replay()
     torch.cuda.synchronize()
-    assert np.array_equal(y_bits(out), y_bits(twin))
+    if twin is not None:
+        assert np.array_equal(y_bits(out), y_bits(twin))
+    assert_parity(y_host(out), oracle.gemm(A, a, W, w), f"{v['name']} captured unsplit")
 
 
-def test_two_streams_run_split_plans_together():
-    vid, v, A, a, W, w = _graph_case()
+@pytest.mark.parametrize("kernel", ["tile", "skinny"])
+def test_two_streams_run_split_plans_together(kernel):
+    vid, v, A, a, W, w = _graph_case(kernel)
     dA, da, dW, dw = _dev(A, a, W, w)
     A2, a2 = inputgen.make_activations(A.shape[0], A.shape[1], seed=33)
     dA2, da2 = _dev(A2, a2)
