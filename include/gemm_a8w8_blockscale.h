@@ -122,7 +122,8 @@ int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
  * Run a specific instance (for tuning).  Same contract as gemm_a8w8_blockscale;
  * returns A8W8_ERR_PLAN if the instance cannot handle the shape (the skinny
  * kernels need M <= 16, a pskinny instance also K/128 <= waves * kblocks; a
- * tall instance needs N <= its bn).
+ * tall instance needs N <= its bn; a split instance needs K/128 >= 2 * splits
+ * and at most 128 MB of fp32 partials).
  */
 int gemm_a8w8_blockscale_run_variant(int32_t variant,
                                      const void *A, const float *a_scale,
