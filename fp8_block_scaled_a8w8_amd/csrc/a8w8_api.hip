@@ -186,7 +186,10 @@ bool stream_workspace(int dev, hipStream_t stream, int64_t bytes, int64_t counte
 // Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
 // with the widest row group that still yields at least ~200 workgroups (wider
 // groups share each activation fragment across more weight tiles), covering
-// K in one pass with the fewest blocks per wave.  Above, for N <= 32: the
+// K in the fewest passes with the most blocks per pass (8 waves x 6 blocks
+// measured fastest at K = 2048..8192); with fewer than 32 row groups, K split
+// four ways over 16-row groups (measured 1.3-1.6x faster at N = 32..256,
+// slower from ~64 groups up).  Above, for N <= 32: the
 // tall kernel (16-row activation groups, 16 waves; 32-row groups from
 // M = 4096).  Otherwise the largest tile that still gives every compute unit
 // at least two workgroups, else the smallest, with K split when even that
@@ -201,14 +204,19 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
             if (v.kernel != A8W8_KERNEL_SKINNY || v.splits > 1)
                 continue;
             const int64_t groups = (N + v.bn - 1) / v.bn;
-            const int64_t passes = a8w8::variant_passes(i, K);
-            // rank: enough workgroups, then one pass, then wider rows, then fewer blocks per pass
-            const int64_t key = (groups >= 200 || v.bn == 16 ? 1 : 0) * 1000000 + (passes == 1 ? 1 : 0) * 100000 +
-                                v.bn * 100 - v.waves * v.kblocks;
+            const int64_t passes = std::min<int64_t>(a8w8::variant_passes(i, K), 99);
+            // rank: enough workgroups, then fewer passes, then wider rows, then more blocks per pass
+            const int64_t key = (groups >= 200 || v.bn == 16 ? 1 : 0) * 100000000 - passes * 1000000 +
+                                v.bn * 1000 + v.waves * v.kblocks;
             if (best < 0 || key > best_key) {
                 best = i;
                 best_key = key;
             }
+        }
+        if (best >= 0 && (N + 15) / 16 < 32) {
+            const int sid = find_variant(A8W8_KERNEL_SKINNY, 16, 16, 4, 3, 4);
+            if (sid >= 0 && variant_accepts(sid, M, N, K))
+                return sid;
         }
         if (best >= 0)
             return best;

@@ -180,6 +180,21 @@ def test_every_m_has_a_tuned_plan_within_125_percent(N, K):
             assert M <= 16
 
 
+def test_heuristic_skinny_rule():
+    # Up to M = 16 on an unregistered (N, K): fewest passes over K, then the deepest
+    # pass (8 waves x 6 blocks); fewer than 32 sixteen-row groups split K four ways.
+    for M, N, K in ((1, 1000, 3072), (16, 640, 4096), (1, 2000, 2048), (16, 3000, 5120), (1, 4096, 4096)):
+        p = g.gemm_a8w8_blockscale_plan(M, N, K)
+        assert p["fallback"] == 1 and p["name"] == "skinny_r1_d6_w8" and p["kpasses"] == 1, (M, N, K, p)
+    for M, N, K in ((8, 128, 8192), (5, 100, 1024), (16, 496, 4096), (1, 32, 3072)):
+        p = g.gemm_a8w8_blockscale_plan(M, N, K)
+        assert p["fallback"] == 1 and p["name"] == "skinny_r1_d3_w4_k4", (M, N, K, p)
+        assert p["grid"] == -(-N // 16) * 4
+    # too few K blocks for four splits (K/128 < 8): unsplit
+    p = g.gemm_a8w8_blockscale_plan(5, 100, 896)
+    assert p["fallback"] == 1 and p["splits"] == 1 and p["kernel_name"] == "skinny"
+
+
 def test_unregistered_shape_falls_back_not_fails():
     p = g.gemm_a8w8_blockscale_plan(3, 1000, 384)
     assert p["fallback"] == 1 and p["kernel_name"] == "skinny"

@@ -219,6 +219,24 @@ def test_integer_valued_inputs_exact():
         assert np.array_equal(y_host(y), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 128, 8192), (5, 100, 1024), (16, 496, 4096), (1, 1000, 3072),
+                                   (3, 2000, 2048), (5, 100, 896)])
+def test_heuristic_skinny_plans(M, N, K):
+    # Unregistered shapes at M <= 16: the heuristic's split and unsplit skinny plans,
+    # full output against the oracle and bitwise repeatable.
+    plan = g.gemm_a8w8_blockscale_plan(M, N, K)
+    assert plan["fallback"] == 1 and plan["kernel_name"] == "skinny"
+    A, a_s = inputgen.make_activations(M, K, seed=M + N)
+    W, w_s = inputgen.make_weights(N, K, seed=K)
+    dA, da, dW, dw = to_dev(A, a_s, W, w_s)
+    say(f"heuristic {plan['name']} M={M} N={N} K={K}")
+    y = g.gemm_a8w8_blockscale(dA, da, dW, dw)
+    first = y_bits(y).copy()
+    assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"heuristic {plan['name']}")
+    for _ in range(2):
+        assert np.array_equal(y_bits(g.gemm_a8w8_blockscale(dA, da, dW, dw)), first)
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 5120, 6144), (300, 1000, 1024)])
 def test_doubling_activation_scales_doubles_output(M, N, K):
     A, a_s, W, w_s = _inputs(M, N, K)
