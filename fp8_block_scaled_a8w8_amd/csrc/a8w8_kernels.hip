@@ -216,6 +216,8 @@ __device__ __forceinline__ void store4(uint16_t *Y, int64_t row_off, int n, int 
 // feeds TPW MFMAs.  Per block: one MFMA per tile, then one FMA per output with
 // a_scale * w_scale.  The NW wave partials of each tile are summed through LDS
 // in wave order (fixed order: bitwise deterministic), rounded once to bf16.
+// Split instances (SK) give each of S workgroups per row group 1/S of K and
+// combine their sums through the workspace in split order before rounding.
 //
 // Weight loads cover whole 128-byte lines: load 0 of a block takes rows 0-7 of
 // the 16-row tile and load 1 rows 8-15, lane (rho = l/16, p = l%16) reading
