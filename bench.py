@@ -142,6 +142,39 @@ def timed_replays(torch, graph, n):
     return t0.elapsed_time(t1) / n
 
 
+def read_ceiling_block(torch, dev, nbytes, R, replays, us_decode):
+    """The part's streaming-read ceiling at the decode's byte count: a plain read kernel
+    (fp8_block_scaled_a8w8_amd/csrc/read_ceiling.hip) over R rotated buffers of `nbytes`,
+    timed like the GEMM (one HIP graph of R launches), best of a few grids."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "libread_ceiling.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.a8w8_read_ceiling_launch
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    best = None
+    for grid in (512, 1024, 2048, 4096):
+        sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+        for unroll in (8, 16):
+            def launch(b, grid=grid, unroll=unroll, sink=sink):
+                rc = fn(b.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"read_ceiling launch failed ({rc})")
+            graph = time_graph(torch, [(lambda b=b: launch(b)) for b in bufs], 0, 2)
+            us = timed_replays(torch, graph, replays) * 1000.0 / R
+            del graph
+            if best is None or us < best[0]:
+                best = (us, grid, unroll)
+    del bufs
+    us, grid, unroll = best
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bytes": nbytes, "us": round(us, 3), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "config": f"{grid} workgroups x 256 lanes, {unroll} 16-byte loads per lane in flight, {R} rotated buffers",
+            "decode_frac_of_ceiling": round(us / us_decode, 4)}
+
+
 def quantize_bytes(M: int, K: int) -> int:
     """Algorithmic bytes of the activation quantisation: bf16 in, e4m3fn codes and fp32 scales out."""
     return 2 * M * K + M * K + 4 * M * (K // 128)
@@ -371,6 +404,10 @@ def main():
         del gm
     log("per-M:", json.dumps(per_m))
 
+    # the part's streaming-read ceiling at the same bytes per call
+    ceiling = read_ceiling_block(torch, dev, round(bytes_mean), R, max(5, args.steps // 10), us_per_call)
+    log("read ceiling:", json.dumps(ceiling))
+
     # the same workload with the weights prepacked offline (a8w8_prepack_weights)
     pcopies = [g.prepack_weights(c) for c in copies]
     for r in (0, R - 1):                                  # bitwise the same as the row-major call
@@ -489,6 +526,7 @@ def main():
                                + ", ".join(sorted({v["plan"] for v in per_m.values()})),
                      "bytes_per_launch": round(bytes_mean)},
         "per_m": per_m,
+        "read_ceiling": ceiling,
         "prepacked_weights": packed,
         "prefill": prefill,
         "quantize": quant,

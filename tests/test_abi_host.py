@@ -343,3 +343,22 @@ def test_split_instances_beyond_the_workspace_cap_are_rejected():
 def test_plans_report_splits():
     for M, N, K in ((1, 14336, 5120), (8192, 14336, 5120)):
         assert g.gemm_a8w8_blockscale_plan(M, N, K)["splits"] >= 1
+
+
+# ---------------------------------------------------------------- benchmark read-ceiling kernel
+
+def test_read_ceiling_library_builds_and_checks_arguments():
+    # The benchmark's streaming-read kernel lives in a library of its own; bad arguments are
+    # refused before anything is launched.
+    import ctypes
+    import os
+    from fp8_block_scaled_a8w8_amd import build as libbuild
+    if not os.path.exists(libbuild.READ_CEILING_LIB):
+        libbuild.build_read_ceiling()
+    lib = ctypes.CDLL(libbuild.READ_CEILING_LIB)
+    fn = lib.a8w8_read_ceiling_launch
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    for args in ((16, 1000, 16, 8, 8), (16, 1024, None, 8, 8), (None, 1024, 16, 8, 8), (16, 1024, 16, 0, 8),
+                 (16, 1024, 16, 8, 4), (16, 0, 16, 8, 16)):
+        assert fn(*args, None) != 0, args
