@@ -104,9 +104,8 @@ _SIDE_STREAM = None
 
 
 def time_graph(torch, calls, replays, warmup):
-    """Capture `calls` (list of zero-arg callables) into one HIP graph (after one eager pass on the
-    capture stream, which also gives split-K plans their per-stream workspace); returns the graph.
-    One side stream serves every capture, so the library keeps one workspace for all of them."""
+    """Capture `calls` (list of zero-arg callables) into one HIP graph on a side stream, after one
+    eager pass of them there (warm-up); returns the graph after `warmup` replays."""
     global _SIDE_STREAM
     if _SIDE_STREAM is None:
         _SIDE_STREAM = torch.cuda.Stream()
@@ -229,7 +228,8 @@ def mx_block(torch, g, inputgen, oracle, dev, replays):
         copies = [torch.from_numpy(W0).to(dev)] + \
             [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
         fn = g.batched_gemm_a8w8_mxscale if b > 1 else g.gemm_a8w8_mxscale
-        y = fn(dA, da, copies[-1], dw)
+        ws = g.Workspace(b * (64 << 20))
+        y = fn(dA, da, copies[-1], dw, workspace=ws)
         torch.cuda.synchronize()
         W_last = inputgen.sign_flip_copy(W0, seed=1000 + R - 1)
         rows = sorted({0, M // 2, M - 1})
@@ -243,11 +243,11 @@ def mx_block(torch, g, inputgen, oracle, dev, replays):
                 raise SystemExit(f"parity gate failed (MX b={b} M={M} N={N} K={K}): rel_l2={rel:.3e}")
             worst = max(worst, rel)
         yo = torch.empty_like(y)
-        gr = time_graph(torch, [(lambda r=r: fn(dA, da, copies[r], dw, out=yo)) for r in range(R)], 0, 2)
+        gr = time_graph(torch, [(lambda r=r: fn(dA, da, copies[r], dw, out=yo, workspace=ws)) for r in range(R)], 0, 2)
         us = timed_replays(torch, gr, replays) * 1000.0 / R
         t_hbm = mx_bytes(b, M, N, K) / (HBM_PEAK_GBS * 1e9) * 1e6
         t_mfma = b * flops(M, N, K) / (FP8_PEAK_TFLOPS * 1e12) * 1e6
-        plan = g.gemm_a8w8_mxscale_plan(M, N, K)
+        plan = g.gemm_a8w8_ex_plan(M, N, K, scale_kind="mx", batch=b, workspace_bytes=ws.nbytes)
         out[f"b{b}_M{M}_N{N}_K{K}"] = {
             "us_per_call": round(us, 3), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
             "frac": round(max(t_hbm, t_mfma) / us, 4),
@@ -255,7 +255,7 @@ def mx_block(torch, g, inputgen, oracle, dev, replays):
             "TFLOP_s": round(b * flops(M, N, K) / (us * 1e-6) / 1e12, 1),
             "plan": plan["name"], "tuned": plan["fallback"] == 0, "weight_copies": R,
             "parity_rel_l2": round(worst, 6)}
-        del gr, copies
+        del gr, copies, ws
         torch.cuda.empty_cache()
     return out
 
@@ -575,8 +575,9 @@ def sweep(args, torch, g, inputgen, oracle):
         copies = [torch.from_numpy(W0).to(dev)] + \
             [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
         picked = []
+        ws = g.Workspace(64 << 20)
         for M in Ms:
-            plan = g.gemm_a8w8_blockscale_plan(M, N, K)
+            plan = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=ws.nbytes)
             fallbacks += plan["fallback"]
             worst_ratio = max(worst_ratio, plan["key_m"] / M)
             # long calls need no rotation to be cold: cap the graph at ~20 ms of work
@@ -584,13 +585,14 @@ def sweep(args, torch, g, inputgen, oracle):
             est_us = max(algorithmic_bytes(M, N, K) / 6e3, fl / 2e9)
             Rp = max(2, min(R, int(20000 / max(est_us, 1.0))))
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            gr = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw, out=out))
+            gr = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw, out=out,
+                                                                        workspace=ws))
                                     for r in range(Rp)], 0, 1)
             reps = max(2, int(5000 / (est_us * Rp)))
             us = timed_replays(torch, gr, reps) * 1000.0 / Rp
             del gr
             # the graph's last call used a rotated copy: recompute with copy 0 for the parity check
-            g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[0], dw, out=out)
+            g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[0], dw, out=out, workspace=ws)
             rows = sorted({M - 1, int(rng.integers(0, M))})
             picked.append((M, rows, out[rows].float().cpu().numpy().astype(np.float64)))
             by = algorithmic_bytes(M, N, K)

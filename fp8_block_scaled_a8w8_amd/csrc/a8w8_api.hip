@@ -17,10 +17,10 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
 #include <mutex>
 #include <set>
 #include <tuple>
@@ -41,7 +41,7 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 // Batches are the grid's y dimension.
 constexpr int64_t kMaxBatch = 65535;
-// Largest split-K workspace (fp32 partial tiles) one stream may hold.
+// Largest fp32 partial-tile area one split-K launch may use (per batch).
 constexpr int64_t kMaxWorkspace = (int64_t)128 << 20;
 
 // Per-device state: 0 = not yet checked, 1 = gfx950 ready, 2 = unsupported.
@@ -137,64 +137,41 @@ int find_variant(int kernel, int bm, int bn, int waves, int kblocks, int splits 
     return -1;
 }
 
-// Split-K workspace of one (device, stream): fp32 partial tiles and the
-// per-tile counters, which start at zero and are reset by the last split of
-// each tile.  One per stream, so calls on different streams never share one;
-// calls on one stream run in order.
-struct Workspace {
-    float *buf = nullptr;
-    int64_t bytes = 0;
-    int32_t *cnt = nullptr;
-    int64_t counters = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+// Split-K workspace.  A split instance runs S workgroups per output tile;
+// they meet through caller-owned device memory laid out as
+//   [counters: kCounterBytes, one int32 per (batch, tile) from the start][fp32 partials]
+// (partials [batch][tile][split][BM * BN]).  The counter area has the same
+// size and place for every call, so calls of different shapes and plans can
+// share a workspace: every counter is zero when a call starts, and every split
+// call leaves the counters it used zero again (the last split of a tile resets
+// its counter), so a workspace cleared once with gemm_a8w8_workspace_init
+// serves any number of calls in stream order.  Partials need no clearing.
+constexpr int64_t kCounterBytes = A8W8_WORKSPACE_COUNTER_BYTES;
 
-// The calling stream's workspace with room for `bytes` and `counters`,
-// allocated (or replaced by a larger one) here -- only while the stream is not
-// capturing a graph.  A replaced workspace is retired, never freed: graphs
-// captured earlier keep using it.  Returns false when no suitable workspace
-// can be had; the caller then runs the unsplit instance.
-bool stream_workspace(int dev, hipStream_t stream, int64_t bytes, int64_t counters, float **ws, int32_t **cnt)
+// Workspace bytes instance `id` needs for `batch` problems of (M, N): 0 when
+// it splits no K; INT64_MAX when its counters do not fit the counter area.
+int64_t workspace_need(int id, int64_t M, int64_t N, int64_t batch)
 {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
-    if (w.bytes < bytes || w.counters < counters) {
-        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone)
-            return false;
-        const int64_t nb = std::max<int64_t>(std::max<int64_t>(bytes, 2 * w.bytes), (int64_t)32 << 20);
-        const int64_t nc = std::max<int64_t>(std::max<int64_t>(counters, 2 * w.counters), (int64_t)1 << 15);
-        void *b = nullptr, *c = nullptr;
-        if (hipMalloc(&b, (size_t)std::min(nb, kMaxWorkspace)) != hipSuccess || hipMalloc(&c, (size_t)nc * 4) != hipSuccess ||
-            hipMemsetAsync(c, 0, (size_t)nc * 4, stream) != hipSuccess) {
-            (void)hipGetLastError();
-            (void)hipFree(b);
-            (void)hipFree(c);
-            return false;
-        }
-        w.buf = static_cast<float *>(b);          // the previous buffers (if any) stay allocated
-        w.bytes = std::min(nb, kMaxWorkspace);
-        w.cnt = static_cast<int32_t *>(c);
-        w.counters = nc;
-    }
-    *ws = w.buf;
-    *cnt = w.cnt;
-    return true;
+    if (a8w8::variant(id).splits <= 1)
+        return 0;
+    if (batch * a8w8::variant_counters(id, M, N) * 4 > kCounterBytes)
+        return INT64_MAX;
+    return kCounterBytes + batch * a8w8::variant_workspace_bytes(id, M, N);
 }
 
 // Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
 // with the widest row group that still yields at least ~200 workgroups (wider
 // groups share each activation fragment across more weight tiles), covering
 // K in the fewest passes with the most blocks per pass (8 waves x 6 blocks
-// measured fastest at K = 2048..8192); with fewer than 32 row groups, K split
-// four ways over 16-row groups (measured 1.3-1.6x faster at N = 32..256,
-// slower from ~64 groups up).  Above, for N <= 32: the
+// measured fastest at K = 2048..8192); with fewer than 32 row groups and a
+// split-K workspace, K split four ways over 16-row groups (measured 1.3-1.6x
+// faster at N = 32..256, slower from ~64 groups up).  Above, for N <= 32: the
 // tall kernel (16-row activation groups, 16 waves; 32-row groups from
 // M = 4096).  Otherwise the largest tile that still gives every compute unit
-// at least two workgroups, else the smallest, with K split when even that
-// leaves compute units idle.
-int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
+// at least two workgroups, else the smallest, with K split (given a
+// workspace) when even that leaves compute units idle.  Returns the plan with
+// split K allowed in *split and the one without in *unsplit.
+void heuristic_variants(int64_t M, int64_t N, int64_t K, int cus, int *split, int *unsplit)
 {
     if (M <= 16 && skinny_fits(N, K)) {
         int best = -1;
@@ -213,20 +190,24 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
                 best_key = key;
             }
         }
-        if (best >= 0 && (N + 15) / 16 < 32) {
-            const int sid = find_variant(A8W8_KERNEL_SKINNY, 16, 16, 4, 3, 4);
-            if (sid >= 0 && variant_accepts(sid, M, N, K))
-                return sid;
+        if (best >= 0) {
+            *split = *unsplit = best;
+            if ((N + 15) / 16 < 32) {
+                const int sid = find_variant(A8W8_KERNEL_SKINNY, 16, 16, 4, 3, 4);
+                if (sid >= 0 && variant_accepts(sid, M, N, K))
+                    *split = sid;
+            }
+            return;
         }
-        if (best >= 0)
-            return best;
     }
     if (N <= 32 && skinny_fits(N, K) && skinny_fits(M, K)) {
         const int bn = N <= 16 ? 16 : 32;
         const int id = M < 4096 ? find_variant(A8W8_KERNEL_TALL, 16, bn, bn == 32 ? 16 : 8, 3)
                                 : find_variant(A8W8_KERNEL_TALL, 32, bn, 8, bn == 32 ? 6 : 3);
-        if (id >= 0)
-            return id;
+        if (id >= 0) {
+            *split = *unsplit = id;
+            return;
+        }
     }
     static const int kTiles[][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}, {32, 64}, {32, 32}};
     const int nt = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
@@ -235,8 +216,10 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
         if (N <= 32 && bn > 32)
             continue;
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-        if (tiles >= 2 * (int64_t)cus)
-            return find_variant(A8W8_KERNEL_TILE, bm, bn, 0, 0);
+        if (tiles >= 2 * (int64_t)cus) {
+            *split = *unsplit = find_variant(A8W8_KERNEL_TILE, bm, bn, 0, 0);
+            return;
+        }
     }
     // Fewer tiles than two per CU even at 32 x 32: split K over S workgroups per tile,
     // the smallest S (2, 4, 8) that gives every CU a workgroup, keeping >= 4 K blocks
@@ -244,18 +227,17 @@ int heuristic_variant(int64_t M, int64_t N, int64_t K, int cus)
     const int base = find_variant(A8W8_KERNEL_TILE, 32, 32, 0, 0);
     const Variant &bv = a8w8::variant(base);
     const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
-    int best = base;
+    *unsplit = *split = base;
     for (int s : {2, 4, 8}) {
         if (K / 128 < 4 * (int64_t)s)
             break;
         const int sid = find_variant(A8W8_KERNEL_TILE, 32, 32, bv.waves, bv.kblocks, s);
         if (sid < 0 || !variant_accepts(sid, M, N, K))
             continue;
-        best = sid;
+        *split = sid;
         if (tiles * s >= cus)
             break;
     }
-    return best;
 }
 
 struct Choice {
@@ -264,7 +246,10 @@ struct Choice {
     int fallback;
 };
 
-Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx)
+// The instance serving (M, N, K): the fastest one of the table row (or of the
+// heuristic), or -- when the call brings less workspace than that instance
+// needs for `batch` problems -- the fastest one that splits no K.
+Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t batch, int64_t ws_bytes)
 {
     using namespace a8w8_table;
     for (int t = 0; t < kNumShapes; ++t) {
@@ -282,15 +267,21 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx)
         }
         if (lo < s.count) {
             const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo], s.kblocks[lo], s.splits[lo]);
-            if (v >= 0 && variant_accepts(v, M, N, K))
+            if (v >= 0 && variant_accepts(v, M, N, K) && workspace_need(v, M, N, batch) <= ws_bytes)
                 return {v, s.key_m[lo], 0};
+            const int u = find_variant(s.u_kernel[lo], s.u_bm[lo], s.u_bn[lo], s.u_waves[lo], s.u_kblocks[lo], 1);
+            if (u >= 0 && variant_accepts(u, M, N, K))
+                return {u, s.key_m[lo], 0};
         }
         break;
     }
-    return {heuristic_variant(M, N, K, cus), M, 1};
+    int split = -1, unsplit = -1;
+    heuristic_variants(M, N, K, cus, &split, &unsplit);
+    return {workspace_need(split, M, N, batch) <= ws_bytes ? split : unsplit, M, 1};
 }
 
-void fill_plan(int id, int64_t M, int64_t N, int64_t K, int cus, int64_t key_m, int fallback, a8w8_plan *out)
+void fill_plan(int id, int64_t M, int64_t N, int64_t K, int64_t batch, int cus, int64_t key_m, int fallback,
+               a8w8_plan *out)
 {
     const Variant &v = a8w8::variant(id);
     std::memset(out, 0, sizeof(*out));
@@ -305,6 +296,7 @@ void fill_plan(int id, int64_t M, int64_t N, int64_t K, int cus, int64_t key_m, 
     out->key_m = key_m;
     out->fallback = fallback;
     out->splits = v.splits;
+    out->workspace = M > 0 ? workspace_need(id, M, N, batch > 0 ? batch : 1) : 0;
 }
 
 // GEMM_A8W8_LOG=1: one stderr line per distinct (M, N, K) with the plan used.
@@ -325,7 +317,8 @@ void log_plan(int64_t M, int64_t N, int64_t K, int id, int64_t key_m, int fallba
                  (long long)K, a8w8::variant(id).name, (long long)key_m, fallback ? " fallback" : "");
 }
 
-// Operand set of one call: `batch` consecutive problems of one shape.
+// Operand set of one call: `batch` consecutive problems of one shape, and the
+// split-K workspace it brings (NULL / 0: none).
 struct Operands {
     const void *A;
     const void *a_scale;
@@ -335,6 +328,8 @@ struct Operands {
     int64_t batch;
     int wpk;   // W in the packed layout
     int sm;    // scale kind: 0 fp32 block scales, 1 MX (E8M0), 2 row-wise fp32
+    void *ws;
+    int64_t ws_bytes;
 };
 
 // Elements of each array per batch (scale arrays in 32-bit words: an MX row of
@@ -352,20 +347,19 @@ void batch_strides(const Operands &o, int64_t M, int64_t N, int64_t K, Args &a)
     a.bs_y = M * N;
 }
 
+// Enqueue instance `id` exactly as planned: a split instance takes its
+// counters and partials from the call's workspace (the caller checked that it
+// is large enough).
 int launch(int id, const Operands &o, int64_t M, int64_t N, int64_t K, int cus, void *stream)
 {
     Args a;
-    a.splits = 1;
+    a.splits = a8w8::variant(id).splits;
     a.ws = nullptr;
     a.cnt = nullptr;
-    if (a8w8::variant(id).splits > 1) {
-        int dev = 0;
-        const int64_t bytes = o.batch * a8w8::variant_workspace_bytes(id, M, N);
-        const int64_t counters = o.batch * a8w8::variant_counters(id, M, N);
-        if (hipGetDevice(&dev) == hipSuccess && bytes <= kMaxWorkspace &&
-            stream_workspace(dev, static_cast<hipStream_t>(stream), bytes, counters, &a.ws, &a.cnt))
-            a.splits = a8w8::variant(id).splits;
-        // else the instance runs unsplit: one workgroup per tile, no workspace.
+    if (a.splits > 1) {
+        uint8_t *base = static_cast<uint8_t *>(o.ws);
+        a.cnt = reinterpret_cast<int32_t *>(base);
+        a.ws = reinterpret_cast<float *>(base + kCounterBytes);
     }
     a.A = static_cast<const uint8_t *>(o.A);
     a.a_scale = static_cast<const float *>(o.a_scale);
@@ -391,45 +385,44 @@ int check_call(const Operands &o, int64_t M, int64_t N, int64_t K)
         return rc;
     if (o.batch < 0 || o.batch > kMaxBatch)
         return A8W8_ERR_SHAPE;
+    if (o.sm < 0 || o.sm > 2 || o.wpk < 0 || o.wpk > 1)
+        return A8W8_ERR_SHAPE;
     // MX weight-scale rows (one per 32 weight rows): the pskinny kernel's
     // descriptor spans them in 32 bits, the kernels index them in 31.
     if (o.sm == 1 && (N + 31) / 32 * (K / 128) * 4 >= ((int64_t)1 << 31))
         return A8W8_ERR_SHAPE;
+    if (o.ws_bytes < 0)
+        return A8W8_ERR_WORKSPACE;
     return A8W8_OK;
 }
 
-int gemm_impl(const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
+// The workspace argument of a call (planning looks at its size only).
+int check_workspace(const Operands &o)
 {
-    int rc = check_call(o, M, N, K);
-    if (rc != A8W8_OK)
-        return rc;
-    if (M == 0 || o.batch == 0)
-        return A8W8_OK;
-    rc = check_pointers(o.A, o.a_scale, o.W, o.w_scale, o.Y);
-    if (rc != A8W8_OK)
-        return rc;
-    int cus = 0;
-    rc = device_ready(&cus);
-    if (rc != A8W8_OK)
-        return rc;
-    // Row-wise calls use the block-scale tables: same kernels and loads, less
-    // scale work per block.
-    const Choice c = select_variant(M, N, K, cus, o.sm == 1 ? 1 : 0);
-    log_plan(M, N, K, c.variant, c.key_m, c.fallback);
-    return launch(c.variant, o, M, N, K, cus, stream);
+    if (o.ws_bytes > 0 && o.ws == nullptr)
+        return A8W8_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(o.ws) & 255)
+        return A8W8_ERR_ALIGN;
+    return A8W8_OK;
 }
 
-int run_variant_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
+// `variant` < 0: the selector's plan; otherwise that instance, which must
+// accept the shape and find the workspace it needs.
+int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t K, void *stream)
 {
-    if (variant < 0 || variant >= a8w8::num_variants())
+    if (variant >= a8w8::num_variants())
         return A8W8_ERR_PLAN;
     int rc = check_call(o, M, N, K);
+    if (rc == A8W8_OK)
+        rc = check_workspace(o);
     if (rc != A8W8_OK)
         return rc;
     if (M == 0 || o.batch == 0)
         return A8W8_OK;
-    if (!variant_accepts(variant, M, N, K))
+    if (variant >= 0 && !variant_accepts(variant, M, N, K))
         return A8W8_ERR_PLAN;
+    if (variant >= 0 && workspace_need(variant, M, N, o.batch) > o.ws_bytes)
+        return A8W8_ERR_WORKSPACE;
     rc = check_pointers(o.A, o.a_scale, o.W, o.w_scale, o.Y);
     if (rc != A8W8_OK)
         return rc;
@@ -437,7 +430,52 @@ int run_variant_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, i
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
-    return launch(variant, o, M, N, K, cus, stream);
+    int id = variant;
+    if (id < 0) {
+        // Row-wise calls use the block-scale tables: same kernels and loads, less
+        // scale work per block.
+        const Choice c = select_variant(M, N, K, cus, o.sm == 1 ? 1 : 0, o.batch, o.ws_bytes);
+        log_plan(M, N, K, c.variant, c.key_m, c.fallback);
+        id = c.variant;
+    }
+    if (workspace_need(id, M, N, o.batch) > o.ws_bytes)
+        return A8W8_ERR_WORKSPACE;
+    return launch(id, o, M, N, K, cus, stream);
+}
+
+int plan_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
+{
+    if (!out)
+        return A8W8_ERR_NULL;
+    if (variant >= a8w8::num_variants())
+        return A8W8_ERR_PLAN;
+    int rc = check_call(o, M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    const int cus = cu_count > 0 ? cu_count : 256;
+    const int64_t Mp = M > 0 ? M : 1, batch = o.batch > 0 ? o.batch : 1;
+    if (variant >= 0) {
+        if (!variant_accepts(variant, Mp, N, K))
+            return A8W8_ERR_PLAN;
+        if (workspace_need(variant, Mp, N, batch) > o.ws_bytes)
+            return A8W8_ERR_WORKSPACE;
+        fill_plan(variant, M, N, K, batch, cus, M, 0, out);
+        return A8W8_OK;
+    }
+    const Choice c = select_variant(Mp, N, K, cus, o.sm == 1 ? 1 : 0, batch, o.ws_bytes);
+    fill_plan(c.variant, M, N, K, batch, cus, c.key_m, c.fallback, out);
+    return A8W8_OK;
+}
+
+Operands from_desc(const a8w8_gemm_desc &d)
+{
+    return {d.A, d.a_scale, d.W, d.w_scale, d.Y, d.batch, d.w_packed, d.scale_kind, d.workspace, d.workspace_bytes};
+}
+
+__global__ void workspace_clear_kernel(uint4 *p, int64_t n16)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 }  // namespace
@@ -447,89 +485,113 @@ extern "C" {
 int gemm_a8w8_blockscale(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
                          int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, W, w_scale, Y, 1, 0, 0}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, W, w_scale, Y, 1, 0, 0, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_blockscale_packed(const void *A, const float *a_scale, const void *Wp, const float *w_scale, void *Y,
                                 int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, Wp, w_scale, Y, 1, 1, 0}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, Wp, w_scale, Y, 1, 1, 0, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_mxscale(const void *A, const void *a_scale, const void *W, const void *w_scale, void *Y, int64_t M,
                       int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, W, w_scale, Y, 1, 0, 1}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, W, w_scale, Y, 1, 0, 1, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_mxscale_packed(const void *A, const void *a_scale, const void *Wp, const void *w_scale, void *Y,
                              int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, Wp, w_scale, Y, 1, 1, 1}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, Wp, w_scale, Y, 1, 1, 1, nullptr, 0}, M, N, K, stream);
 }
 
 int batched_gemm_a8w8_mxscale(const void *A, const void *a_scale, const void *W, const void *w_scale, void *Y,
                               int64_t batch, int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, W, w_scale, Y, batch, 0, 1}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, W, w_scale, Y, batch, 0, 1, nullptr, 0}, M, N, K, stream);
 }
 
 int batched_gemm_a8w8_mxscale_packed(const void *A, const void *a_scale, const void *Wp, const void *w_scale,
                                      void *Y, int64_t batch, int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, Wp, w_scale, Y, batch, 1, 1}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, Wp, w_scale, Y, batch, 1, 1, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_mxscale_run_variant(int32_t variant, const void *A, const void *a_scale, const void *W,
                                   const void *w_scale, void *Y, int64_t batch, int64_t M, int64_t N, int64_t K,
                                   int32_t w_packed, void *stream)
 {
-    return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, batch, w_packed ? 1 : 0, 1}, M, N, K, stream);
+    if (variant < 0)
+        return A8W8_ERR_PLAN;
+    return gemm_impl(variant, {A, a_scale, W, w_scale, Y, batch, w_packed ? 1 : 0, 1, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_rowwise(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
                       int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, W, w_scale, Y, 1, 0, 2}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, W, w_scale, Y, 1, 0, 2, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_rowwise_packed(const void *A, const float *a_scale, const void *Wp, const float *w_scale, void *Y,
                              int64_t M, int64_t N, int64_t K, void *stream)
 {
-    return gemm_impl({A, a_scale, Wp, w_scale, Y, 1, 1, 2}, M, N, K, stream);
+    return gemm_impl(-1, {A, a_scale, Wp, w_scale, Y, 1, 1, 2, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_rowwise_run_variant(int32_t variant, const void *A, const float *a_scale, const void *W,
                                   const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K, int32_t w_packed,
                                   void *stream)
 {
-    return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, 1, w_packed ? 1 : 0, 2}, M, N, K, stream);
+    if (variant < 0)
+        return A8W8_ERR_PLAN;
+    return gemm_impl(variant, {A, a_scale, W, w_scale, Y, 1, w_packed ? 1 : 0, 2, nullptr, 0}, M, N, K, stream);
+}
+
+int gemm_a8w8_ex(const a8w8_gemm_desc *desc, void *stream)
+{
+    if (!desc)
+        return A8W8_ERR_NULL;
+    return gemm_impl(desc->variant < 0 ? -1 : desc->variant, from_desc(*desc), desc->M, desc->N, desc->K, stream);
+}
+
+int gemm_a8w8_ex_plan(const a8w8_gemm_desc *desc, int32_t cu_count, a8w8_plan *out)
+{
+    if (!desc)
+        return A8W8_ERR_NULL;
+    const Operands o = from_desc(*desc);   // planning looks at the workspace size only
+    return plan_impl(desc->variant < 0 ? -1 : desc->variant, o, desc->M, desc->N, desc->K, cu_count, out);
+}
+
+int gemm_a8w8_workspace_init(void *workspace, int64_t bytes, void *stream)
+{
+    if (bytes < 0)
+        return A8W8_ERR_SHAPE;
+    if (bytes == 0)
+        return A8W8_OK;
+    if (!workspace)
+        return A8W8_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) || (bytes & 255))
+        return A8W8_ERR_ALIGN;
+    int cus = 0;
+    const int rc = device_ready(&cus);
+    if (rc != A8W8_OK)
+        return rc;
+    const int64_t n16 = bytes / 16;
+    const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, (int64_t)cus * 8);
+    hipLaunchKernelGGL(workspace_clear_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint4 *>(workspace), n16);
+    return hipGetLastError() == hipSuccess ? A8W8_OK : A8W8_ERR_HIP;
 }
 
 int gemm_a8w8_mxscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
 {
-    if (!out)
-        return A8W8_ERR_NULL;
-    const int rc = check_call({nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0, 1}, M, N, K);
-    if (rc != A8W8_OK)
-        return rc;
-    const int cus = cu_count > 0 ? cu_count : 256;
-    const Choice c = select_variant(M > 0 ? M : 1, N, K, cus, 1);
-    fill_plan(c.variant, M, N, K, cus, c.key_m, c.fallback, out);
-    return A8W8_OK;
+    return plan_impl(-1, {nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0, 1, nullptr, 0}, M, N, K, cu_count, out);
 }
 
 int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)
 {
-    if (!out)
-        return A8W8_ERR_NULL;
-    const int rc = check_shape(M, N, K);
-    if (rc != A8W8_OK)
-        return rc;
-    const int cus = cu_count > 0 ? cu_count : 256;
-    const Choice c = select_variant(M > 0 ? M : 1, N, K, cus, 0);
-    fill_plan(c.variant, M, N, K, cus, c.key_m, c.fallback, out);
-    return A8W8_OK;
+    return plan_impl(-1, {nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0, 0, nullptr, 0}, M, N, K, cu_count, out);
 }
 
 int gemm_a8w8_num_variants(void) { return a8w8::num_variants(); }
@@ -542,7 +604,7 @@ int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
         return A8W8_ERR_PLAN;
     if (M < 0 || N < 1 || K < 1)
         return A8W8_ERR_SHAPE;
-    fill_plan(variant, M, N, K, 256, M, 0, out);
+    fill_plan(variant, M, N, K, 1, 256, M, 0, out);
     return A8W8_OK;
 }
 
@@ -550,14 +612,18 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant, const void *A, const float
                                      const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
                                      void *stream)
 {
-    return run_variant_impl(variant, {A, a_scale, W, w_scale, Y, 1, 0, 0}, M, N, K, stream);
+    if (variant < 0)
+        return A8W8_ERR_PLAN;
+    return gemm_impl(variant, {A, a_scale, W, w_scale, Y, 1, 0, 0, nullptr, 0}, M, N, K, stream);
 }
 
 int gemm_a8w8_blockscale_packed_run_variant(int32_t variant, const void *A, const float *a_scale, const void *Wp,
                                             const float *w_scale, void *Y, int64_t M, int64_t N, int64_t K,
                                             void *stream)
 {
-    return run_variant_impl(variant, {A, a_scale, Wp, w_scale, Y, 1, 1, 0}, M, N, K, stream);
+    if (variant < 0)
+        return A8W8_ERR_PLAN;
+    return gemm_impl(variant, {A, a_scale, Wp, w_scale, Y, 1, 1, 0, nullptr, 0}, M, N, K, stream);
 }
 
 int a8w8_prepack_weights(const void *W, void *Wp, int64_t N, int64_t K, void *stream)
@@ -590,10 +656,11 @@ const char *gemm_a8w8_status_string(int status)
     case A8W8_OK: return "ok";
     case A8W8_ERR_NULL: return "a required pointer is NULL";
     case A8W8_ERR_SHAPE: return "invalid shape (need M >= 0, N >= 1, K >= 1, K % 128 == 0, M, N <= 2^30, K <= 2^22, 0 <= batch <= 65535)";
-    case A8W8_ERR_ALIGN: return "misaligned buffer (A and W need 16 bytes, scales 4, Y 2)";
+    case A8W8_ERR_ALIGN: return "misaligned buffer (A and W need 16 bytes, scales 4, Y 2, a split-K workspace 256)";
     case A8W8_ERR_ARCH: return "the current device is not gfx950 (MI355X)";
     case A8W8_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case A8W8_ERR_PLAN: return "invalid kernel instance for this shape";
+    case A8W8_ERR_WORKSPACE: return "the kernel instance splits K and the call's workspace is missing or too small";
     default: return "unknown status";
     }
 }

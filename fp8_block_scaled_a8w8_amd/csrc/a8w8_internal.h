@@ -32,7 +32,7 @@ struct Args {
     // Batched calls: gridDim.y batches; batch z reads A + z * bs_a, a_scale + z * bs_as,
     // W + z * bs_w, w_scale + z * bs_ws and writes Y + z * bs_y (elements of each array).
     int64_t bs_a, bs_as, bs_w, bs_ws, bs_y;
-    // Split K (tile kernel): splits per tile; the calling stream's workspace for the
+    // Split K (split instances): splits per tile; the call's workspace for the
     // fp32 partial tiles [batch][tile][split][BM * BN] and one zeroed counter per
     // [batch][tile] (the last split of a tile resets it).
     int32_t splits;

@@ -1349,7 +1349,7 @@ __device__ __forceinline__ void group_tile(int t, int tiles_m, int tiles_n, int 
 // chip): the grid holds S workgroups per tile -- work item t = S * tile + s,
 // XCD-contiguous as above, so a tile's splits mostly share one L2 -- and split
 // s walks K blocks [s KB / S, (s + 1) KB / S).  Each writes its fp32 partial
-// tile to the stream's workspace with device-scope stores, waits for them to
+// tile to the call's workspace with device-scope stores, waits for them to
 // complete and counts itself in the tile's counter;
 // the last of the S to arrive sums the S partials in split order 0, 1, ...
 // (a fixed order whatever the arrival order, so the result is bitwise
@@ -1759,11 +1759,11 @@ hipError_t set_kernel_attributes()
 hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t stream)
 {
     const Entry &e = kEntries[id];
-    // A split instance run with fewer splits (a.splits, 1 when no workspace
-    // could be had) launches that many workgroups per tile.
-    int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
-    if (e.v.splits > 1)
-        grid = grid / e.v.splits * a.splits;
+    // A split instance always runs with its own split count (the host gives it
+    // the workspace that needs); the kernels read the count from a.splits.
+    if (a.splits != e.v.splits)
+        return hipErrorInvalidValue;
+    const int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
     // The kernels number workgroups and tiles in 32 bits (and the x dimension of a
     // grid is limited to 2^31 - 1): refuse, never truncate, a larger grid.
     if (grid < 1 || grid > 0x7fffffff)

@@ -38,7 +38,7 @@ import time
 
 import torch
 
-from . import gemm_a8w8_blockscale_run_variant, gemm_a8w8_mxscale_run_variant, variants
+from . import Workspace, gemm_a8w8_ex, variants
 from . import gen_selector_table as gst
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +57,33 @@ MX_EXTRA_KEYS = (48, 768)
 # best instance can change sharply inside one 1.25x interval of the mid-M band
 # (tile-count quantisation), so the finer grid serves every M with a row tuned closer to it.
 KEY_RATIO = 1.125
+
+# An unsplit instance within this fraction of the fastest wins the row; a new pick must beat the
+# production row by more than this in both re-measurements.
+SPLIT_PREFERENCE = 0.02
+REPLACE_MARGIN = 0.02
+ROW_FIELDS = ("kernel", "bm", "bn", "waves", "kblocks", "splits", "name")
+
+
+def _instance(v: dict) -> dict:
+    return {"kernel": v["kernel_name"], "bm": v["bm"], "bn": v["bn"], "waves": v["waves"],
+            "kblocks": v["kblocks"], "splits": v["splits"], "name": v["name"]}
+
+
+def pick_row(M: int, medians: dict, by_name: dict) -> dict:
+    """Table row for key M from per-instance median times (us) keyed by instance name."""
+    names = sorted(medians, key=lambda n: (medians[n], n))
+    best = names[0]
+    unsplit = [n for n in names if by_name[n]["splits"] == 1]
+    if by_name[best]["splits"] > 1 and unsplit and medians[unsplit[0]] <= (1 + SPLIT_PREFERENCE) * medians[best]:
+        best = unsplit[0]
+    row = {"key_m": M, **_instance(by_name[best]), "us": round(medians[best], 3)}
+    others = [medians[n] for n in names if n != best]
+    row["margin"] = round(min(others) / medians[best] - 1, 4) if others else None
+    if by_name[best]["splits"] > 1:
+        row["unsplit"] = {**_instance(by_name[unsplit[0]]), "us": round(medians[unsplit[0]], 3)}
+    row["candidates"] = {n: round(medians[n], 3) for n in names}
+    return row
 
 
 def key_grid(limit: int = 8192, extra=()) -> list[int]:
@@ -105,7 +132,6 @@ _SIDE_STREAM = None
 
 
 def graph_for(calls):
-    # One side stream for every capture: split-K plans keep one workspace per stream.
     global _SIDE_STREAM
     if _SIDE_STREAM is None:
         _SIDE_STREAM = torch.cuda.Stream()
@@ -155,8 +181,23 @@ def _operands(N: int, K: int, mx: bool, batch: int):
     return [torch.from_numpy(x).to(dev) for x in (A, a_s)], W0, torch.from_numpy(w_s).to(dev)
 
 
+def _measure(cands, make_calls, R: int, rounds: int) -> dict:
+    """Median us per call of each candidate: one graph of R calls each, `rounds` interleaved rounds."""
+    graphs = {v["name"]: graph_for(make_calls(v)) for v in cands}
+    # replays per measurement: about 4 ms of work, at least 2
+    probe = time_graph(graphs[cands[0]["name"]], 1)
+    reps = max(2, min(50, int(4.0 / max(probe, 1e-3))))
+    times = {v["name"]: [] for v in cands}
+    for _ in range(rounds):
+        for v in cands:
+            times[v["name"]].append(time_graph(graphs[v["name"]], reps) * 1000.0 / R)
+    del graphs
+    return {n: statistics.median(ts) for n, ts in times.items()}
+
+
 def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
-               mx: bool = False, batch: int = 1, results_path: str = RESULTS, max_copies: int = 256) -> list[dict]:
+               mx: bool = False, batch: int = 1, results_path: str = RESULTS, max_copies: int = 256,
+               production: dict | None = None) -> list[dict]:
     import inputgen
     dev = "cuda:0"
     prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
@@ -168,6 +209,9 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
     R = min(R, max_copies)          # tiny weights: bounded graphs (the activations dominate the traffic there)
     copies = [torch.from_numpy(W0).to(dev)] + \
         [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
+    ws = Workspace(batch * (128 << 20) + (1 << 20))
+    by_name = {v["name"]: v for v in variants()}
+    prod_rows = {int(r["key_m"]): r for r in (production or {}).get("rows", [])}
     rows = []
     for M in grid:
         key = f"{prefix}{N}:{K}:{M}"
@@ -181,38 +225,107 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
             am = (da[:, :M] if batch > 1 else da[:M]).contiguous()
             out = torch.empty(lead + (M, N), dtype=torch.bfloat16, device=dev)
         else:
+            Am, am = dA[:M], da[:M]
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        graphs = {}
-        for v in cands:
-            if mx:
-                calls = [(lambda r=r, vid=v["variant"]: gemm_a8w8_mxscale_run_variant(
-                    vid, Am, am, copies[r], dw, out=out)) for r in range(R)]
-            else:
-                calls = [(lambda r=r, vid=v["variant"]: gemm_a8w8_blockscale_run_variant(
-                    vid, dA[:M], da[:M], copies[r], dw, out=out)) for r in range(R)]
-            graphs[v["variant"]] = graph_for(calls)
-        # replays per measurement: about 4 ms of work, at least 2
-        probe = time_graph(graphs[cands[0]["variant"]], 1)
-        reps = max(2, min(50, int(4.0 / max(probe, 1e-3))))
-        times = {v["variant"]: [] for v in cands}
-        for _ in range(rounds):
-            for v in cands:
-                times[v["variant"]].append(time_graph(graphs[v["variant"]], reps) * 1000.0 / R)
-        med = {vid: statistics.median(ts) for vid, ts in times.items()}
-        best = min(cands, key=lambda v: med[v["variant"]])
-        row = {"key_m": M, "kernel": best["kernel_name"], "bm": best["bm"], "bn": best["bn"],
-               "waves": best["waves"], "kblocks": best["kblocks"], "splits": best["splits"], "name": best["name"],
-               "us": round(med[best["variant"]], 3),
-               "candidates": {v["name"]: round(med[v["variant"]], 3) for v in cands}}
+
+        def make_calls(v):
+            kind = "mx" if mx else "block"
+            return [(lambda r=r, vid=v["variant"]: gemm_a8w8_ex(Am, am, copies[r], dw, scale_kind=kind, variant=vid,
+                                                                workspace=ws, out=out)) for r in range(R)]
+
+        med = _measure(cands, make_calls, R, rounds)
+        row = pick_row(M, med, by_name)
+        row["remeasure"] = None
+        prod = prod_rows.get(M)
+        if prod is not None and prod.get("name") != row["name"] and prod.get("name") in by_name and \
+                any(v["name"] == prod["name"] for v in cands):
+            # The new pick replaces production only if it wins by > 2% twice, each time in freshly captured graphs.
+            pair = [by_name[row["name"]], by_name[prod["name"]]]
+            trials = []
+            for _ in range(2):
+                m2 = _measure(pair, make_calls, R, rounds)
+                trials.append({"new": round(m2[row["name"]], 3), "production": round(m2[prod["name"]], 3)})
+            accepted = all(t["new"] * (1 + REPLACE_MARGIN) < t["production"] for t in trials)
+            if not accepted:
+                pn = prod["name"]
+                keep = {"key_m": M, **_instance(by_name[pn]), "us": round(med[pn], 3)}
+                others = [t for n, t in med.items() if n != pn]
+                keep["margin"] = round(min(others) / med[pn] - 1, 4) if others else None
+                if by_name[pn]["splits"] > 1:
+                    u = min((n for n in med if by_name[n]["splits"] == 1), key=lambda n: (med[n], n))
+                    keep["unsplit"] = {**_instance(by_name[u]), "us": round(med[u], 3)}
+                keep["candidates"] = row["candidates"]
+                row = keep
+            row["remeasure"] = trials
+            row["replaced"] = accepted
         rows.append(row)
         done[key] = row
         with open(results_path, "a") as f:
             f.write(json.dumps({"key": key, "row": row}) + "\n")
-        log(f"{prefix}N={N} K={K} M={M:5d}: {best['name']:24s} {row['us']:9.2f} us  ({len(cands)} candidates)")
-        del graphs, out
-    del copies
+        log(f"{prefix}N={N} K={K} M={M:5d}: {row['name']:24s} {row['us']:9.2f} us  ({len(cands)} candidates)")
+        del out
+    del copies, ws
     torch.cuda.empty_cache()
     return rows
+
+
+def table_row(r: dict) -> dict:
+    """The fields of a measured row that tuned_table.json keeps."""
+    keep = ("key_m",) + ROW_FIELDS + ("us", "margin", "unsplit", "remeasure", "replaced")
+    return {k: r[k] for k in keep if k in r}
+
+
+def parse_instance(name: str) -> dict:
+    """Instance parameters from a compiled instance's name (the names the library gives them)."""
+    import re
+    m = re.fullmatch(r"skinny_r(\d+)_d(\d+)_w(\d+)(?:_k(\d+))?", name)
+    if m:
+        tpw, d, nw, sk = m.groups()
+        return {"name": name, "kernel_name": "skinny", "bm": 16, "bn": 16 * int(tpw), "waves": int(nw),
+                "kblocks": int(d), "splits": int(sk or 1)}
+    m = re.fullmatch(r"pskinny_d(\d+)_w(\d+)_p(\d+)", name)
+    if m:
+        d, nw, _ = m.groups()
+        return {"name": name, "kernel_name": "pskinny", "bm": 16, "bn": 16, "waves": int(nw), "kblocks": int(d),
+                "splits": 1}
+    m = re.fullmatch(r"(p?tile)_(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)(?:_k(\d+))?", name)
+    if m:
+        kern, bm, bn, wm, wn, st, sk = m.groups()
+        return {"name": name, "kernel_name": kern, "bm": int(bm), "bn": int(bn), "waves": int(wm) * int(wn),
+                "kblocks": int(st), "splits": int(sk or 1)}
+    m = re.fullmatch(r"tall_r(\d+)_n(\d+)_d(\d+)_w(\d+)", name)
+    if m:
+        tpw, nt, d, nw = m.groups()
+        return {"name": name, "kernel_name": "tall", "bm": 16 * int(tpw), "bn": 16 * int(nt), "waves": int(nw),
+                "kblocks": int(d), "splits": 1}
+    raise ValueError(f"unknown instance name {name}")
+
+
+def rebuild(results_path: str = RESULTS) -> dict:
+    """tuned_table.json rows from the measurement log alone (first rule applied; no re-measurement,
+    no library needed: instance parameters come from the recorded names)."""
+    done = {}
+    with open(results_path) as f:
+        for line in f:
+            rec = json.loads(line)
+            done[rec["key"]] = rec["row"]
+    table = gst.load()
+    out = []
+    for sh in table["shapes"]:
+        b = int(sh.get("batch", 1))
+        prefix = ("mx" + (str(b) if b > 1 else "") + ":") if sh.get("mx") else ""
+        rows = []
+        for r in sh["rows"]:
+            rec = done.get(f"{prefix}{sh['n']}:{sh['k']}:{r['key_m']}")
+            if rec is None or not rec.get("candidates"):
+                raise ValueError(f"no measurement for key {prefix}{sh['n']}:{sh['k']}:{r['key_m']}")
+            med = dict(rec["candidates"])
+            by_name = {n: parse_instance(n) for n in med}
+            row = pick_row(int(r["key_m"]), med, by_name)
+            row["remeasure"] = rec.get("remeasure")
+            rows.append(table_row(row))
+        out.append({**{k: v for k, v in sh.items() if k != "rows"}, "rows": rows})
+    return {"shapes": out}
 
 
 def main(argv=None) -> int:
@@ -220,11 +333,19 @@ def main(argv=None) -> int:
     ap.add_argument("--shapes", default=None, help="N:K[,N:K...] (MX: N:K[:batch])")
     ap.add_argument("--mx", action="store_true", help="tune the MX-scaled variant")
     ap.add_argument("--rounds", type=int, default=3)
-    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--rotate-gib", type=float, default=2.0)
     ap.add_argument("--max-copies", type=int, default=256, help="at most this many weight copies per graph")
     ap.add_argument("--fresh", action="store_true", help="ignore earlier results")
     ap.add_argument("--results", default=RESULTS, help="measurement log to resume from and append to")
+    ap.add_argument("--rebuild", action="store_true",
+                    help="rewrite tuned_table.json from the measurement log (no GPU), then exit")
     args = ap.parse_args(argv)
+    if args.rebuild:
+        table = rebuild(args.results)
+        gst.validate(table)
+        with open(gst.TABLE_JSON, "w") as f:
+            json.dump(table, f, indent=1)
+        return 0
     root = os.path.dirname(HERE)
     if root not in sys.path:
         sys.path.insert(0, root)
@@ -247,10 +368,9 @@ def main(argv=None) -> int:
         batch = f[2] if len(f) > 2 else 1
         t = time.time()
         rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log, mx=args.mx, batch=batch,
-                          results_path=args.results, max_copies=args.max_copies)
-        entry = {"n": N, "k": K, "rows": [
-            {k: r.get(k, 1) for k in ("key_m", "kernel", "bm", "bn", "waves", "kblocks", "splits", "name", "us")}
-            for r in rows]}
+                          results_path=args.results, max_copies=args.max_copies,
+                          production=shapes.get((N, K, args.mx)))
+        entry = {"n": N, "k": K, "rows": [table_row(r) for r in rows]}
         if args.mx:
             entry = {"n": N, "k": K, "mx": True, "batch": batch, "rows": entry["rows"]}
         shapes[(N, K, args.mx)] = entry

@@ -27,25 +27,24 @@
  *   Y        bf16 (uint16 bit patterns) [M, N]            2-byte aligned; overwritten
  * Y must not overlap any input.
  *
- * Threading / asynchrony: calls only enqueue one kernel on `stream` (a
- * hipStream_t of the current device; NULL = the null stream) and return.
- * Plans that split K over several workgroups per output tile (shapes with
- * few tiles; plan.splits > 1) use a workspace the library keeps per (device,
- * stream) for the life of the process: the first such call on a stream
- * allocates it (32 to 128 MB, plus a zero fill of its counters on that
- * stream), a later one that needs more allocates a larger one (the old one
- * stays allocated, for graphs captured with it); none is allocated while
- * the stream is capturing a graph -- a split plan without a large enough
- * workspace then runs unsplit.  A captured graph uses the workspace of the
- * stream it was captured on: do not run it concurrently with other work
- * captured or enqueued on that stream.  Otherwise calls never synchronise
- * the host, allocate device memory or issue memsets, so they may be captured
- * into a HIP graph (run one call eagerly on the stream first to keep the
- * split plan).  Each output
- * element is reduced in a fixed order (split partials in split order), so
- * results are bitwise reproducible.  The first call on a device reads its
- * properties (architecture, compute units) once.  Calls are re-entrant; the
- * selector table is immutable.
+ * Threading / asynchrony: every call only enqueues work on `stream` (a
+ * hipStream_t of the current device; NULL = the null stream) and returns.  No
+ * call allocates device memory, issues a memset or synchronises the host, and
+ * the library keeps no per-stream state, so every call may be captured into a
+ * HIP graph and replays it exactly (the pages' split-K check replays a
+ * captured call against eager, "[Perf] Retune gfx942 Qwen3.8-27B a8w8
+ * blockscale decode rows for cold weights", Kernel section).  The first call
+ * on a device reads its properties (architecture, compute units) once.  Calls
+ * are re-entrant; the selector table is immutable.  Each output element is
+ * reduced in a fixed order, so results are bitwise reproducible.
+ *
+ * Split K across workgroups.  For shapes with few output tiles the fastest
+ * plan can split K over several workgroups per tile, which meet in a split-K
+ * workspace: device memory the CALLER owns and passes through gemm_a8w8_ex
+ * (see a8w8_gemm_desc).  The plain entries (gemm_a8w8_blockscale and the
+ * other fixed-signature ones) bring no workspace: they always run the fastest
+ * plan that splits no K across workgroups (gemm_a8w8_blockscale_plan reports
+ * it), which needs nothing beyond the operands.
  */
 #ifndef GEMM_A8W8_BLOCKSCALE_H
 #define GEMM_A8W8_BLOCKSCALE_H
@@ -61,10 +60,19 @@ enum {
     A8W8_OK = 0,
     A8W8_ERR_NULL = 1,    /* a required pointer is NULL                          */
     A8W8_ERR_SHAPE = 2,   /* M < 0, N < 1, K < 1, K % 128 != 0, M or N > 2^30, K > 2^22, batch out of [0, 65535] */
-    A8W8_ERR_ALIGN = 3,   /* A or W not 16-byte aligned, a scale or Y not 4-byte aligned */
+    A8W8_ERR_ALIGN = 3,   /* A or W not 16-byte aligned, a scale not 4, Y not 2, a workspace not 256 */
     A8W8_ERR_ARCH = 4,    /* the current device is not gfx950                    */
     A8W8_ERR_HIP = 5,     /* a HIP runtime call or kernel launch failed          */
-    A8W8_ERR_PLAN = 6     /* a plan passed to gemm_a8w8_blockscale_run_plan is invalid for the shape */
+    A8W8_ERR_PLAN = 6,    /* a forced kernel instance cannot serve the shape         */
+    A8W8_ERR_WORKSPACE = 7 /* a forced split-K instance lacks workspace, or a workspace  */
+                          /* argument is inconsistent (NULL with a size, size < 0)      */
+};
+
+/* Scale kinds of gemm_a8w8_ex (a8w8_gemm_desc.scale_kind). */
+enum {
+    A8W8_SCALE_BLOCK = 0,   /* fp32 per 1x128 activation group and 128x128 weight block */
+    A8W8_SCALE_MX = 1,      /* E8M0 per 1x32 activation group and 32x32 weight block    */
+    A8W8_SCALE_ROWWISE = 2  /* fp32 per activation row and per weight row               */
 };
 
 /* Kernels behind the selector. */
@@ -93,6 +101,7 @@ typedef struct {
     int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
     int32_t splits;     /* tile, skinny: workgroups per output tile, each taking 1/splits of K (1: none) */
     int32_t reserved;
+    int64_t workspace;  /* bytes of split-K workspace this launch uses (0: none)     */
 } a8w8_plan;
 
 /*
@@ -105,8 +114,14 @@ int gemm_a8w8_blockscale(const void *A, const float *a_scale,
                          void *stream);
 
 /*
- * The plan gemm_a8w8_blockscale would launch for (M, N, K) on a gfx950
- * device with `cu_count` compute units (0 = 256).  Host only; needs no GPU.
+ * The plan gemm_a8w8_blockscale launches for (M, N, K) on a gfx950 device with
+ * `cu_count` compute units (0 = 256): exactly the instance, tile, grid and
+ * table key of that call (never a split-K plan, workspace = 0).  Host only;
+ * needs no GPU.  The pages decide from lookup logs which tuned row each
+ * served shape hit ("Why aiter#5069's measured -25% kernel win moved serving
+ * throughput by 0.0%", its census-tool section); this query is the library's
+ * way of giving that answer without running the kernel (a project reading:
+ * the pages print no such call).
  */
 int gemm_a8w8_blockscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count,
                               a8w8_plan *out);
@@ -123,7 +138,8 @@ int gemm_a8w8_describe_variant(int32_t variant, int64_t M, int64_t N, int64_t K,
  * returns A8W8_ERR_PLAN if the instance cannot handle the shape (the skinny
  * kernels need M <= 16, a pskinny instance also K/128 <= waves * kblocks; a
  * tall instance needs N <= its bn; a split instance needs K/128 >= 2 * splits
- * and at most 128 MB of fp32 partials).
+ * and at most 128 MB of fp32 partials) and A8W8_ERR_WORKSPACE for a split
+ * instance (these entries bring no workspace: run those through gemm_a8w8_ex).
  */
 int gemm_a8w8_blockscale_run_variant(int32_t variant,
                                      const void *A, const float *a_scale,
@@ -242,7 +258,10 @@ int gemm_a8w8_rowwise_run_variant(int32_t variant, const void *A, const float *a
 /* Static name of a compiled instance, e.g. "tile_256x128" (NULL if out of range). */
 const char *gemm_a8w8_variant_name(int32_t variant);
 
-/* Static, human-readable text for a status code. */
+/* Static, human-readable text for a status code (a project reading: the pages
+   say only that a lookup miss should fall back rather than fail, "Rounds
+   40-41: the CK int8 GEMM ...", Gate 1; errors the call cannot recover from
+   are returned as these codes, never thrown or printed). */
 const char *gemm_a8w8_status_string(int status);
 
 /* Hash of the compiled selector table (identifies the tuning that is deployed). */
@@ -273,6 +292,60 @@ uint64_t gemm_a8w8_table_hash(void);
  * errors are returned before anything is enqueued.
  */
 int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64_t K, void *stream);
+
+/*
+ * One call of any scale kind and weight layout, with an optional caller-owned
+ * split-K workspace and an optional forced instance.  The plain entries above
+ * are this call with workspace = NULL, workspace_bytes = 0, variant = -1.
+ *
+ *   A, a_scale, W, w_scale, Y  as for the entry of that scale kind (device
+ *                              memory, row-major; W packed when w_packed = 1)
+ *   batch        >= 0 consecutive problems of one shape (every operand has a
+ *                leading batch dimension; 1 for plain 2-D operands)
+ *   scale_kind   A8W8_SCALE_BLOCK, A8W8_SCALE_MX or A8W8_SCALE_ROWWISE
+ *   variant      -1: the selector's plan; else a compiled instance (tuning, tests)
+ *   workspace    NULL, or split-K workspace: caller-owned device memory,
+ *                256-byte aligned, of workspace_bytes bytes, zero-filled once
+ *                by gemm_a8w8_workspace_init before its first use.  Its first
+ *                A8W8_WORKSPACE_COUNTER_BYTES hold the per-tile counters of a
+ *                split call (the same area for every call), the rest the
+ *                fp32 partial tiles.  Every call leaves the counters zero
+ *                again, so one workspace serves any number of calls, of any
+ *                shapes, IN STREAM ORDER; calls (or graph replays) that may
+ *                overlap in time need workspaces of their own.  The library
+ *                keeps no pointer to it.
+ *
+ * Plan rule (variant = -1): the table row's fastest instance if its split-K
+ * workspace (gemm_a8w8_ex_plan with workspace_bytes large: plan.workspace)
+ * fits in workspace_bytes, else the row's fastest instance that splits no K
+ * across workgroups.  A forced split instance without enough workspace
+ * returns A8W8_ERR_WORKSPACE before anything is enqueued.
+ */
+#define A8W8_WORKSPACE_COUNTER_BYTES 65536
+
+typedef struct {
+    const void *A;
+    const void *a_scale;
+    const void *W;
+    const void *w_scale;
+    void *Y;
+    int64_t batch;
+    int64_t M, N, K;
+    int32_t scale_kind;
+    int32_t w_packed;
+    int32_t variant;
+    int32_t reserved;
+    void *workspace;
+    int64_t workspace_bytes;
+} a8w8_gemm_desc;
+
+int gemm_a8w8_ex(const a8w8_gemm_desc *desc, void *stream);
+/* The plan gemm_a8w8_ex launches for `desc` (host only; pointers are not
+   read, workspace_bytes is): plan.workspace is the workspace it uses. */
+int gemm_a8w8_ex_plan(const a8w8_gemm_desc *desc, int32_t cu_count, a8w8_plan *out);
+/* Enqueue the zero fill of a split-K workspace (one kernel of the library on
+   `stream`, no memset, so it may be captured too). */
+int gemm_a8w8_workspace_init(void *workspace, int64_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -92,8 +92,8 @@ def test_misaligned_pointers(kw):
 
 
 def test_status_strings_and_variant_names():
-    for s in range(7):
-        assert g.gemm_a8w8_status_string(s)
+    for s in range(8):
+        assert g.gemm_a8w8_status_string(s) != "unknown status"
     assert g.gemm_a8w8_status_string(99) == "unknown status"
     n = g.gemm_a8w8_num_variants()
     names = [g.gemm_a8w8_variant_name(i) for i in range(n)]
@@ -180,18 +180,26 @@ def test_every_m_has_a_tuned_plan_within_125_percent(N, K):
             assert M <= 16
 
 
+BIG_WS = 1 << 40
+
+
 def test_heuristic_skinny_rule():
     # Up to M = 16 on an unregistered (N, K): fewest passes over K, then the deepest
-    # pass (8 waves x 6 blocks); fewer than 32 sixteen-row groups split K four ways.
+    # pass (8 waves x 6 blocks); fewer than 32 sixteen-row groups split K four ways
+    # when the call brings a workspace.
     for M, N, K in ((1, 1000, 3072), (16, 640, 4096), (1, 2000, 2048), (16, 3000, 5120), (1, 4096, 4096)):
         p = g.gemm_a8w8_blockscale_plan(M, N, K)
         assert p["fallback"] == 1 and p["name"] == "skinny_r1_d6_w8" and p["kpasses"] == 1, (M, N, K, p)
     for M, N, K in ((8, 128, 8192), (5, 100, 1024), (16, 496, 4096), (1, 32, 3072)):
-        p = g.gemm_a8w8_blockscale_plan(M, N, K)
+        p = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=BIG_WS)
         assert p["fallback"] == 1 and p["name"] == "skinny_r1_d3_w4_k4", (M, N, K, p)
-        assert p["grid"] == -(-N // 16) * 4
+        assert p["grid"] == -(-N // 16) * 4 and p["workspace"] > 0
+        u = g.gemm_a8w8_blockscale_plan(M, N, K)                   # no workspace: unsplit
+        assert u["fallback"] == 1 and u["splits"] == 1 and u["workspace"] == 0 and u["kernel_name"] == "skinny"
+        assert g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=p["workspace"] - 256)["name"] == u["name"]
+        assert g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=p["workspace"])["name"] == p["name"]
     # too few K blocks for four splits (K/128 < 8): unsplit
-    p = g.gemm_a8w8_blockscale_plan(5, 100, 896)
+    p = g.gemm_a8w8_ex_plan(5, 100, 896, workspace_bytes=BIG_WS)
     assert p["fallback"] == 1 and p["splits"] == 1 and p["kernel_name"] == "skinny"
 
 
@@ -343,6 +351,83 @@ def test_split_instances_beyond_the_workspace_cap_are_rejected():
 def test_plans_report_splits():
     for M, N, K in ((1, 14336, 5120), (8192, 14336, 5120)):
         assert g.gemm_a8w8_blockscale_plan(M, N, K)["splits"] >= 1
+
+
+@pytest.mark.parametrize("N,K", REGISTERED)
+def test_plain_entry_never_splits_and_ex_follows_the_table(N, K):
+    """The plain entry's plan never needs a workspace; gemm_a8w8_ex with room for it runs the
+    row's instance, with less room the row's unsplit instance (the one the plain entry runs)."""
+    rows = {int(r["key_m"]): r for s in gst.load()["shapes"]
+            if (int(s["n"]), int(s["k"])) == (N, K) and not s.get("mx") for r in s["rows"]}
+    keys = sorted(rows)
+    for M in list(range(1, 200)) + list(range(200, 8193, 37)):
+        key = next(k for k in keys if k >= M)
+        r = rows[key]
+        u = gst.unsplit_of(r)
+        p = g.gemm_a8w8_blockscale_plan(M, N, K)
+        assert p["splits"] == 1 and p["workspace"] == 0 and p["name"] == u["name"], (M, p["name"], u["name"])
+        e = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=BIG_WS)
+        assert e["name"] == r["name"] and e["key_m"] == key, (M, e["name"], r["name"])
+        assert (e["workspace"] > 0) == (int(r.get("splits", 1)) > 1)
+        if e["workspace"] > 0:
+            assert g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=e["workspace"] - 1)["name"] == u["name"]
+
+
+def _desc(**kw):
+    d = dict(A=16, a_scale=16, W=16, w_scale=16, Y=16, batch=1, M=64, N=512, K=1024, scale_kind=0,
+             w_packed=0, variant=-1, reserved=0, workspace=None, workspace_bytes=0)
+    d.update(kw)
+    return g.GemmDesc(*(d[f] for f, _ in g.GemmDesc._fields_))
+
+
+def test_ex_entry_checks_arguments():
+    L = g.lib()
+    ex = lambda **kw: L.gemm_a8w8_ex(ctypes.byref(_desc(**kw)), None)
+    assert L.gemm_a8w8_ex(None, None) == g.A8W8_ERR_NULL
+    assert L.gemm_a8w8_ex_plan(None, 0, ctypes.byref(g.Plan())) == g.A8W8_ERR_NULL
+    assert ex(K=1000) == g.A8W8_ERR_SHAPE
+    assert ex(batch=-1) == g.A8W8_ERR_SHAPE
+    assert ex(scale_kind=3) == g.A8W8_ERR_SHAPE
+    assert ex(w_packed=2) == g.A8W8_ERR_SHAPE
+    assert ex(workspace_bytes=4096) == g.A8W8_ERR_WORKSPACE       # a size without memory
+    assert ex(workspace=256, workspace_bytes=-256) == g.A8W8_ERR_WORKSPACE
+    assert ex(workspace=272, workspace_bytes=4096) == g.A8W8_ERR_ALIGN
+    assert ex(A=None) == g.A8W8_ERR_NULL
+    assert ex(M=0, A=None, Y=None) == g.A8W8_OK
+    assert ex(batch=0, A=None) == g.A8W8_OK
+    assert ex(variant=10 ** 6) == g.A8W8_ERR_PLAN
+    split = next(v for v in g.variants() if v["splits"] > 1 and v["kernel_name"] == "tile")
+    need = g.gemm_a8w8_describe_variant(split["variant"], 64, 512, 1024)["workspace"]
+    assert need > 0
+    # a forced split instance without enough workspace is refused before any device call
+    assert ex(variant=split["variant"]) == g.A8W8_ERR_WORKSPACE
+    assert ex(variant=split["variant"], workspace=256, workspace_bytes=need - 256) == g.A8W8_ERR_WORKSPACE
+    assert L.gemm_a8w8_blockscale_run_variant(split["variant"], 16, 16, 16, 16, 16, 64, 512, 1024,
+                                              None) == g.A8W8_ERR_WORKSPACE
+    p = g.Plan()
+    assert L.gemm_a8w8_ex_plan(ctypes.byref(_desc(variant=split["variant"])), 0, ctypes.byref(p)) == \
+        g.A8W8_ERR_WORKSPACE
+    assert L.gemm_a8w8_ex_plan(ctypes.byref(_desc(variant=split["variant"], workspace_bytes=need)), 0,
+                               ctypes.byref(p)) == g.A8W8_OK
+    assert p.workspace == need and p.variant == split["variant"]
+
+
+def test_workspace_init_checks_arguments():
+    L = g.lib()
+    assert L.gemm_a8w8_workspace_init(None, 0, None) == g.A8W8_OK
+    assert L.gemm_a8w8_workspace_init(256, -256, None) == g.A8W8_ERR_SHAPE
+    assert L.gemm_a8w8_workspace_init(None, 256, None) == g.A8W8_ERR_NULL
+    assert L.gemm_a8w8_workspace_init(272, 256, None) == g.A8W8_ERR_ALIGN
+    assert L.gemm_a8w8_workspace_init(256, 300, None) == g.A8W8_ERR_ALIGN
+
+
+def test_workspace_size_covers_counters_and_partials():
+    for v in g.variants():
+        if v["splits"] > 1:
+            for M, N in ((64, 512), (300, 1000), (16, 32)):
+                d = g.gemm_a8w8_describe_variant(v["variant"], M, N, 4096)
+                tiles = -(-M // v["bm"]) * -(-N // v["bn"])
+                assert d["workspace"] == 65536 + tiles * v["splits"] * v["bm"] * v["bn"] * 4
 
 
 # ---------------------------------------------------------------- benchmark read-ceiling kernel

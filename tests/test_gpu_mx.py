@@ -21,7 +21,7 @@ import torch
 import fp8_block_scaled_a8w8_amd as g
 import inputgen
 import oracle
-from tests.gpu_util import DEV, say, y_bits, y_host
+from tests.gpu_util import DEV, say, shared_workspace, variant_by_name, variant_names, y_bits, y_host
 from tests.parity_util import assert_parity, bf16_round
 
 pytestmark = pytest.mark.gpu
@@ -64,21 +64,20 @@ def _shape_for(v, cus):
     return tiles_m * v["bm"] - v["bm"] // 2 - 3, N
 
 
-@pytest.mark.parametrize("variant", range(96))
-def test_every_instance_mx(variant):
-    if variant >= g.gemm_a8w8_num_variants():
-        pytest.skip("no such instance")
-    v = g.gemm_a8w8_describe_variant(variant)
+@pytest.mark.parametrize("name", variant_names())
+def test_every_instance_mx(name):
+    v = variant_by_name(name)
+    variant = v["variant"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     K = max(640, 256 * v["splits"])   # split-K instances need >= 2 K blocks per split
     M, N = _shape_for(v, cus)
     A, a, W, w = _mx_operands(M, N, K, seed=1000 + variant)
     dA, da, dW, dw = _dev(A, a, W, w)
     say(f"mx {v['name']} M={M} N={N} K={K}")
-    y = g.gemm_a8w8_mxscale_run_variant(variant, dA, da, dW, dw)
+    y = g.gemm_a8w8_mxscale_run_variant(variant, dA, da, dW, dw, workspace=shared_workspace())
     rows = _rows(M)
     assert_parity(y_host(y)[rows], oracle.gemm_mx(A, a, W, w, rows=rows), f"mx {v['name']}")
-    yp = g.gemm_a8w8_mxscale_run_variant(variant, dA, da, g.prepack_weights(dW), dw, packed_n=N)
+    yp = g.gemm_a8w8_mxscale_run_variant(variant, dA, da, g.prepack_weights(dW), dw, packed_n=N, workspace=shared_workspace())
     assert np.array_equal(y_bits(yp), y_bits(y)), f"mx packed {v['name']}"
 
 
@@ -145,7 +144,7 @@ def test_batched_ragged_every_kernel_family():
         A, a, W, w = _batched_operands(3, M, N, K, seed=vid)
         dA, da, dW, dw = _dev(A, a, W, w)
         say(f"mx batched {v['name']} b=3 M={M} N={N} K={K}")
-        y = g.gemm_a8w8_mxscale_run_variant(vid, dA, da, dW, dw)
+        y = g.gemm_a8w8_mxscale_run_variant(vid, dA, da, dW, dw, workspace=shared_workspace())
         yh = y_host(y)
         rows = _rows(M)
         for i in range(3):
@@ -170,7 +169,7 @@ def test_integer_case_bitwise():
         if v["kernel_name"] in ("skinny", "pskinny") or (v["kernel_name"] == "tall" and v["bn"] < N) \
                 or K // 128 < 2 * v["splits"]:
             continue
-        y = y_host(g.gemm_a8w8_mxscale_run_variant(vid, dA, da, dW, dw))
+        y = y_host(g.gemm_a8w8_mxscale_run_variant(vid, dA, da, dW, dw, workspace=shared_workspace()))
         assert np.array_equal(y, ref), v["name"]
     Ms = 9
     y = y_host(g.gemm_a8w8_mxscale(dA[:Ms].contiguous(), da[:Ms].contiguous(), dW, dw))

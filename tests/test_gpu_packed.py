@@ -15,7 +15,7 @@ import torch
 import fp8_block_scaled_a8w8_amd as g
 import inputgen
 import oracle
-from tests.gpu_util import DEV, say, to_dev, y_bits, y_host
+from tests.gpu_util import DEV, say, shared_workspace, to_dev, variant_by_name, variant_names, y_bits, y_host
 from tests.parity_util import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -57,19 +57,18 @@ def _shape_for(v, cus):
     return tiles_m * v["bm"] - v["bm"] // 2 - 3, N
 
 
-@pytest.mark.parametrize("variant", range(96))
-def test_every_instance_packed_equals_row_major(variant):
-    if variant >= g.gemm_a8w8_num_variants():
-        pytest.skip("no such instance")
-    v = g.gemm_a8w8_describe_variant(variant)
+@pytest.mark.parametrize("name", variant_names())
+def test_every_instance_packed_equals_row_major(name):
+    v = variant_by_name(name)
+    variant = v["variant"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     K = max(640, 256 * v["splits"])   # split-K instances need >= 2 K blocks per split
     M, N = _shape_for(v, cus)
     A, a_s = inputgen.make_activations(M, K, seed=M)
     W, w_s = inputgen.make_weights(N, K, seed=N)
     dA, da, dW, dw = to_dev(A, a_s, W, w_s)
-    y_row = g.gemm_a8w8_blockscale_run_variant(variant, dA, da, dW, dw)
-    y_pk = g.gemm_a8w8_blockscale_packed_run_variant(variant, dA, da, g.prepack_weights(dW), dw, N)
+    y_row = g.gemm_a8w8_blockscale_run_variant(variant, dA, da, dW, dw, workspace=shared_workspace())
+    y_pk = g.gemm_a8w8_blockscale_packed_run_variant(variant, dA, da, g.prepack_weights(dW), dw, N, workspace=shared_workspace())
     assert np.array_equal(y_bits(y_pk), y_bits(y_row)), f"{v['name']} M={M} N={N}"
     rows = sorted({0, M // 2, M - 1})
     assert_parity(y_host(y_pk)[rows], oracle.gemm(A, a_s, W, w_s, rows=rows), f"{v['name']} packed")

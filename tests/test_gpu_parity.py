@@ -18,7 +18,7 @@ import torch
 import fp8_block_scaled_a8w8_amd as g
 import inputgen
 import oracle
-from tests.gpu_util import DEV, run, say, to_dev, y_bits, y_host
+from tests.gpu_util import DEV, run, say, shared_workspace, to_dev, variant_by_name, variant_names, y_bits, y_host
 from tests.parity_util import assert_parity, bf16_round
 
 pytestmark = pytest.mark.gpu
@@ -86,18 +86,48 @@ def test_prefill_sampled_rows(N, K):
 SWEEP_NK = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6144), (32, 6144)]
 
 
+def sweep_rows(M, bm, pool, count=16):
+    """Rows of an M-row output to check: 0, M - 1, the rows on each side of every third tile
+    boundary of the plan's tile height bm (spread evenly when there are many), then rows of a
+    fixed seeded pool, `count` in all when M has that many."""
+    rows = {0, M - 1}
+    bounds = [k * bm for k in range(3, -(-M // bm), 3)]
+    if len(bounds) > 5:
+        bounds = [bounds[int(i * (len(bounds) - 1) / 4)] for i in range(5)]
+    for b in bounds:
+        rows.update({b - 1, b})
+    for r in pool:
+        if len(rows) >= min(count, M):
+            break
+        if r < M:
+            rows.add(int(r))
+    r = 1
+    while len(rows) < min(count, M):
+        rows.add(r)
+        r += 1
+    return sorted(rows)
+
+
 @pytest.mark.parametrize("N,K", SWEEP_NK)
 def test_dense_m_sweep_sampled_rows(N, K):
+    """256 seeded M in 1..8192 through the selector with a split-K workspace (the table's
+    fastest plans), 16 checked rows per M including both sides of every third tile boundary;
+    every fifth M also through the plain entry (the unsplit plans)."""
     Ms = inputgen.random_m_values(256, seed=2)
     A_all, a_all = inputgen.make_activations(8192, K, seed=0)
     W, w_s = inputgen.make_weights(N, K, seed=1)
     dA, da, dW, dw = to_dev(A_all, a_all, W, w_s)
-    rng = np.random.default_rng(6)
+    pool = np.random.default_rng(6).permutation(8192)[:64]
+    ws = g.Workspace(64 << 20)
     picked = []          # (M, rows, gpu values of those rows)
-    for M in Ms:
-        y = run(dA[:M], da[:M], dW, dw)
-        rows = sorted({M - 1, int(rng.integers(0, M))})
+    for i, M in enumerate(Ms):
+        plan = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=ws.nbytes)
+        rows = sweep_rows(M, plan["bm"], pool)
+        y = g.gemm_a8w8_blockscale(dA[:M], da[:M], dW, dw, workspace=ws)
         picked.append((M, rows, y[rows].to(torch.float32).cpu().numpy().astype(np.float64)))
+        if i % 5 == 0:
+            y = run(dA[:M], da[:M], dW, dw)
+            picked.append((M, rows, y[rows].to(torch.float32).cpu().numpy().astype(np.float64)))
     union = sorted({r for _, rows, _ in picked for r in rows})
     ref = oracle.gemm(A_all, a_all, W, w_s, rows=union)
     pos = {r: i for i, r in enumerate(union)}
@@ -110,11 +140,11 @@ def test_dense_m_sweep_sampled_rows(N, K):
 
 # ---------------------------------------------------------------- every compiled instance
 
-@pytest.mark.parametrize("variant", range(96))
-def test_every_instance_on_ragged_shape(variant):
-    if variant >= g.gemm_a8w8_num_variants():
-        pytest.skip("no such instance")
-    info = g.gemm_a8w8_describe_variant(variant)
+@pytest.mark.parametrize("name", variant_names())
+def test_every_instance_on_ragged_shape(name):
+    info = variant_by_name(name)
+    variant = info["variant"]
+    ws = shared_workspace()
     K = max(640, 256 * info["splits"])   # split-K instances need >= 2 K blocks per split
     if info["kernel_name"] in ("skinny", "pskinny"):
         shapes = [(1, 300), (7, 130), (16, 64)]
@@ -124,7 +154,7 @@ def test_every_instance_on_ragged_shape(variant):
         shapes = [(77, 300), (200, 520), (33, 32)]
     for (M, N) in shapes:
         A, a_s, W, w_s = _inputs(M, N, K, a_seed=10 + M, w_seed=20 + N)
-        y = run(*to_dev(A, a_s, W, w_s), variant=variant)
+        y = g.gemm_a8w8_blockscale_run_variant(variant, *to_dev(A, a_s, W, w_s), workspace=ws)
         assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"{info['name']} M={M} N={N}")
     say(f"instance {info['name']} ok")
 
