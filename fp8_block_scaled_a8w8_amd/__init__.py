@@ -68,6 +68,7 @@ EXPORTED = (
     "gemm_a8w8_ex",
     "gemm_a8w8_ex_plan",
     "gemm_a8w8_workspace_init",
+    "gemm_a8w8_blockscale_noalloc",
 )
 
 
@@ -159,6 +160,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_ex_plan.argtypes = [ctypes.POINTER(GemmDesc), i32, ctypes.POINTER(Plan)]
         L.gemm_a8w8_workspace_init.restype = ctypes.c_int
         L.gemm_a8w8_workspace_init.argtypes = [vp, i64, vp]
+        L.gemm_a8w8_blockscale_noalloc.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_noalloc.argtypes = [vp] * 5 + [i64] * 3 + [vp]
         _lib = L
     return _lib
 
@@ -298,6 +301,18 @@ def gemm_a8w8_blockscale(A: torch.Tensor, a_scale: torch.Tensor, W: torch.Tensor
                                     _stream_handle(stream))
     if rc != A8W8_OK:
         raise A8W8Error(rc, "gemm_a8w8_blockscale")
+    return out
+
+
+def gemm_a8w8_blockscale_noalloc(A, a_scale, W, w_scale, out=None, stream=None) -> torch.Tensor:
+    """gemm_a8w8_blockscale_noalloc of the C ABI: the table's fastest plan (split K included) with
+    the library's static scratch as workspace; the C call allocates nothing (``out`` may be given
+    so that nothing is allocated here either).  Calls overlapping in time on one GPU race."""
+    M, N, K, out = _check(A, a_scale, W, w_scale, out)
+    rc = lib().gemm_a8w8_blockscale_noalloc(A.data_ptr(), a_scale.data_ptr(), W.data_ptr(), w_scale.data_ptr(),
+                                            out.data_ptr(), M, N, K, _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_blockscale_noalloc")
     return out
 
 

@@ -49,11 +49,30 @@ std::atomic<int> g_dev_state[kMaxDevices];
 std::atomic<int> g_dev_cus[kMaxDevices];
 std::mutex g_init_mutex;
 
-int device_ready(int *cus)
+}  // namespace
+
+// Scratch of the allocation-free entry point (gemm_a8w8_blockscale_noalloc): a
+// split-K workspace in static device memory, one copy per GPU (each at its own
+// address), held until the process ends.  Its counter area starts zeroed and
+// every call leaves it zeroed.  In host code this name stands for the host-side
+// symbol, not the device copy: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[A8W8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` per device (0: not looked up yet), and whether
+// its counter area has been cleared by an eager (not captured) call.
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+std::atomic<int> g_scratch_clean[kMaxDevices];
+
+int device_ready(int *cus, int *device = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return A8W8_ERR_HIP;
+    if (device)
+        *device = dev;
     int st = g_dev_state[dev].load(std::memory_order_acquire);
     if (st == 0) {
         std::lock_guard<std::mutex> lock(g_init_mutex);
@@ -582,6 +601,62 @@ int gemm_a8w8_workspace_init(void *workspace, int64_t bytes, void *stream)
     hipLaunchKernelGGL(workspace_clear_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<uint4 *>(workspace), n16);
     return hipGetLastError() == hipSuccess ? A8W8_OK : A8W8_ERR_HIP;
+}
+
+int gemm_a8w8_blockscale_noalloc(const void *A, const float *a_scale, const void *W, const float *w_scale, void *Y,
+                                 int64_t M, int64_t N, int64_t K, void *stream)
+{
+    Operands o = {A, a_scale, W, w_scale, Y, 1, 0, 0, nullptr, 0};
+    int rc = check_call(o, M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M == 0)
+        return A8W8_OK;
+    rc = check_pointers(A, a_scale, W, w_scale, Y);
+    if (rc != A8W8_OK)
+        return rc;
+    int cus = 0, dev = 0;
+    rc = device_ready(&cus, &dev);
+    if (rc != A8W8_OK)
+        return rc;
+    // The table's fastest plan, split or not; a plan needing more scratch than
+    // the array holds is refused, never run with less.
+    const Choice c = select_variant(M, N, K, cus, 0, 1, INT64_MAX);
+    if (workspace_need(c.variant, M, N, 1) > (int64_t)A8W8_NOALLOC_SCRATCH_BYTES)
+        return A8W8_ERR_WORKSPACE;
+    // Set-up, once per device with that device current: the device address of
+    // this GPU's copy of the array.
+    uintptr_t addr = g_scratch[dev].load(std::memory_order_acquire);
+    if (addr == 0) {
+        std::lock_guard<std::mutex> lock(g_init_mutex);
+        addr = g_scratch[dev].load(std::memory_order_acquire);
+        if (addr == 0) {
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+                return A8W8_ERR_HIP;
+            addr = reinterpret_cast<uintptr_t>(ptr);
+            g_scratch[dev].store(addr, std::memory_order_release);
+        }
+    }
+    // Static device memory starts zero-filled; until an eager call has cleared
+    // the counter area with the library's fill kernel (stream-ordered before
+    // this call's GEMM), every call enqueues that clear first -- inside a
+    // captured graph too, where it is part of each replay.
+    if (g_scratch_clean[dev].load(std::memory_order_acquire) == 0) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess)
+            return A8W8_ERR_HIP;
+        hipLaunchKernelGGL(workspace_clear_kernel, dim3(16), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           reinterpret_cast<uint4 *>(addr), (int64_t)(kCounterBytes / 16));
+        if (hipGetLastError() != hipSuccess)
+            return A8W8_ERR_HIP;
+        if (cs == hipStreamCaptureStatusNone)
+            g_scratch_clean[dev].store(1, std::memory_order_release);
+    }
+    o.ws = reinterpret_cast<void *>(addr);
+    o.ws_bytes = A8W8_NOALLOC_SCRATCH_BYTES;
+    log_plan(M, N, K, c.variant, c.key_m, c.fallback);
+    return launch(c.variant, o, M, N, K, cus, stream);
 }
 
 int gemm_a8w8_mxscale_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, a8w8_plan *out)

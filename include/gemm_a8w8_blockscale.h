@@ -347,6 +347,27 @@ int gemm_a8w8_ex_plan(const a8w8_gemm_desc *desc, int32_t cu_count, a8w8_plan *o
    `stream`, no memset, so it may be captured too). */
 int gemm_a8w8_workspace_init(void *workspace, int64_t bytes, void *stream);
 
+/*
+ * Allocation-free entry: for callers that cannot allocate device memory
+ * (code under HIP-graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc) yet want the split-K plans, which need a workspace.  Same
+ * arguments and result as gemm_a8w8_blockscale, but it runs the table row's
+ * fastest plan (what gemm_a8w8_ex runs with an unlimited workspace) and takes
+ * that plan's split-K workspace from a static device array of
+ * A8W8_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until the
+ * process ends.  A plan that needs more than that returns A8W8_ERR_WORKSPACE
+ * before anything is enqueued (gemm_a8w8_ex_plan with workspace_bytes =
+ * INT64_MAX reports the need as plan.workspace).  It allocates nothing, issues
+ * no memset and does not synchronise.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, concurrent
+ * graph replays) race and give wrong results; calls in stream order are safe.
+ */
+#define A8W8_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int gemm_a8w8_blockscale_noalloc(const void *A, const float *a_scale,
+                                 const void *W, const float *w_scale,
+                                 void *Y, int64_t M, int64_t N, int64_t K,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif
