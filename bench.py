@@ -146,7 +146,7 @@ def read_ceiling_block(torch, dev, nbytes, R, replays, us_decode):
     (fp8_block_scaled_a8w8_amd/csrc/read_ceiling.hip) over R rotated buffers of `nbytes`,
     timed like the GEMM (one HIP graph of R launches), best of a few grids."""
     import ctypes
-    path = os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "libread_ceiling.so")
+    path = os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "libceilings.so")
     lib = ctypes.CDLL(path)
     fn = lib.a8w8_read_ceiling_launch
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -172,6 +172,71 @@ def read_ceiling_block(torch, dev, nbytes, R, replays, us_decode):
     return {"bytes": nbytes, "us": round(us, 3), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "config": f"{grid} workgroups x 256 lanes, {unroll} 16-byte loads per lane in flight, {R} rotated buffers",
             "decode_frac_of_ceiling": round(us / us_decode, 4)}
+
+
+def decode_shape_block(torch, g, inputgen, oracle, dev, N, K, Ms, replays, seed_w=11):
+    """One decode shape with cold weights (>= 2 GiB of rotated copies): parity gate on the first
+    and last copy for every M (all 16 rows against the oracle), then, per M, one HIP graph of R
+    calls timed with HIP events; returns per-M us/call and HBM fractions and their mean."""
+    A, a_s = inputgen.make_activations(16, K, seed=seed_w + 1)
+    W0, w_s = inputgen.make_weights(N, K, seed=seed_w)
+    R = math.ceil(ROTATE_BYTES / (W0.nbytes + w_s.nbytes))
+    dA, da, dw = (torch.from_numpy(x).to(dev) for x in (A, a_s, w_s))
+    copies = [torch.from_numpy(W0 if r == 0 else inputgen.sign_flip_copy(W0, seed=2000 + r)).to(dev)
+              for r in range(R)]
+    worst = 0.0
+    for r in (0, R - 1):
+        Wr = W0 if r == 0 else inputgen.sign_flip_copy(W0, seed=2000 + r)
+        worst = max(worst, parity_gate(g, oracle, A, a_s, Wr, w_s, dA, da, copies[r], dw, Ms,
+                                       f"decode N={N} K={K} copy {r}"))
+    per_m = {}
+    for M in Ms:
+        outM = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gm = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw, out=outM))
+                                for r in range(R)], 0, 2)
+        us = timed_replays(torch, gm, replays) * 1000.0 / R
+        gbs = algorithmic_bytes(M, N, K) / (us * 1e-6) / 1e9
+        per_m[str(M)] = {"us_per_call": round(us, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "plan": g.gemm_a8w8_blockscale_plan(M, N, K)["name"]}
+        del gm
+    del copies
+    torch.cuda.empty_cache()
+    us_mean = sum(v["us_per_call"] for v in per_m.values()) / len(per_m)
+    bytes_mean = sum(algorithmic_bytes(M, N, K) for M in Ms) / len(Ms)
+    return {"us_per_call_mean": round(us_mean, 3),
+            "hbm_frac": round(bytes_mean / (us_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_call_mean": round(bytes_mean), "weight_copies": R,
+            "rotate_bytes": R * (W0.nbytes + w_s.nbytes), "parity_worst_rel_l2": round(worst, 6), "per_m": per_m}
+
+
+def mfma_ceiling_block(torch, dev, W_bytes_dev, replays):
+    """The part's sustained fp8 MFMA rate (fp8_block_scaled_a8w8_amd/csrc/mfma_ceiling.hip): 8
+    independent in-place MFMA chains per wave, two waves per SIMD, operands taken from real weight
+    bytes; one HIP graph of 4 launches of about 2 ms each, timed with HIP events."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "libceilings.so"))
+    fn = lib.a8w8_mfma_ceiling_launch
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    fl = lib.a8w8_mfma_ceiling_flops
+    fl.argtypes = [ctypes.c_int, ctypes.c_int]
+    fl.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid, iters = 2 * cus, 4000                    # 8 waves per CU
+    nfrag = W_bytes_dev.numel() // 2048
+    sink = torch.zeros(grid, dtype=torch.float32, device=dev)
+
+    def launch():
+        rc = fn(W_bytes_dev.data_ptr(), nfrag, sink.data_ptr(), grid, iters, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"mfma_ceiling launch failed ({rc})")
+    gr = time_graph(torch, [launch] * 4, 0, 1)
+    ms = timed_replays(torch, gr, replays) / 4
+    tf = fl(grid, iters) / (ms * 1e-3) / 1e12
+    return {"TFLOP_s": round(tf, 1), "frac_of_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+            "ms_per_launch": round(ms, 4),
+            "config": f"{grid} workgroups x 4 waves, {iters} rounds of 8 independent "
+                      f"v_mfma_f32_16x16x128_f8f6f4 per wave, fp8 weight bytes as operands"}
 
 
 def quantize_bytes(M: int, K: int) -> int:
@@ -309,6 +374,97 @@ def rowwise_block(torch, g, inputgen, oracle, dev, replays):
     return out
 
 
+PREFILL_POINTS = [(M, N) for N in (14336, 16384) for M in (512, 2048, 6016, 8192)]
+DECODE_SHAPES = {"out_proj": (5120, 6144), "gate_up": (34816, 5120)}
+
+
+def check_rows(y_rows, ref, what):
+    """The parity bar on sampled rows: rel-L2 <= 3e-3 and the max-error rule (|err| <= 2e-2 rms(ref),
+    or the GPU value is one of the two bf16 neighbours of the exact result)."""
+    rel = float(np.linalg.norm(y_rows - ref) / np.linalg.norm(ref))
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rel > 3e-3 or not np.all(np.isfinite(y_rows)):
+        raise SystemExit(f"parity gate failed ({what}): rel_l2={rel:.3e}")
+    bad = np.abs(y_rows - ref) > 2e-2 * rms
+    if bad.any():
+        f, e = np.frexp(ref[bad])
+        lo = np.ldexp(np.floor(np.abs(f) * 256) / 256, e)
+        hi = np.ldexp(np.ceil(np.abs(f) * 256) / 256, e)
+        v = np.abs(y_rows[bad])
+        if not np.all((v == lo) | (v == hi)):
+            raise SystemExit(f"parity gate failed ({what}): max-error rule")
+    return rel
+
+
+def prefill_block(torch, g, inputgen, oracle, dev, points):
+    """Prefill points (K = 5120): per point a parity gate on sampled rows (first, middle, last and the
+    rows on both sides of three tile boundaries of the plan), then a HIP graph of 4 calls replayed
+    10 times; TFLOP/s and fraction of the 5 PF fp8 peak."""
+    Kp = 5120
+    Mmax = max(M for M, _ in points)
+    A8, a8 = inputgen.make_activations(Mmax, Kp, seed=0)
+    dA8, da8 = torch.from_numpy(A8).to(dev), torch.from_numpy(a8).to(dev)
+    out_res = {}
+    for Np in sorted({N for _, N in points}):
+        Wp, wp = inputgen.make_weights(Np, Kp, seed=1)
+        dWp, dwp = torch.from_numpy(Wp).to(dev), torch.from_numpy(wp).to(dev)
+        for Mp in [M for M, N in points if N == Np]:
+            plan = g.gemm_a8w8_blockscale_plan(Mp, Np, Kp)
+            bm = plan["bm"]
+            rows = sorted({0, Mp // 2, Mp - 1} | {b + d for b in (bm, (Mp // bm // 2) * bm, (Mp // bm - 1) * bm)
+                                                  for d in (-1, 0) if 0 <= b + d < Mp})
+            out = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
+            g.gemm_a8w8_blockscale(dA8[:Mp], da8[:Mp], dWp, dwp, out=out)
+            torch.cuda.synchronize()
+            yh = out[rows].float().cpu().numpy().astype(np.float64)
+            rel = check_rows(yh, oracle.gemm(A8[:Mp], a8[:Mp], Wp, wp, rows=rows), f"prefill M={Mp} N={Np}")
+            gp = time_graph(torch, [lambda: g.gemm_a8w8_blockscale(dA8[:Mp], da8[:Mp], dWp, dwp, out=out)] * 4, 0, 2)
+            ms = timed_replays(torch, gp, 10) / 4
+            tf = flops(Mp, Np, Kp) / (ms * 1e-3) / 1e12
+            out_res[f"M{Mp}_N{Np}_K{Kp}"] = {"us_per_call": round(ms * 1000, 2), "TFLOP_s": round(tf, 1),
+                                             "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4), "plan": plan["name"],
+                                             "parity_rows": len(rows), "parity_rel_l2": round(rel, 6)}
+            log(f"prefill M={Mp} N={Np}: {out_res[f'M{Mp}_N{Np}_K{Kp}']}")
+            del gp, out
+        del dWp
+    return out_res
+
+
+def cpu_baseline_block(inputgen, oracle, A, a_s, W0, w_s, Ms, N, K, seconds):
+    """The oracle as it stands, on the host cores: the decode workload (full outputs, ~`seconds`),
+    the tiny configuration (full, median of 3) and the prefill configuration M = 8192, N = 14336
+    on a bounded sample of rows (the time per row scaled to all 8192 rows: every row of Y costs the
+    same N x K products)."""
+    n_calls, t_cpu = 0, 0.0
+    while t_cpu < seconds:
+        M = Ms[n_calls % len(Ms)]
+        t = time.time()
+        oracle.gemm(A[:M], a_s[:M], W0, w_s)
+        t_cpu += time.time() - t
+        n_calls += 1
+    At, at = inputgen.make_activations(4, 1024, seed=0)
+    Wt, wt = inputgen.make_weights(512, 1024, seed=1)
+    tiny = []
+    for _ in range(3):
+        t = time.time()
+        oracle.gemm(At, at, Wt, wt)
+        tiny.append(time.time() - t)
+    Ap, ap_ = inputgen.make_activations(64, 5120, seed=0)
+    Wp, wp = inputgen.make_weights(14336, 5120, seed=1)
+    t = time.time()
+    oracle.gemm(Ap, ap_, Wp, wp)
+    per_row = (time.time() - t) / 64
+    return {"value": round(t_cpu / n_calls * 1e6, 1), "unit": "µs/call", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{n_calls} calls of the decode workload (M cycling {','.join(map(str, Ms))}; N={N}, K={K}; "
+                      f"fp64, full output) on the host cores",
+            "host_cpu_count": os.cpu_count(), "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
+            "threads_used": oracle.threads(),
+            "tiny_M4_N512_K1024_us": round(float(np.median(tiny)) * 1e6, 1),
+            "prefill_M8192_N14336_K5120_us": round(per_row * 8192 * 1e6, 1),
+            "prefill_sample": "64 rows of the M = 8192, N = 14336, K = 5120 prefill (full N), time per row x 8192"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,9 +472,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode-shapes", action="store_true",
+                    help="skip the out_proj (5120:6144) and gate_up (34816:5120) decode shapes")
+    ap.add_argument("--prefill-points", default=None,
+                    help="with --workload prefill: M:N[,M:N...] (K = 5120) to run, one after another")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--workload", choices=["decode", "sweep"], default="decode",
-                    help="decode: the headline decode workload (default); sweep: dense-M sweep report")
+    ap.add_argument("--workload", choices=["decode", "sweep", "prefill"], default="decode",
+                    help="decode: the headline decode workload and every other leg (default); sweep: the "
+                         "dense-M sweep report; prefill: only the prefill points (for per-point profiles)")
     ap.add_argument("--sweep-out", default=None, help="where the sweep writes its per-point table (markdown)")
     ap.add_argument("--decode-nk", default="14336:5120",
                     help="N:K of the decode workload (default: the qkv shape 14336:5120)")
@@ -346,6 +507,12 @@ def main():
 
     if args.workload == "sweep":
         return sweep(args, torch, g, inputgen, oracle)
+    if args.workload == "prefill":
+        pts = PREFILL_POINTS if not args.prefill_points else \
+            [tuple(int(x) for x in p.split(":")) for p in args.prefill_points.split(",")]
+        res = prefill_block(torch, g, inputgen, oracle, dev, pts)
+        print(json.dumps({"metric": "prefill fp8 TFLOP/s", "points": res}), flush=True)
+        return None
 
     # ------------------------------------------------------------ decode, cold W
     N, K = (int(x) for x in args.decode_nk.split(":"))
@@ -442,37 +609,23 @@ def main():
     log("prepacked:", json.dumps(packed))
 
     # ------------------------------------------------------------ prefill (compute-bound)
-    prefill = {}
-    if not args.no_prefill:
-        Kp = 5120
-        A8, a8 = inputgen.make_activations(8192, Kp, seed=0)
-        dA8 = torch.from_numpy(A8).to(dev)
-        da8 = torch.from_numpy(a8).to(dev)
-        for Np in (14336, 16384):
-            Wp, wp = inputgen.make_weights(Np, Kp, seed=1)
-            dWp = torch.from_numpy(Wp).to(dev)
-            dwp = torch.from_numpy(wp).to(dev)
-            rows = [0, 4095, 8191]
-            ref = oracle.gemm(A8, a8, Wp, wp, rows=rows)
-            for Mp in (512, 2048, 6016, 8192):
-                out = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
-                g.gemm_a8w8_blockscale(dA8[:Mp], da8[:Mp], dWp, dwp, out=out)
-                torch.cuda.synchronize()
-                rr = [r for r in rows if r < Mp]
-                yh = out[rr].float().cpu().numpy().astype(np.float64)
-                rel = float(np.linalg.norm(yh - ref[:len(rr)]) / np.linalg.norm(ref[:len(rr)]))
-                if rel > 3e-3:
-                    raise SystemExit(f"parity gate failed (prefill M={Mp} N={Np}): rel_l2={rel:.3e}")
-                gp = time_graph(torch, [lambda: g.gemm_a8w8_blockscale(dA8[:Mp], da8[:Mp], dWp, dwp, out=out)] * 4,
-                                0, 2)
-                ms = timed_replays(torch, gp, 10) / 4
-                tf = flops(Mp, Np, Kp) / (ms * 1e-3) / 1e12
-                prefill[f"M{Mp}_N{Np}_K{Kp}"] = {"us_per_call": round(ms * 1000, 2), "TFLOP_s": round(tf, 1),
-                                                 "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4),
-                                                 "plan": g.gemm_a8w8_blockscale_plan(Mp, Np, Kp)["name"]}
-                del gp, out
-            del dWp
-        log("prefill:", json.dumps(prefill))
+    prefill = {} if args.no_prefill else prefill_block(torch, g, inputgen, oracle, dev, PREFILL_POINTS)
+    log("prefill:", json.dumps(prefill))
+
+    # ------------------------------------------------------------ other decode shapes (out_proj, gate_up)
+    decode_shapes = {}
+    if not args.no_decode_shapes:
+        for name, (Nd, Kd) in DECODE_SHAPES.items():
+            decode_shapes[f"{name}_N{Nd}_K{Kd}"] = decode_shape_block(torch, g, inputgen, oracle, dev, Nd, Kd,
+                                                                     list(range(1, 17)), max(5, args.steps // 5))
+            log(f"decode {name}:", json.dumps(decode_shapes[f"{name}_N{Nd}_K{Kd}"]))
+
+    # ------------------------------------------------------------ sustained MFMA ceiling
+    mfma_ceiling = mfma_ceiling_block(torch, dev, copies[0], 5)
+    log("mfma ceiling:", json.dumps(mfma_ceiling))
+    if prefill:
+        for v in prefill.values():
+            v["frac_of_mfma_ceiling"] = round(v["TFLOP_s"] / mfma_ceiling["TFLOP_s"], 4)
 
     # ------------------------------------------------------------ activation quantisation
     quant = quantize_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
@@ -489,17 +642,8 @@ def main():
     # ------------------------------------------------------------ CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
-        n_calls, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds:
-            M = Ms[n_calls % len(Ms)]
-            t = time.time()
-            oracle.gemm(A[:M], a_s[:M], W0, w_s)
-            t_cpu += time.time() - t
-            n_calls += 1
-        cpu = {"value": round(t_cpu / n_calls * 1e6, 1), "unit": "µs/call", "cores": oracle.threads(),
-               "kind": "oracle",
-               "sample": f"{n_calls} calls of the decode workload (M cycling 1,2,4,8,16; N={N}, K={K}; "
-                         f"fp64, full output) on the host cores"}
+        cpu = cpu_baseline_block(inputgen, oracle, A, a_s, W0, w_s, Ms, N, K, args.cpu_seconds)
+        log("cpu baseline:", json.dumps(cpu))
 
     res = {
         "metric": METRIC,
@@ -529,6 +673,8 @@ def main():
         "read_ceiling": ceiling,
         "prepacked_weights": packed,
         "prefill": prefill,
+        "decode_shapes": decode_shapes,
+        "mfma_ceiling": mfma_ceiling,
         "quantize": quant,
         "mx": mx,
         "rowwise": rowwise,

@@ -9,9 +9,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libgemm_a8w8.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("a8w8_api.hip", "a8w8_kernels.hip", "a8w8_quant.hip", "a8w8_prepack.hip")]
-# The benchmark's streaming-read ceiling (a measurement aid, a library of its own).
-READ_CEILING_LIB = os.path.join(HERE, "libread_ceiling.so")
-READ_CEILING_SRC = os.path.join(HERE, "csrc", "read_ceiling.hip")
+# The benchmark's measured ceilings (streaming read, sustained fp8 MFMA): measurement aids,
+# a library of their own.
+CEILINGS_LIB = os.path.join(HERE, "libceilings.so")
+CEILINGS_SRC = [os.path.join(HERE, "csrc", f) for f in ("read_ceiling.hip", "mfma_ceiling.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -43,21 +44,21 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB_PATH)
-    build_read_ceiling(verbose)
+    build_ceilings(verbose)
     return LIB_PATH
 
 
-def build_read_ceiling(verbose: bool = False) -> str:
-    """Compile the benchmark's streaming-read kernel into READ_CEILING_LIB."""
-    tmp = READ_CEILING_LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, READ_CEILING_SRC]
+def build_ceilings(verbose: bool = False) -> str:
+    """Compile the benchmark's read- and MFMA-ceiling kernels into CEILINGS_LIB."""
+    tmp = CEILINGS_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *CEILINGS_SRC]
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, READ_CEILING_LIB)
-    return READ_CEILING_LIB
+    os.replace(tmp, CEILINGS_LIB)
+    return CEILINGS_LIB
 
 
 if __name__ == "__main__":

@@ -432,15 +432,25 @@ def test_workspace_size_covers_counters_and_partials():
 
 # ---------------------------------------------------------------- benchmark read-ceiling kernel
 
-def test_read_ceiling_library_builds_and_checks_arguments():
-    # The benchmark's streaming-read kernel lives in a library of its own; bad arguments are
-    # refused before anything is launched.
+def test_ceilings_library_builds_and_checks_arguments():
+    # The benchmark's streaming-read and MFMA kernels live in a library of their own; bad
+    # arguments are refused before anything is launched.
     import ctypes
     import os
     from fp8_block_scaled_a8w8_amd import build as libbuild
-    if not os.path.exists(libbuild.READ_CEILING_LIB):
-        libbuild.build_read_ceiling()
-    lib = ctypes.CDLL(libbuild.READ_CEILING_LIB)
+    if not os.path.exists(libbuild.CEILINGS_LIB):
+        libbuild.build_ceilings()
+    lib = ctypes.CDLL(libbuild.CEILINGS_LIB)
+    mf = lib.a8w8_mfma_ceiling_launch
+    mf.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    mf.restype = ctypes.c_int
+    for args in ((None, 4, 16, 8, 10), (16, 1, 16, 8, 10), (16, 4, None, 8, 10), (16, 4, 16, 0, 10),
+                 (16, 4, 16, 8, 0)):
+        assert mf(*args, None) != 0, args
+    fl = lib.a8w8_mfma_ceiling_flops
+    fl.argtypes = [ctypes.c_int, ctypes.c_int]
+    fl.restype = ctypes.c_double
+    assert fl(512, 1000) == 512 * 4 * 1000 * 8 * 16 * 16 * 128 * 2
     fn = lib.a8w8_read_ceiling_launch
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     fn.restype = ctypes.c_int
