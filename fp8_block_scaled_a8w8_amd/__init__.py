@@ -41,7 +41,7 @@ A8W8_ERR_HIP = 5
 A8W8_ERR_PLAN = 6
 A8W8_ERR_WORKSPACE = 7
 SCALE_KINDS = {"block": 0, "mx": 1, "rowwise": 2}
-KERNEL_NAMES = {1: "skinny", 2: "tile", 3: "ptile", 4: "pskinny", 5: "tall"}
+KERNEL_NAMES = {1: "skinny", 2: "tile", 3: "ptile", 4: "pskinny", 5: "tall", 6: "rskinny"}
 
 EXPORTED = (
     "gemm_a8w8_blockscale",

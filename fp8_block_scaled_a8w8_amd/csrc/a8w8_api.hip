@@ -130,9 +130,13 @@ bool skinny_fits(int64_t N, int64_t K)
     return ((N + 15) & ~(int64_t)15) * K < ((int64_t)1 << 32) && 16 * K < ((int64_t)1 << 32);
 }
 
-bool variant_accepts(int id, int64_t M, int64_t N, int64_t K)
+// `cus`: compute units of the device (0: not known yet; the row-range skinny
+// instances, whose grid depends on it, are then checked again at launch).
+bool variant_accepts(int id, int64_t M, int64_t N, int64_t K, int cus)
 {
     const Variant &v = a8w8::variant(id);
+    if (v.kernel == A8W8_KERNEL_RSKINNY)
+        return M <= v.max_m && skinny_fits(N, K) && (cus <= 0 || a8w8::rskinny_rows_fit(id, N, cus));
     // Split K: at least two K blocks per split, and a workspace within the cap.
     if (v.splits > 1 && (K / 128 < 2 * (int64_t)v.splits || a8w8::variant_workspace_bytes(id, M, N) > kMaxWorkspace))
         return false;
@@ -213,7 +217,7 @@ void heuristic_variants(int64_t M, int64_t N, int64_t K, int cus, int *split, in
             *split = *unsplit = best;
             if ((N + 15) / 16 < 32) {
                 const int sid = find_variant(A8W8_KERNEL_SKINNY, 16, 16, 4, 3, 4);
-                if (sid >= 0 && variant_accepts(sid, M, N, K))
+                if (sid >= 0 && variant_accepts(sid, M, N, K, cus))
                     *split = sid;
             }
             return;
@@ -251,7 +255,7 @@ void heuristic_variants(int64_t M, int64_t N, int64_t K, int cus, int *split, in
         if (K / 128 < 4 * (int64_t)s)
             break;
         const int sid = find_variant(A8W8_KERNEL_TILE, 32, 32, bv.waves, bv.kblocks, s);
-        if (sid < 0 || !variant_accepts(sid, M, N, K))
+        if (sid < 0 || !variant_accepts(sid, M, N, K, cus))
             continue;
         *split = sid;
         if (tiles * s >= cus)
@@ -286,10 +290,10 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t 
         }
         if (lo < s.count) {
             const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo], s.kblocks[lo], s.splits[lo]);
-            if (v >= 0 && variant_accepts(v, M, N, K) && workspace_need(v, M, N, batch) <= ws_bytes)
+            if (v >= 0 && variant_accepts(v, M, N, K, cus) && workspace_need(v, M, N, batch) <= ws_bytes)
                 return {v, s.key_m[lo], 0};
             const int u = find_variant(s.u_kernel[lo], s.u_bm[lo], s.u_bn[lo], s.u_waves[lo], s.u_kblocks[lo], 1);
-            if (u >= 0 && variant_accepts(u, M, N, K))
+            if (u >= 0 && variant_accepts(u, M, N, K, cus))
                 return {u, s.key_m[lo], 0};
         }
         break;
@@ -438,7 +442,7 @@ int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
         return rc;
     if (M == 0 || o.batch == 0)
         return A8W8_OK;
-    if (variant >= 0 && !variant_accepts(variant, M, N, K))
+    if (variant >= 0 && !variant_accepts(variant, M, N, K, 0))
         return A8W8_ERR_PLAN;
     if (variant >= 0 && workspace_need(variant, M, N, o.batch) > o.ws_bytes)
         return A8W8_ERR_WORKSPACE;
@@ -449,6 +453,8 @@ int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
     rc = device_ready(&cus);
     if (rc != A8W8_OK)
         return rc;
+    if (variant >= 0 && !variant_accepts(variant, M, N, K, cus))
+        return A8W8_ERR_PLAN;
     int id = variant;
     if (id < 0) {
         // Row-wise calls use the block-scale tables: same kernels and loads, less
@@ -474,7 +480,7 @@ int plan_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
     const int cus = cu_count > 0 ? cu_count : 256;
     const int64_t Mp = M > 0 ? M : 1, batch = o.batch > 0 ? o.batch : 1;
     if (variant >= 0) {
-        if (!variant_accepts(variant, Mp, N, K))
+        if (!variant_accepts(variant, Mp, N, K, cus))
             return A8W8_ERR_PLAN;
         if (workspace_need(variant, Mp, N, batch) > o.ws_bytes)
             return A8W8_ERR_WORKSPACE;

@@ -13,7 +13,7 @@ struct Variant {
     int32_t waves;     // waves per workgroup
     int32_t kblocks;   // K blocks each wave loads (skinny, pskinny), LDS ring depth (tile)
     int32_t max_m;     // largest M the instance accepts (skinny, pskinny: 16), 0 = any
-    int32_t per_cu;    // ptile, pskinny: workgroups per CU the persistent grid is sized for
+    int32_t per_cu;    // ptile, pskinny, rskinny: workgroups per CU the grid is sized for
     int32_t splits;    // tile: workgroups per output tile, each taking 1/splits of K (1: no split)
     const char *name;
 };
@@ -51,6 +51,10 @@ int64_t variant_counters(int id, int64_t M, int64_t N);
 // (skinny: ceil(K/128 / (waves * kblocks)); pskinny: 1; tile: K/128 blocks per tile).
 int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus);
 int64_t variant_passes(int id, int64_t K);
+// Row-range skinny instances: their grid (row-major or packed weights) and whether
+// every workgroup's run of rows fits the instance's tiles on a device with `cus` CUs.
+int64_t rskinny_grid(int id, int64_t N, int cus, bool packed);
+bool rskinny_rows_fit(int id, int64_t N, int cus);
 // Raise the dynamic-LDS limit of the instances that need more than 64 KB
 // (once per device, with that device current).
 hipError_t set_kernel_attributes();

@@ -616,6 +616,219 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 }
 
 // ---------------------------------------------------------------------------
+// Row-range skinny kernel ("rskinny"), M <= 16 (decode): every compute unit
+// streams an equal share of the weight rows.  The row-group kernel above gives
+// each workgroup whole 16-row tiles, so the tile count per workgroup is an
+// integer and N = 14336 (896 tiles) either leaves CUs idle (224 workgroups of
+// four tiles) or loads some CUs more than others; N = 5120 (320 tiles) had
+// 160 workgroups of two tiles.  Here workgroup b of G (about one per CU) owns
+// the rows [r0, r1) of a split of N into G nearly equal runs of RG-row units
+// (RG = 4 for row-major weights: 56 rows per CU at N = 14336 and 20 at
+// N = 5120; 16 for packed weights, whose tiles are 16-row aligned).  T 16-row
+// tiles cover the run, the last one partly: lanes on rows at or past r1 load
+// through an out-of-range offset, which returns zeros without touching memory,
+// and their outputs are never stored.
+//
+// Scales: each wave fetches the activation scales of its pass (M rows x D
+// blocks) with one word per lane and shares them through its own LDS slot (a
+// per-lane load of a_scale[m][kb] in every block touched sixteen cache lines
+// for 64 bytes at M = 16, which measured ~0.9 us on N = 14336); block-scale
+// weight scales come through scalar loads of the two scale rows the run can
+// span, so a tile may straddle a 128-row boundary: each output row takes its
+// own row's scale (MX: each lane passes its own row's 32-row scale word to the
+// scaled MFMA).  Otherwise as the row-group kernel: NW waves split K into runs
+// of D blocks (passes if NW * D < K/128), whole-line weight loads with the
+// DPP fix (packed: two contiguous kilobytes), one activation fragment per
+// block feeding T MFMAs, and the wave partials summed through LDS in wave
+// order (bitwise reproducible), rounded once to bf16.
+// Rows [r0, r1) of workgroup b of G: RG-row units split as evenly as integers allow.
+template <bool PK>
+__device__ __forceinline__ void rsk_rows(int b, int G, int N, int &r0, int &r1)
+{
+    constexpr int RG = PK ? 16 : 4;
+    const int units = (N + RG - 1) / RG;
+    r0 = RG * (int)((int64_t)b * units / G);
+    r1 = min(N, RG * (int)((int64_t)(b + 1) * units / G));
+}
+
+template <int T, int D, int NW, bool PK, int SM>
+__global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
+{
+    select_batch(p);
+    constexpr bool MX = SM == SM_MX, PER_BLOCK_SCALES = SM != SM_ROWWISE;
+    constexpr int SH = wscale_shift<SM>();
+    constexpr int AS32 = (16 * D + 63) / 64;                  // a_scale words per lane per pass
+    static_assert(T <= NW, "wave t sums and stores tile t");
+    __shared__ float s_as[NW][16 * D];                         // this wave's a_scale [m][block of the pass]
+    __shared__ v4f red[NW][T][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
+    int r0, r1;
+    rsk_rows<PK>((int)blockIdx.x, (int)gridDim.x, N, r0, r1);
+    const int r16 = lane & 15, g = lane >> 4, lrow = r16 & 7;
+    const uint32_t lcol = (uint32_t)(g + 4 * (r16 >> 3)) * 16;
+    constexpr uint32_t OOB = 0x7ffff000u;                     // beyond any buffer: loads return zeros
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.W, 0u);   // zero records: every load returns zeros
+    const __amdgpu_buffer_rsrc_t sares = buffer_rsrc(p.a_scale, PER_BLOCK_SCALES ? (uint32_t)(M * KB) * 4u : 0u);
+    const int NB = (N + (1 << SH) - 1) >> SH;
+    const int sb0 = min(r0, N - 1) >> SH;
+    // Block scale: the run's rows lie in weight-scale rows sb0 and sb0 + 1 (scalar loads).
+    const_f32 *wsp0 = (const_f32 *)(p.w_scale + (size_t)sb0 * KB);
+    const_f32 *wsp1 = (const_f32 *)(p.w_scale + (size_t)min(sb0 + 1, NB - 1) * KB);
+    // Row-wise: the scales of the tile this wave stores.
+    const RowScales rs = rowwise_fetch<SM>(p, r16, min(r0 + 16 * wave + 4 * g, N - 1));
+
+    // Per-lane load offsets.  Row layout: load h of a tile takes row 8h + (r16 & 7),
+    // chunk g + 4 (r16 >> 3) (whole lines, DPP fix below); packed: lane l reads
+    // bytes 16 l (+1024) of the tile's block.  Rows at or past r1, M: out of range.
+    uint32_t woff[T][2];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (PK) {
+                woff[t][h] = r0 + 16 * t < r1 ? (uint32_t)(lane * 16 + h * 1024) : OOB;
+            } else {
+                const int row = r0 + 16 * t + 8 * h + lrow;
+                woff[t][h] = row < r1 ? (uint32_t)row * (uint32_t)K + lcol : OOB;
+            }
+        }
+    uint32_t aoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int m = 8 * h + lrow;
+        aoff[h] = m < M ? (uint32_t)m * (uint32_t)K + lcol : OOB;
+    }
+    // Block scale: output rows n = r0 + 16 t + 4 g + i take scale row sb0 or sb0 + 1.
+    bool second[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            second[t][i] = ((r0 + 16 * t + 4 * g + i) >> SH) > sb0;
+    // MX: the scale-row offset (words) of this lane's own weight row in tile t.
+    uint32_t mxoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        mxoff[t] = (uint32_t)(min(r0 + 16 * t + r16, N - 1) >> SH) * (uint32_t)KB * 4u;
+    const __amdgpu_buffer_rsrc_t swres = buffer_rsrc(p.w_scale, MX ? (uint32_t)NB * (uint32_t)KB * 4u : 0u);
+
+    v4f acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    v4i ar[D][2];
+    v4i wr[D][T][2];
+    float asv[AS32];
+    float mxw[D][T];
+    // Issue every load of the pass starting at block kb_begin: first this wave's
+    // activation scales (one word per lane: rows m < M, blocks of the pass, in
+    // consecutive words of each row), then the weights and activations; blocks
+    // past K read through the zero-record descriptor (no traffic).
+    auto issue = [&](int kb_begin) {
+        if constexpr (PER_BLOCK_SCALES) {
+#pragma unroll
+            for (int u = 0; u < AS32; ++u) {
+                const int i = lane + 64 * u, m = i / D, j = i - m * D;
+                const bool ok = m < M && kb_begin + j < KB;
+                asv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       sares, ok ? (m * KB + kb_begin + j) * 4 : (int)OOB, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int kb = kb_begin + j;
+            const bool live = kb < KB;
+            const int koff = (live ? kb : 0) * 128;
+            const __amdgpu_buffer_rsrc_t rw = live ? wres : none, ra = live ? ares : none;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int so = PK ? (int)packed_block((uint32_t)((r0 >> 4) + t), (uint32_t)(live ? kb : 0),
+                                                      (uint32_t)KB) : koff;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[t][h], so, 2 /* nt */);
+                if constexpr (MX)
+                    mxw[j][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                              live ? swres : none, (int)mxoff[t], (live ? kb : 0) * 4, 0));
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff[h], koff, 0);
+        }
+    };
+    // Multiply the pass starting at kb_begin.
+    auto consume = [&](int kb_begin) {
+        if constexpr (PER_BLOCK_SCALES) {
+            // this wave's scales into its own LDS slot (read back by other lanes of the wave)
+#pragma unroll
+            for (int u = 0; u < AS32; ++u)
+                if (lane + 64 * u < 16 * D)
+                    s_as[wave][lane + 64 * u] = asv[u];
+            __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the wave's LDS writes are done
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int kb = kb_begin + j;
+            if (kb < KB) {
+                const v8i af = fix_row_layout(ar[j][0], ar[j][1]);
+                const float sa = PER_BLOCK_SCALES ? s_as[wave][min(r16, M - 1) * D + j] : 0.f;
+                float sc0 = 0.f, sc1 = 0.f;
+                if constexpr (SM == SM_BLOCK) {
+                    sc0 = sa * wsp0[kb];
+                    sc1 = sa * wsp1[kb];
+                }
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const v8i wf = w_fragment(wr[j][t][0], wr[j][t][1], PK);
+                    if constexpr (SM == SM_BLOCK) {
+                        const v4f d = mfma_block(wf, af);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[t][i] = __builtin_fmaf(d[i], second[t][i] ? sc1 : sc0, acc[t][i]);
+                    } else {
+                        acc[t] = block_step<SM>(acc[t], wf, af, MX ? mxw[j][t] : 0.f, sa, g);
+                    }
+                }
+            }
+        }
+        if constexpr (PER_BLOCK_SCALES)
+            __builtin_amdgcn_wave_barrier();       // the slot is rewritten by the next pass
+    };
+
+    for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
+        issue(kb_begin);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(kb_begin);
+    }
+
+    // Wave t sums tile t over the waves in wave order and stores it.
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        red[wave][t][lane] = acc[t];
+    __syncthreads();
+    if (wave < T) {
+        v4f v = red[0][wave][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            const v4f o = red[w][wave][lane];
+            v[0] += o[0];
+            v[1] += o[1];
+            v[2] += o[2];
+            v[3] += o[3];
+        }
+        const int n = r0 + 16 * wave + 4 * g;
+        if (r16 < M && n < r1)
+            store4(p.Y, (int64_t)r16 * N, n, N, vec_store != 0, rowwise_apply<SM>(v, rs));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tall kernel, N <= 16 * NT (a few weight rows, many activation rows): the
 // skinny kernel with the roles of the two dimensions exchanged.  Here the
 // activations are the stream read once from HBM and the small weight matrix
@@ -1659,6 +1872,9 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
                               FN6(tall_kernel<TPW, NT, D, NW), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
                            FN6(pskinny_kernel<D, NW, P), 0}
+// Row-range skinny: T tiles per workgroup at most, about G = WPC workgroups per CU.
+#define RSKINNY(T, D, NW, WPC) {{A8W8_KERNEL_RSKINNY, 16, 16 * T, NW, D, 16, WPC, 1, \
+                                 "rskinny_t" #T "_d" #D "_w" #NW "_g" #WPC}, FN6(rskinny_kernel<T, D, NW), 0}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
@@ -1682,6 +1898,8 @@ const Entry kEntries[] = {
     TILE_SK(64, 32, 2, 2, 3, 8), TILE_SK(32, 32, 2, 2, 3, 4), TILE_SK(32, 32, 2, 2, 3, 8),
     SKINNY_SK(1, 3, 4, 4), SKINNY_SK(1, 3, 8, 2), SKINNY_SK(2, 3, 8, 2), SKINNY_SK(4, 3, 4, 4),
     SKINNY_SK(2, 5, 4, 2), SKINNY_SK(4, 5, 4, 2), SKINNY_SK(1, 5, 2, 4), SKINNY_SK(2, 4, 8, 2),
+    RSKINNY(2, 3, 16, 1), RSKINNY(2, 6, 8, 1), RSKINNY(4, 5, 8, 1), RSKINNY(3, 5, 8, 1), RSKINNY(1, 5, 8, 2),
+    RSKINNY(1, 3, 16, 2), RSKINNY(2, 5, 8, 1), RSKINNY(4, 3, 8, 1),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -1691,12 +1909,33 @@ int num_variants() { return kNumEntries; }
 
 const Variant &variant(int id) { return kEntries[id].v; }
 
+int64_t rskinny_grid(int id, int64_t N, int cus, bool packed)
+{
+    const Variant &v = kEntries[id].v;
+    const int64_t units = packed ? (N + 15) / 16 : (N + 3) / 4;
+    const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * v.per_cu;
+    return units < slots ? units : slots;
+}
+
+bool rskinny_rows_fit(int id, int64_t N, int cus)
+{
+    const Variant &v = kEntries[id].v;
+    for (int packed = 0; packed < 2; ++packed) {
+        const int64_t rg = packed ? 16 : 4, units = (N + rg - 1) / rg, G = rskinny_grid(id, N, cus, packed != 0);
+        if (rg * ((units + G - 1) / G) > v.bn)
+            return false;
+    }
+    return true;
+}
+
 int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
 {
     (void)K;
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return (N + v.bn - 1) / v.bn * v.splits;
+    if (v.kernel == A8W8_KERNEL_RSKINNY)
+        return rskinny_grid(id, N, cus, false);
     if (v.kernel == A8W8_KERNEL_TALL)
         return (M + v.bm - 1) / v.bm;
     if (v.kernel == A8W8_KERNEL_PSKINNY) {
@@ -1718,7 +1957,7 @@ int64_t variant_passes(int id, int64_t K)
     const Variant &v = kEntries[id].v;
     if (v.kernel == A8W8_KERNEL_PSKINNY)
         return 1;
-    if (v.kernel != A8W8_KERNEL_SKINNY && v.kernel != A8W8_KERNEL_TALL)
+    if (v.kernel != A8W8_KERNEL_SKINNY && v.kernel != A8W8_KERNEL_TALL && v.kernel != A8W8_KERNEL_RSKINNY)
         return (K / 128 + v.splits - 1) / v.splits;
     const int64_t per_pass = (int64_t)v.waves * v.kblocks, per_split = (K / 128 + v.splits - 1) / v.splits;
     return (per_split + per_pass - 1) / per_pass;
@@ -1763,11 +2002,17 @@ hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t
     // the workspace that needs); the kernels read the count from a.splits.
     if (a.splits != e.v.splits)
         return hipErrorInvalidValue;
-    const int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
+    int64_t grid = variant_grid(id, a.M, a.N, a.K, cus);
     // The kernels number workgroups and tiles in 32 bits (and the x dimension of a
     // grid is limited to 2^31 - 1): refuse, never truncate, a larger grid.
     if (grid < 1 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
+    if (e.v.kernel == A8W8_KERNEL_RSKINNY) {
+        // packed weights split rows in 16-row units (the layout's tiles)
+        if (!rskinny_rows_fit(id, a.N, cus))
+            return hipErrorInvalidConfiguration;
+        grid = rskinny_grid(id, a.N, cus, a.wpk != 0);
+    }
     // 8-byte stores need every row (and, batched, every batch) 8-byte aligned.
     int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
     Args args = a;

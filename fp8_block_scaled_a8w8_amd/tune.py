@@ -38,7 +38,7 @@ import time
 
 import torch
 
-from . import Workspace, gemm_a8w8_ex, variants
+from . import A8W8Error, Workspace, gemm_a8w8_ex, gemm_a8w8_ex_plan, variants
 from . import gen_selector_table as gst
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +106,15 @@ def candidates(M: int, N: int, K: int) -> list[dict]:
         if v["kernel_name"] == "pskinny":
             if M <= 16 and K // 128 <= v["waves"] * v["kblocks"]:
                 out.append(v)
+            continue
+        if v["kernel_name"] == "rskinny":
+            # the instance must take the shape: each workgroup's run of rows within its tiles
+            if M <= 16:
+                try:
+                    gemm_a8w8_ex_plan(M, N, K, variant=v["variant"])
+                    out.append(v)
+                except A8W8Error:
+                    pass
             continue
         if v["kernel_name"] == "tall":
             if N <= v["bn"] < 2 * max(N, 16):
@@ -197,13 +206,15 @@ def _measure(cands, make_calls, R: int, rounds: int) -> dict:
 
 def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
                mx: bool = False, batch: int = 1, results_path: str = RESULTS, max_copies: int = 256,
-               production: dict | None = None) -> list[dict]:
+               production: dict | None = None, retune=()) -> list[dict]:
     import inputgen
     dev = "cuda:0"
     prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
     grid = key_grid(extra=MX_EXTRA_KEYS if mx else ())
+    done = {k: v for k, v in done.items() if not (k.startswith(f"{prefix}{N}:{K}:") and
+                                                   int(k.rsplit(":", 1)[1]) in retune)}
     if all(f"{prefix}{N}:{K}:{M}" in done for M in grid):
-        return [done[f"{prefix}{N}:{K}:{M}"] for M in grid]      # all measured: no GPU needed
+        return [row_from_log(done[f"{prefix}{N}:{K}:{M}"]) for M in grid]   # all measured: no GPU needed
     (dA, da), W0, dw = _operands(N, K, mx, batch)
     R = max(2, math.ceil(rotate_gib * 2**30 / (W0.nbytes + dw.numel() * dw.element_size())))
     R = min(R, max_copies)          # tiny weights: bounded graphs (the activations dominate the traffic there)
@@ -216,7 +227,7 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
     for M in grid:
         key = f"{prefix}{N}:{K}:{M}"
         if key in done:
-            rows.append(done[key])
+            rows.append(row_from_log(done[key]))
             continue
         cands = candidates(M, N, K)
         if mx:
@@ -293,12 +304,28 @@ def parse_instance(name: str) -> dict:
         kern, bm, bn, wm, wn, st, sk = m.groups()
         return {"name": name, "kernel_name": kern, "bm": int(bm), "bn": int(bn), "waves": int(wm) * int(wn),
                 "kblocks": int(st), "splits": int(sk or 1)}
+    m = re.fullmatch(r"rskinny_t(\d+)_d(\d+)_w(\d+)_g(\d+)", name)
+    if m:
+        t, d, nw, _ = m.groups()
+        return {"name": name, "kernel_name": "rskinny", "bm": 16, "bn": 16 * int(t), "waves": int(nw),
+                "kblocks": int(d), "splits": 1}
     m = re.fullmatch(r"tall_r(\d+)_n(\d+)_d(\d+)_w(\d+)", name)
     if m:
         tpw, nt, d, nw = m.groups()
         return {"name": name, "kernel_name": "tall", "bm": 16 * int(tpw), "bn": 16 * int(nt), "waves": int(nw),
                 "kblocks": int(d), "splits": 1}
     raise ValueError(f"unknown instance name {name}")
+
+
+def row_from_log(rec: dict) -> dict:
+    """The table row for a logged measurement: a logged two-re-measurement decision stands as it
+    is; otherwise the first rule picks from the logged candidate times."""
+    if rec.get("remeasure") is not None or not rec.get("candidates"):
+        return rec
+    med = dict(rec["candidates"])
+    row = pick_row(int(rec["key_m"]), med, {n: parse_instance(n) for n in med})
+    row["remeasure"] = None
+    return row
 
 
 def rebuild(results_path: str = RESULTS) -> dict:
@@ -319,11 +346,7 @@ def rebuild(results_path: str = RESULTS) -> dict:
             rec = done.get(f"{prefix}{sh['n']}:{sh['k']}:{r['key_m']}")
             if rec is None or not rec.get("candidates"):
                 raise ValueError(f"no measurement for key {prefix}{sh['n']}:{sh['k']}:{r['key_m']}")
-            med = dict(rec["candidates"])
-            by_name = {n: parse_instance(n) for n in med}
-            row = pick_row(int(r["key_m"]), med, by_name)
-            row["remeasure"] = rec.get("remeasure")
-            rows.append(table_row(row))
+            rows.append(table_row(row_from_log(rec)))
         out.append({**{k: v for k, v in sh.items() if k != "rows"}, "rows": rows})
     return {"shapes": out}
 
@@ -337,6 +360,8 @@ def main(argv=None) -> int:
     ap.add_argument("--max-copies", type=int, default=256, help="at most this many weight copies per graph")
     ap.add_argument("--fresh", action="store_true", help="ignore earlier results")
     ap.add_argument("--results", default=RESULTS, help="measurement log to resume from and append to")
+    ap.add_argument("--keys", default="",
+                    help="key M values to measure again even if the log has them, e.g. 1-16 or 1,2,4")
     ap.add_argument("--rebuild", action="store_true",
                     help="rewrite tuned_table.json from the measurement log (no GPU), then exit")
     args = ap.parse_args(argv)
@@ -359,6 +384,10 @@ def main(argv=None) -> int:
             for line in f:
                 rec = json.loads(line)
                 done[rec["key"]] = rec["row"]
+    retune = set()
+    for part in filter(None, args.keys.split(",")):
+        lo, _, hi = part.partition("-")
+        retune.update(range(int(lo), int(hi or lo) + 1))
     table = gst.load()
     shapes = {(int(s["n"]), int(s["k"]), bool(s.get("mx", False))): s for s in table["shapes"]}
     default = REGISTERED_MX if args.mx else [f"{n}:{k}" for n, k in REGISTERED]
@@ -369,7 +398,7 @@ def main(argv=None) -> int:
         t = time.time()
         rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log, mx=args.mx, batch=batch,
                           results_path=args.results, max_copies=args.max_copies,
-                          production=shapes.get((N, K, args.mx)))
+                          production=shapes.get((N, K, args.mx)), retune=retune)
         entry = {"n": N, "k": K, "rows": [table_row(r) for r in rows]}
         if args.mx:
             entry = {"n": N, "k": K, "mx": True, "batch": batch, "rows": entry["rows"]}

@@ -129,6 +129,9 @@ def test_variant_shapes_are_launchable():
             assert 2 * (v["bm"] + v["bn"]) * 128 <= 160 * 1024
         elif v["kernel_name"] == "tall":
             assert v["bn"] in (16, 32) and v["bm"] in (16, 32, 64), v     # all weight rows in weight block 0
+        elif v["kernel_name"] == "rskinny":
+            assert v["bm"] == 16 and v["bn"] % 16 == 0 and v["bn"] <= 128, v   # at most two weight-scale rows
+            assert v["bn"] // 16 <= v["waves"], v                          # wave t stores tile t
         else:
             assert v["bm"] == 16 and v["bn"] in (16, 32, 64, 128), v   # row group inside one weight block
             assert v["waves"] >= 1 and v["kblocks"] >= 1
@@ -274,7 +277,7 @@ def test_mx_every_m_has_a_tuned_plan_within_125_percent(N, K):
         assert M <= p["key_m"] <= 1.25 * M, (M, p)
         if M <= 16:
             assert p["key_m"] == M
-        if p["kernel_name"] in ("skinny", "pskinny"):
+        if p["kernel_name"] in ("skinny", "pskinny", "rskinny"):
             assert M <= 16
 
 
@@ -293,7 +296,7 @@ def test_mx_unregistered_shape_gets_a_valid_heuristic_plan(M, N, K):
     p = g.gemm_a8w8_mxscale_plan(M, N, K)
     assert p["fallback"] == 1 and p["key_m"] == M
     assert 0 <= p["variant"] < g.gemm_a8w8_num_variants()
-    if p["kernel_name"] in ("skinny", "pskinny"):
+    if p["kernel_name"] in ("skinny", "pskinny", "rskinny"):
         assert M <= 16
     if p["kernel_name"] == "tall":
         assert N <= p["bn"]
@@ -346,6 +349,30 @@ def test_split_instances_beyond_the_workspace_cap_are_rejected():
     # 8 splits x (M x N) fp32 partials far above 128 MB
     rc = g.lib().gemm_a8w8_blockscale_run_variant(v["variant"], 16, 16, 16, 16, 16, 8192, 8192, 4096, None)
     assert rc == g.A8W8_ERR_PLAN
+
+
+def test_rskinny_instances_split_rows_evenly_or_refuse():
+    """Row-range skinny instances take a shape only when every workgroup's run of rows fits their
+    tiles (row-major runs of 4-row units, packed runs of 16-row tiles), at the device's CU count."""
+    rs = [v for v in g.variants() if v["kernel_name"] == "rskinny"]
+    assert rs
+    for v in rs:
+        T = v["bn"] // 16
+        wpc = g.gemm_a8w8_describe_variant(v["variant"], 1, 1 << 20, 1024)["grid"] // 256
+        for N in (64, 300, 5120, 5122, 14336, 16384, 34816):
+            for cus in (256, 80):
+                G4 = min(-(-N // 4), cus * wpc)
+                G16 = min(-(-N // 16), cus * wpc)
+                fits = 4 * -(-(-(-N // 4)) // G4) <= 16 * T and 16 * -(-(-(-N // 16)) // G16) <= 16 * T
+                p = g.Plan()
+                d = g.GemmDesc(None, None, None, None, None, 1, 8, N, 1024, 0, 0, v["variant"], 0, None, 0)
+                rc = g.lib().gemm_a8w8_ex_plan(ctypes.byref(d), cus, ctypes.byref(p))
+                assert (rc == g.A8W8_OK) == fits, (v["name"], N, cus, rc)
+                if fits:
+                    assert p.grid == G4
+        assert g.lib().gemm_a8w8_ex_plan(ctypes.byref(g.GemmDesc(None, None, None, None, None, 1, 17, 5120, 1024,
+                                                                  0, 0, v["variant"], 0, None, 0)), 0,
+                                         ctypes.byref(g.Plan())) == g.A8W8_ERR_PLAN     # M > 16
 
 
 def test_plans_report_splits():

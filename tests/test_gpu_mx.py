@@ -55,6 +55,8 @@ def _shape_for(v, cus):
         return 9, 300
     if k == "pskinny":
         return 9, 16 * (2 * cus + 37) + 5
+    if k == "rskinny":
+        return 9, 20 * cus + 2           # runs of 24 rows: tiles straddle 32-row scale blocks
     if k == "tall":
         return 3 * v["bm"] + 5, v["bn"] - 3
     per_cu = g.gemm_a8w8_describe_variant(v["variant"], 1 << 24, 1 << 16, 640)["grid"] // 256
@@ -149,7 +151,7 @@ def test_batched_ragged_every_kernel_family():
         rows = _rows(M)
         for i in range(3):
             assert_parity(yh[i][rows], oracle.gemm_mx(A[i], a[i], W[i], w[i], rows=rows), f"{v['name']} batch {i}")
-    assert seen == {"skinny", "pskinny", "tall", "tile", "ptile"}
+    assert seen == {"skinny", "pskinny", "tall", "tile", "ptile", "rskinny"}
 
 
 def test_integer_case_bitwise():
@@ -166,7 +168,7 @@ def test_integer_case_bitwise():
     ref = bf16_round(oracle.gemm_mx(A, a, W, w))
     for vid in range(g.gemm_a8w8_num_variants()):
         v = g.gemm_a8w8_describe_variant(vid)
-        if v["kernel_name"] in ("skinny", "pskinny") or (v["kernel_name"] == "tall" and v["bn"] < N) \
+        if v["kernel_name"] in ("skinny", "pskinny", "rskinny") or (v["kernel_name"] == "tall" and v["bn"] < N) \
                 or K // 128 < 2 * v["splits"]:
             continue
         y = y_host(g.gemm_a8w8_mxscale_run_variant(vid, dA, da, dW, dw, workspace=shared_workspace()))

@@ -46,6 +46,8 @@ def _shape_for(v, cus):
     k = v["kernel_name"]
     if k == "skinny":
         return 9, 300
+    if k == "rskinny":
+        return 9, 20 * cus + 2
     if k == "pskinny":
         return 9, 16 * (2 * cus + 37) + 5
     if k == "tall":

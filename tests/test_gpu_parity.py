@@ -146,7 +146,7 @@ def test_every_instance_on_ragged_shape(name):
     variant = info["variant"]
     ws = shared_workspace()
     K = max(640, 256 * info["splits"])   # split-K instances need >= 2 K blocks per split
-    if info["kernel_name"] in ("skinny", "pskinny"):
+    if info["kernel_name"] in ("skinny", "pskinny", "rskinny"):
         shapes = [(1, 300), (7, 130), (16, 64)]
     elif info["kernel_name"] == "tall":
         shapes = [(300, info["bn"]), (1000, info["bn"] - 5), (77, 3), (5, info["bn"])]

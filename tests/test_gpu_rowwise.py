@@ -38,6 +38,8 @@ def _shape_for(v, cus):
     k = v["kernel_name"]
     if k == "skinny":
         return 9, 300
+    if k == "rskinny":
+        return 9, 20 * cus + 2
     if k == "pskinny":
         return 9, 16 * (2 * cus + 37) + 5
     if k == "tall":
@@ -92,7 +94,7 @@ def test_integer_case_bitwise():
     ref = bf16_round(oracle.gemm_rowwise(A, a, W, w))
     for vid in range(g.gemm_a8w8_num_variants()):
         v = g.gemm_a8w8_describe_variant(vid)
-        if v["kernel_name"] in ("skinny", "pskinny") or (v["kernel_name"] == "tall" and v["bn"] < N) \
+        if v["kernel_name"] in ("skinny", "pskinny", "rskinny") or (v["kernel_name"] == "tall" and v["bn"] < N) \
                 or K // 128 < 2 * v["splits"]:
             continue
         y = y_host(g.gemm_a8w8_rowwise_run_variant(vid, dA, da, dW, dw, workspace=shared_workspace()))
