@@ -4,8 +4,10 @@ Default workload (the decode configuration the headline metric is quoted on):
 M in {1, 2, 4, 8, 16}, N = 14336, K = 5120, fp8 e4m3 operands with 1x128 /
 128x128 fp32 scales, bf16 out, and the weights rotated over >= 2 GiB of
 distinct copies so that every call streams W from HBM (the 256 MB MALL cannot
-hold them).  One step = one HIP-graph replay of R calls, one per weight copy,
-cycling M through {1, 2, 4, 8, 16}; value = microseconds per call.
+hold them).  Each M has its own HIP graph of R calls, one per weight copy; one
+step replays the graph of every M once, and value = microseconds per call
+averaged over M (the pages quote each (M, N, K) row on its own).  The same
+calls in one graph with M cycling call by call are reported beside it.
 
 Before any number is printed the GPU output is checked against the fp64 CPU
 oracle (first, middle and last weight copy, every M); a mismatch aborts the
@@ -511,6 +513,8 @@ def main():
         pts = PREFILL_POINTS if not args.prefill_points else \
             [tuple(int(x) for x in p.split(":")) for p in args.prefill_points.split(",")]
         res = prefill_block(torch, g, inputgen, oracle, dev, pts)
+        if args.calib_copy:
+            calib_copy(torch)
         print(json.dumps({"metric": "prefill fp8 TFLOP/s", "points": res}), flush=True)
         return None
 
@@ -541,35 +545,53 @@ def main():
         gate = max(gate, parity_gate(g, oracle, A, a_s, Wr, w_s, dA, da, copies[r], dw, Ms, f"copy {r}"))
     log(f"parity gate passed: worst rel_l2 {gate:.3e}")
 
-    outs = [torch.empty((Ms[r % len(Ms)], N), dtype=torch.bfloat16, device=dev) for r in range(R)]
-
-    def call(r):
-        M = Ms[r % len(Ms)]
-        return lambda: g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw, out=outs[r])
-
-    graph = time_graph(torch, [call(r) for r in range(R)], 0, args.warmup)
-    t_wall = time.time()
-    ms_per_step = timed_replays(torch, graph, args.steps)
-    wall = time.time() - t_wall
-    us_per_call = ms_per_step * 1000.0 / R
-    bytes_mean = sum(algorithmic_bytes(Ms[r % len(Ms)], N, K) for r in range(R)) / R
-    achieved = bytes_mean / (us_per_call * 1e-6) / 1e9
-    del graph
-
-    # per-M breakdown (same cold rotation, one M at a time)
-    per_m = {}
+    # One HIP graph per M, each of R calls over the R rotated weight copies (the pages time
+    # each (M, N, K) row on its own); one step replays the graphs of every M once, so a step
+    # is len(Ms) * R calls and the value is the mean over M of the per-call time.
+    graphs = {}
     for M in Ms:
         outM = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        gm = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw, out=outM))
-                                for r in range(R)], 0, 2)
-        ms = timed_replays(torch, gm, max(5, args.steps // 5))
+        graphs[M] = time_graph(torch, [(lambda r=r, M=M, outM=outM: g.gemm_a8w8_blockscale(
+            dA[:M], da[:M], copies[r], dw, out=outM)) for r in range(R)], 0, args.warmup)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.time()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        for M in Ms:
+            graphs[M].replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.time() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    us_per_call = ms_per_step * 1000.0 / (R * len(Ms))
+    bytes_mean = sum(algorithmic_bytes(M, N, K) for M in Ms) / len(Ms)
+    achieved = bytes_mean / (us_per_call * 1e-6) / 1e9
+
+    # per-M breakdown: each M's graph on its own
+    per_m = {}
+    for M in Ms:
+        ms = timed_replays(torch, graphs[M], max(5, args.steps // 5))
         us = ms * 1000.0 / R
         gbs = algorithmic_bytes(M, N, K) / (us * 1e-6) / 1e9
         per_m[str(M)] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                          "plan": g.gemm_a8w8_blockscale_plan(M, N, K)["name"]}
-        del gm
+    del graphs
     log("per-M:", json.dumps(per_m))
+
+    # The same calls in one graph with M cycling call by call (a different kernel instance may
+    # follow each call): reported beside the per-M value, not as it.
+    outs = [torch.empty((Ms[r % len(Ms)], N), dtype=torch.bfloat16, device=dev) for r in range(R)]
+    gmix = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale(dA[:Ms[r % len(Ms)]], da[:Ms[r % len(Ms)]],
+                                                                  copies[r], dw, out=outs[r])) for r in range(R)],
+                      0, 2)
+    us_mixed = timed_replays(torch, gmix, max(5, args.steps // 5)) * 1000.0 / R
+    del gmix
+    mixed = {"us_per_call": round(us_mixed, 3),
+             "note": f"one graph of {R} calls with M cycling {','.join(map(str, Ms))} call by call"}
+    log("mixed-M graph:", json.dumps(mixed))
 
     # the part's streaming-read ceiling at the same bytes per call
     ceiling = read_ceiling_block(torch, dev, round(bytes_mean), R, max(5, args.steps // 10), us_per_call)
@@ -584,13 +606,6 @@ def main():
             if not torch.equal(y_row.view(torch.int16), y_pk.view(torch.int16)):
                 raise SystemExit(f"parity gate failed (packed weights, copy {r}, M={M})")
 
-    def call_pk(r):
-        M = Ms[r % len(Ms)]
-        return lambda: g.gemm_a8w8_blockscale_packed(dA[:M], da[:M], pcopies[r], dw, N, out=outs[r])
-
-    graph = time_graph(torch, [call_pk(r) for r in range(R)], 0, args.warmup)
-    us_pk = timed_replays(torch, graph, args.steps) * 1000.0 / R
-    del graph
     per_m_pk = {}
     for M in Ms:
         outM = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -600,6 +615,7 @@ def main():
         per_m_pk[str(M)] = {"us_per_call": round(us, 3),
                             "hbm_frac": round(algorithmic_bytes(M, N, K) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del gm
+    us_pk = sum(v["us_per_call"] for v in per_m_pk.values()) / len(per_m_pk)
     packed = {"us_per_call": round(us_pk, 3),
               "hbm_frac": round(bytes_mean / (us_pk * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
               "per_m": per_m_pk,
@@ -661,8 +677,8 @@ def main():
         "config": {"workload": f"decode{' qkv-like' if qkv else ''}: M in {{{','.join(map(str, Ms))}}}, "
                                f"N={N}, K={K}, cold weights "
                                f"rotated over {R} copies ({R * w_bytes / 2**30:.2f} GiB); one step = one "
-                               f"HIP-graph replay of {R} calls",
-                   "calls_per_step": R, "rotate_bytes": R * w_bytes,
+                               f"HIP-graph replay of {R} calls for each M; value = mean over M of us/call",
+                   "calls_per_step": R * len(Ms), "rotate_bytes": R * w_bytes,
                    "table_hash": f"0x{g.gemm_a8w8_table_hash():016x}"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic() if qkv else None,
@@ -670,6 +686,7 @@ def main():
                                + ", ".join(sorted({v["plan"] for v in per_m.values()})),
                      "bytes_per_launch": round(bytes_mean)},
         "per_m": per_m,
+        "mixed_m_graph": mixed,
         "read_ceiling": ceiling,
         "prepacked_weights": packed,
         "prefill": prefill,
@@ -721,7 +738,7 @@ def sweep(args, torch, g, inputgen, oracle):
         copies = [torch.from_numpy(W0).to(dev)] + \
             [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
         picked = []
-        ws = g.Workspace(64 << 20)
+        ws = g.Workspace((128 << 20) + (1 << 20))
         for M in Ms:
             plan = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=ws.nbytes)
             fallbacks += plan["fallback"]

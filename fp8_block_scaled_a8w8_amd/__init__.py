@@ -41,7 +41,7 @@ A8W8_ERR_HIP = 5
 A8W8_ERR_PLAN = 6
 A8W8_ERR_WORKSPACE = 7
 SCALE_KINDS = {"block": 0, "mx": 1, "rowwise": 2}
-KERNEL_NAMES = {1: "skinny", 2: "tile", 3: "ptile", 4: "pskinny", 5: "tall", 6: "rskinny"}
+KERNEL_NAMES = {1: "skinny", 2: "tile", 3: "ptile", 4: "pskinny", 5: "tall", 6: "rskinny", 7: "sktile"}
 
 EXPORTED = (
     "gemm_a8w8_blockscale",
@@ -335,8 +335,8 @@ def gemm_a8w8_blockscale_run_variant(variant: int, A, a_scale, W, w_scale, out=N
 def gemm_a8w8_ex(A, a_scale, W, w_scale, *, scale_kind: str = "block", packed_n: int | None = None,
                  variant: int | None = None, workspace: Workspace | None = None, out=None, stream=None):
     """gemm_a8w8_ex of the C ABI: any scale kind ("block", "mx", "rowwise"), row-major or packed W
-    (packed_n = real row count), 2-D or batched (3-D, MX and block) operands, an optional forced
-    instance and an optional split-K workspace."""
+    (packed_n = real row count), 2-D operands or batched 3-D MX operands, an optional forced
+    instance and an optional workspace (split-K and stream-K plans)."""
     if scale_kind == "mx":
         batched = A.dim() == 3
         batch, M, N, K, out = _check_mx(A, a_scale, W, w_scale, out, batched, packed_n)

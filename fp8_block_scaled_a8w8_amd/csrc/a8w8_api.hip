@@ -137,8 +137,12 @@ bool variant_accepts(int id, int64_t M, int64_t N, int64_t K, int cus)
     const Variant &v = a8w8::variant(id);
     if (v.kernel == A8W8_KERNEL_RSKINNY)
         return M <= v.max_m && skinny_fits(N, K) && (cus <= 0 || a8w8::rskinny_rows_fit(id, N, cus));
-    // Split K: at least two K blocks per split, and a workspace within the cap.
-    if (v.splits > 1 && (K / 128 < 2 * (int64_t)v.splits || a8w8::variant_workspace_bytes(id, M, N) > kMaxWorkspace))
+    // Split K: at least two K blocks per split, and a workspace within the cap
+    // (stream-K: its partial slots on this device; 256 CUs while not known).
+    if (v.splits > 1 && K / 128 < 2 * (int64_t)v.splits)
+        return false;
+    if ((v.splits > 1 || v.kernel == A8W8_KERNEL_SKTILE) &&
+        a8w8::variant_workspace_bytes(id, M, N, K, cus > 0 ? cus : 256) > kMaxWorkspace)
         return false;
     if (v.kernel == A8W8_KERNEL_SKINNY)
         return M <= v.max_m && skinny_fits(N, K);
@@ -171,15 +175,21 @@ int find_variant(int kernel, int bm, int bn, int waves, int kblocks, int splits 
 // serves any number of calls in stream order.  Partials need no clearing.
 constexpr int64_t kCounterBytes = A8W8_WORKSPACE_COUNTER_BYTES;
 
-// Workspace bytes instance `id` needs for `batch` problems of (M, N): 0 when
-// it splits no K; INT64_MAX when its counters do not fit the counter area.
-int64_t workspace_need(int id, int64_t M, int64_t N, int64_t batch)
+// Workspace bytes instance `id` needs for `batch` problems of (M, N, K) on a
+// device with `cus` compute units: 0 when it cuts no K; INT64_MAX when its
+// counters do not fit the counter area.  A stream-K instance's need depends on
+// the device (its grid): with `cus` <= 0 (not known yet) this returns the
+// counter area alone, a lower bound, and the caller checks again once it is.
+int64_t workspace_need(int id, int64_t M, int64_t N, int64_t K, int64_t batch, int cus)
 {
-    if (a8w8::variant(id).splits <= 1)
+    if (a8w8::variant(id).kernel == A8W8_KERNEL_SKTILE && cus <= 0)
+        return kCounterBytes;
+    const int64_t counters = a8w8::variant_counters(id, M, N, K, cus);
+    if (counters == 0)
         return 0;
-    if (batch * a8w8::variant_counters(id, M, N) * 4 > kCounterBytes)
+    if (batch * counters * 4 > kCounterBytes)
         return INT64_MAX;
-    return kCounterBytes + batch * a8w8::variant_workspace_bytes(id, M, N);
+    return kCounterBytes + batch * a8w8::variant_workspace_bytes(id, M, N, K, cus);
 }
 
 // Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
@@ -290,7 +300,7 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t 
         }
         if (lo < s.count) {
             const int v = find_variant(s.kernel[lo], s.bm[lo], s.bn[lo], s.waves[lo], s.kblocks[lo], s.splits[lo]);
-            if (v >= 0 && variant_accepts(v, M, N, K, cus) && workspace_need(v, M, N, batch) <= ws_bytes)
+            if (v >= 0 && variant_accepts(v, M, N, K, cus) && workspace_need(v, M, N, K, batch, cus) <= ws_bytes)
                 return {v, s.key_m[lo], 0};
             const int u = find_variant(s.u_kernel[lo], s.u_bm[lo], s.u_bn[lo], s.u_waves[lo], s.u_kblocks[lo], 1);
             if (u >= 0 && variant_accepts(u, M, N, K, cus))
@@ -300,7 +310,7 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t 
     }
     int split = -1, unsplit = -1;
     heuristic_variants(M, N, K, cus, &split, &unsplit);
-    return {workspace_need(split, M, N, batch) <= ws_bytes ? split : unsplit, M, 1};
+    return {workspace_need(split, M, N, K, batch, cus) <= ws_bytes ? split : unsplit, M, 1};
 }
 
 void fill_plan(int id, int64_t M, int64_t N, int64_t K, int64_t batch, int cus, int64_t key_m, int fallback,
@@ -319,7 +329,7 @@ void fill_plan(int id, int64_t M, int64_t N, int64_t K, int64_t batch, int cus, 
     out->key_m = key_m;
     out->fallback = fallback;
     out->splits = v.splits;
-    out->workspace = M > 0 ? workspace_need(id, M, N, batch > 0 ? batch : 1) : 0;
+    out->workspace = M > 0 ? workspace_need(id, M, N, K, batch > 0 ? batch : 1, cus) : 0;
 }
 
 // GEMM_A8W8_LOG=1: one stderr line per distinct (M, N, K) with the plan used.
@@ -379,7 +389,7 @@ int launch(int id, const Operands &o, int64_t M, int64_t N, int64_t K, int cus, 
     a.splits = a8w8::variant(id).splits;
     a.ws = nullptr;
     a.cnt = nullptr;
-    if (a.splits > 1) {
+    if (o.ws != nullptr) {
         uint8_t *base = static_cast<uint8_t *>(o.ws);
         a.cnt = reinterpret_cast<int32_t *>(base);
         a.ws = reinterpret_cast<float *>(base + kCounterBytes);
@@ -444,7 +454,7 @@ int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
         return A8W8_OK;
     if (variant >= 0 && !variant_accepts(variant, M, N, K, 0))
         return A8W8_ERR_PLAN;
-    if (variant >= 0 && workspace_need(variant, M, N, o.batch) > o.ws_bytes)
+    if (variant >= 0 && workspace_need(variant, M, N, K, o.batch, 0) > o.ws_bytes)
         return A8W8_ERR_WORKSPACE;
     rc = check_pointers(o.A, o.a_scale, o.W, o.w_scale, o.Y);
     if (rc != A8W8_OK)
@@ -463,7 +473,7 @@ int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
         log_plan(M, N, K, c.variant, c.key_m, c.fallback);
         id = c.variant;
     }
-    if (workspace_need(id, M, N, o.batch) > o.ws_bytes)
+    if (workspace_need(id, M, N, K, o.batch, cus) > o.ws_bytes)
         return A8W8_ERR_WORKSPACE;
     return launch(id, o, M, N, K, cus, stream);
 }
@@ -482,7 +492,7 @@ int plan_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
     if (variant >= 0) {
         if (!variant_accepts(variant, Mp, N, K, cus))
             return A8W8_ERR_PLAN;
-        if (workspace_need(variant, Mp, N, batch) > o.ws_bytes)
+        if (workspace_need(variant, Mp, N, K, batch, cus) > o.ws_bytes)
             return A8W8_ERR_WORKSPACE;
         fill_plan(variant, M, N, K, batch, cus, M, 0, out);
         return A8W8_OK;
@@ -625,10 +635,10 @@ int gemm_a8w8_blockscale_noalloc(const void *A, const float *a_scale, const void
     rc = device_ready(&cus, &dev);
     if (rc != A8W8_OK)
         return rc;
-    // The table's fastest plan, split or not; a plan needing more scratch than
-    // the array holds is refused, never run with less.
-    const Choice c = select_variant(M, N, K, cus, 0, 1, INT64_MAX);
-    if (workspace_need(c.variant, M, N, 1) > (int64_t)A8W8_NOALLOC_SCRATCH_BYTES)
+    // The table's fastest plan when its workspace fits the array, else the
+    // fastest one that cuts no K (the selector's rule for a call's workspace).
+    const Choice c = select_variant(M, N, K, cus, 0, 1, (int64_t)A8W8_NOALLOC_SCRATCH_BYTES);
+    if (workspace_need(c.variant, M, N, K, 1, cus) > (int64_t)A8W8_NOALLOC_SCRATCH_BYTES)
         return A8W8_ERR_WORKSPACE;
     // Set-up, once per device with that device current: the device address of
     // this GPU's copy of the array.

@@ -14,7 +14,8 @@ struct Variant {
     int32_t kblocks;   // K blocks each wave loads (skinny, pskinny), LDS ring depth (tile)
     int32_t max_m;     // largest M the instance accepts (skinny, pskinny: 16), 0 = any
     int32_t per_cu;    // ptile, pskinny, rskinny: workgroups per CU the grid is sized for
-    int32_t splits;    // tile: workgroups per output tile, each taking 1/splits of K (1: no split)
+    int32_t splits;    // tile: workgroups per output tile, each taking 1/splits of K (1: no split;
+                       // stream-K instances cut tiles by their own rule and keep 1 here)
     const char *name;
 };
 
@@ -34,7 +35,8 @@ struct Args {
     int64_t bs_a, bs_as, bs_w, bs_ws, bs_y;
     // Split K (split instances): splits per tile; the call's workspace for the
     // fp32 partial tiles [batch][tile][split][BM * BN] and one zeroed counter per
-    // [batch][tile] (the last split of a tile resets it).
+    // [batch][tile] (the last split of a tile resets it).  Stream-K instances:
+    // partials [batch][2 * grid][BM * BN], counters [batch][stream-K tile].
     int32_t splits;
     float *ws;
     int32_t *cnt;
@@ -42,9 +44,10 @@ struct Args {
 
 int num_variants();
 const Variant &variant(int id);
-// Workspace a split-K instance needs per batch: fp32 partial bytes and counters.
-int64_t variant_workspace_bytes(int id, int64_t M, int64_t N);
-int64_t variant_counters(int id, int64_t M, int64_t N);
+// Workspace a split-K or stream-K instance needs per batch on a device with
+// `cus` compute units: fp32 partial bytes and counters (0 and 0: none).
+int64_t variant_workspace_bytes(int id, int64_t M, int64_t N, int64_t K, int cus);
+int64_t variant_counters(int id, int64_t M, int64_t N, int64_t K, int cus);
 // Workgroups the instance launches for (M, N, K) on a device with `cus`
 // compute units (ptile, pskinny: min(tiles, cus * per_cu), each workgroup
 // looping over its share of the tiles), and the passes over K one wave makes

@@ -1141,7 +1141,7 @@ __device__ __forceinline__ void linear_tile(int L, int tiles_m, int tiles_n, int
     tn = in_group / gsize;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool PK, int SM>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool SKM, bool PK, int SM>
 __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_store)
 {
     select_batch(p);
@@ -1188,6 +1188,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     static_assert(LATE || STAGES > 2 || C_BEFORE == PER_BLOCK, "two stages: next block's copies precede the barrier");
     static_assert(VM_AT_BARRIER >= 0 && VM_AT_BARRIER < 64 && (AHEAD - 1) * PER_BLOCK < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    __shared__ int sk_last;                       // stream-K fixup: this workgroup arrived last
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1198,9 +1199,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     // the workgroups of one XCD on consecutive tile ids.
     const int grid = (int)gridDim.x, b = (int)blockIdx.x;
     const int rank = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
-    if (rank >= T)
+    // Stream-K instances (SKM): when T is not a multiple of the grid, the
+    // tiles of the last one or two waves (sk_tiles of them, the last ids of
+    // the tile order) are not dealt out whole.  Their T_sk x KB blocks form one
+    // stream cut into `grid` nearly equal runs, run r = steps [B(r), B(r+1))
+    // with B(r) = r * S / grid, so every workgroup does the same number of
+    // blocks; a tile cut between runs is finished by the fixed-order fixup
+    // after the K loop.  The other tiles go round-robin as below.
+    int dp_tiles = T, sk_tiles = 0;
+    if constexpr (SKM) {
+        const int full = T / grid, rem = T - full * grid;
+        if (rem != 0) {
+            dp_tiles = full >= 1 ? (full - 1) * grid : 0;
+            sk_tiles = T - dp_tiles;
+        }
+    }
+    // stream-K steps (the host keeps S_sk >= grid; sk_tiles < 2 grid, so S_sk fits 31 bits)
+    const int64_t S_sk = (int64_t)sk_tiles * KB;
+    const int64_t sk_lo = (int64_t)rank * S_sk / grid, sk_hi = (int64_t)(rank + 1) * S_sk / grid;
+    if (rank >= T && S_sk == 0)
         return;
-    const int ntiles = (T - 1 - rank) / grid + 1;
+    const int ntiles = rank < dp_tiles ? (dp_tiles - 1 - rank) / grid + 1 : 0;   // whole tiles of this workgroup
     int G = 1;
     while (4 * G * G <= (grid >> 3) && G < tiles_m)   // about sqrt(grid / 8) tile rows per group
         G *= 2;
@@ -1247,9 +1266,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         int m0, n0;
         const float *s_src;
     };
-    auto copy_tile = [&](int i) {
+    // Tile of linear id L (see linear_tile).
+    auto copy_at = [&](int L) __attribute__((always_inline)) {
         int tm, tn;
-        linear_tile(rank + i * grid, tiles_m, tiles_n, G, tm, tn);
+        linear_tile(L, tiles_m, tiles_n, G, tm, tn);
         CopyTile c;
         c.m0 = tm * BM;
         c.n0 = tn * BN;
@@ -1260,15 +1280,32 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
                               : p.w_scale + (size_t)min((c.n0 >> SH) + min(slot - BM, NBW - 1), NB - 1) * KB;
         return c;
     };
+    // The i-th whole tile of this workgroup.
+    auto copy_tile = [&](int i) __attribute__((always_inline)) { return copy_at(rank + i * grid); };
+    // Position v of this workgroup's block stream: its whole tiles, then (SKM)
+    // its stream-K run.  Returns the tile's linear id in L and the block in kb.
+    const int dp_steps = ntiles * KB;
+    auto step_pos = [&](int v, int &L, int &kb) __attribute__((always_inline)) {
+        if (v < dp_steps) {
+            const int i = v / KB;
+            L = rank + i * grid;
+            kb = v - i * KB;
+        } else {
+            const int s = (int)sk_lo + (v - dp_steps);        // < S_sk, which fits 31 bits
+            const int t = s / KB;
+            L = dp_tiles + t;
+            kb = s - t * KB;
+        }
+    };
     // Descriptors of K block kb of a tile: the rows that exist, minus the
     // bytes before the block in the first row.
-    auto rsrc_a = [&](int m0, int kb) {
+    auto rsrc_a = [&](int m0, int kb) __attribute__((always_inline)) {
         return tile_rsrc(p.A + (size_t)m0 * K + (size_t)kb * 128,
                          (uint32_t)min(M - m0, BM) * (uint32_t)K - (uint32_t)kb * 128u);
     };
     // Packed weights: the tile's 16-row tiles from block kb of its first one
     // to the end of its last one that exists.
-    auto rsrc_w = [&](int n0, int kb) {
+    auto rsrc_w = [&](int n0, int kb) __attribute__((always_inline)) {
         if (PK) {
             const int t0 = n0 >> 4, tiles = min(((N + 15) >> 4) - t0, BN / 16);
             return tile_rsrc(p.W + (((size_t)t0 * KB + kb) << 11),
@@ -1289,12 +1326,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     // fragments of block 0.  (Stream position q is block q % KB of this
     // workgroup's tile q / KB; past the end it repeats the last block, into
     // stages nobody reads again.)
-    const int steps = ntiles * KB;
+    const int steps = dp_steps + (int)(sk_hi - sk_lo);
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s) {
         const int q = min(s, steps - 1);
-        const CopyTile c = copy_tile(q / KB);
-        const int ckb = q % KB;
+        int cL, ckb;
+        step_pos(q, cL, ckb);
+        const CopyTile c = copy_at(cL);
         issue_tile_loads<A_LOADS, W_LOADS, A_BYTES, W_BYTES, SC>(rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), a_off, w_off,
                                                             c.s_src, ckb, lds0 + (uint32_t)(s * STAGE), wave);
     }
@@ -1330,7 +1368,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
 
     // One K block at stream position `step`; its copies fetch block ckb of the
     // copy tile described by ra, rw and s_src.
-    auto block = [&](int step, v4i ra, v4i rw, const float *s_src, int ckb) {
+    auto block = [&](int step, v4i ra, v4i rw, const float *s_src, int ckb) __attribute__((always_inline)) {
         const uint8_t *sA = smem + (step % STAGES) * STAGE;
         const uint32_t cstage = lds0 + (uint32_t)(((step + AHEAD) % STAGES) * STAGE);
 
@@ -1430,27 +1468,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         s_last = s_cur;
     };
 
-    // Per tile: the blocks whose copies stay inside the tile, then the last
-    // AHEAD blocks, whose copies already fetch the next tile, then the stores.
-    const int main_blocks = KB - AHEAD > 0 ? KB - AHEAD : 0;
-    int step = 0;
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const CopyTile cur = copy_tile(tile);
-        for (int kb = 0; kb < main_blocks; ++kb, ++step)
-            block(step, rsrc_a(cur.m0, kb + AHEAD), rsrc_w(cur.n0, kb + AHEAD), cur.s_src, kb + AHEAD);
-        for (int kb = main_blocks; kb < KB; ++kb, ++step) {
-            const int q = min(step + AHEAD, steps - 1);
-            const CopyTile c = copy_tile(q / KB);
-            const int ckb = q % KB;
-            block(step, rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), c.s_src, ckb);
-        }
-
-        // Tile done: fold in the last slice (block scale), round to bf16 and store.
+    // A tile's blocks are done: fold in the last slice (block scale).
+    auto fold_last = [&]() __attribute__((always_inline)) {
         if constexpr (SM == SM_BLOCK) {
 #pragma unroll
             for (int u = 0; u < TN; ++u)
                 acc[TM - 1][u] = fma4(d_last[u], s_last, acc[TM - 1][u]);
         }
+    };
+    // Round the tile to bf16 and store it.
+    auto store_tile = [&](const CopyTile &cur) __attribute__((always_inline)) {
         const int n_base = cur.n0 + wn * WN + 4 * g;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
@@ -1462,6 +1489,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
                            rowwise_scale<SM>(acc[t][u], p, m, n_base + 16 * u));
             }
         }
+    };
+    auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < TM; ++t)
 #pragma unroll
@@ -1471,18 +1500,152 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         for (int u = 0; u < TN; ++u)
             d_last[u] = (v4f){0.f, 0.f, 0.f, 0.f};
         s_last = 0.f;
+    };
+
+    if constexpr (!SKM) {
+        // Per tile: the blocks whose copies stay inside the tile, then the last
+        // AHEAD blocks, whose copies already fetch the next tile, then the stores.
+        const int main_blocks = KB - AHEAD > 0 ? KB - AHEAD : 0;
+        int step = 0;
+        for (int tile = 0; tile < ntiles; ++tile) {
+            const CopyTile cur = copy_tile(tile);
+            for (int kb = 0; kb < main_blocks; ++kb, ++step)
+                block(step, rsrc_a(cur.m0, kb + AHEAD), rsrc_w(cur.n0, kb + AHEAD), cur.s_src, kb + AHEAD);
+            for (int kb = main_blocks; kb < KB; ++kb, ++step) {
+                const int q = min(step + AHEAD, steps - 1);
+                const CopyTile c = copy_tile(q / KB);
+                const int ckb = q % KB;
+                block(step, rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), c.s_src, ckb);
+            }
+            fold_last();
+            store_tile(cur);
+            reset();
+        }
+    } else {
+        // Pieces of the block stream: each lies in one tile, a whole tile (the
+        // round-robin ones and some of the stream-K run) or a cut piece of a
+        // stream-K tile.  As in the loop above, the blocks whose copies stay
+        // inside the piece take kb + AHEAD, the last AHEAD look the copy target
+        // up in the stream.
+        //
+        // Fixup of stream-K tile tp, cut between runs r_lo..r_hi (the runs
+        // whose steps meet [tp KB, (tp + 1) KB)): every piece writes its fp32
+        // partial tile to the call's workspace with device-coherent stores and
+        // goes on with its run; at the end of the run the workgroup waits for
+        // its stores and counts each of its pieces in that tile's counter.
+        // The last piece of a tile to be counted sums the pieces in run order
+        // r_lo, r_lo + 1, ... (a fixed order whatever the arrival order, so the
+        // result is bitwise reproducible), stores the tile and resets the
+        // counter to zero for the next call.  Nothing waits on another
+        // workgroup.  A run holds at most two cut pieces: the one with its
+        // first step goes to partial slot 2r, the one with its last to 2r + 1
+        // (workspace: counters [batch][sk_tiles], then [batch][2 grid][BM * BN]
+        // fp32 partials; a slot is [wave][t][u][lane][4]).
+        constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 256;
+        const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(p.ws + (size_t)blockIdx.y * 2 * grid * TILE_F,
+                                                        (uint32_t)(2 * grid) * (uint32_t)TILE_F * 4u);
+        const int lane_off = (wave * WAVE_F + lane * 4) * 4;              // bytes, + ((t TN + u) 64 * 4) * 4
+        auto sk_range = [&](int tp, int &r_lo, int &r_hi) __attribute__((always_inline)) {
+            const int64_t x0 = (int64_t)tp * KB;
+            r_lo = (int)min((int64_t)grid - 1, ((x0 + 1) * grid - 1) / S_sk);
+            r_hi = (int)min((int64_t)grid - 1, ((x0 + KB) * grid - 1) / S_sk);
+        };
+        auto slot_of = [&](int r, int tp) __attribute__((always_inline)) {
+            return 2 * r + ((int64_t)r * S_sk / grid >= (int64_t)tp * KB ? 0 : 1);
+        };
+        auto write_partial = [&](int tp) __attribute__((always_inline)) {
+            const int soff = slot_of(rank, tp) * TILE_F * 4;
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[t][u]), pres,
+                                                           lane_off + (t * TN + u) * 1024, soff, 16 /* sc1 */);
+        };
+        // Count this workgroup's piece of tile tp; the last one sums and stores the tile.
+        auto finish_piece = [&](int tp) __attribute__((always_inline)) {
+            int r_lo, r_hi;
+            sk_range(tp, r_lo, r_hi);
+            int32_t *cnt = p.cnt + (size_t)blockIdx.y * sk_tiles + tp;
+            __syncthreads();                                     // sk_last of the previous piece is read out
+            if (threadIdx.x == 0)
+                sk_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == r_hi - r_lo;
+            __syncthreads();
+            if (!sk_last)
+                return;
+            // Every other piece was counted after its stores completed.
+            for (int r = r_lo; r <= r_hi; ++r) {
+                const int soff = slot_of(r, tp) * TILE_F * 4;
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+#pragma unroll
+                    for (int u = 0; u < TN; ++u) {
+                        const v4f x = __builtin_bit_cast(
+                            v4f, __builtin_amdgcn_raw_buffer_load_b128(pres, lane_off + (t * TN + u) * 1024, soff,
+                                                                       16 /* sc1 */));
+                        if (r == r_lo) {
+                            acc[t][u] = x;
+                        } else {
+                            acc[t][u][0] += x[0];
+                            acc[t][u][1] += x[1];
+                            acc[t][u][2] += x[2];
+                            acc[t][u][3] += x[3];
+                        }
+                    }
+            }
+            store_tile(copy_at(dp_tiles + tp));
+            if (threadIdx.x == 0)
+                __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            reset();
+        };
+        int pend0 = -1, pend1 = -1;                              // cut pieces written, counted at the end
+        int v = 0;
+        while (v < steps) {
+            int L, kb0;
+            step_pos(v, L, kb0);
+            const int len = min(KB - kb0, steps - v);
+            const CopyTile cur = copy_at(L);
+            const int inner = len - AHEAD > 0 ? len - AHEAD : 0;
+            for (int j = 0; j < inner; ++j, ++v)
+                block(v, rsrc_a(cur.m0, kb0 + j + AHEAD), rsrc_w(cur.n0, kb0 + j + AHEAD), cur.s_src, kb0 + j + AHEAD);
+            for (int j = inner; j < len; ++j, ++v) {
+                const int q = min(v + AHEAD, steps - 1);
+                int cL, ckb;
+                step_pos(q, cL, ckb);
+                const CopyTile c = copy_at(cL);
+                block(v, rsrc_a(c.m0, ckb), rsrc_w(c.n0, ckb), c.s_src, ckb);
+            }
+            fold_last();
+            if (kb0 == 0 && len == KB) {
+                store_tile(cur);
+            } else {
+                write_partial(L - dp_tiles);
+                if (pend0 < 0)
+                    pend0 = L - dp_tiles;
+                else
+                    pend1 = L - dp_tiles;
+            }
+            reset();
+        }
+        if (pend0 >= 0) {
+            wait_vmcnt<0>();                                     // this wave's partial stores are complete
+            finish_piece(pend0);                                 // (its first barrier: every wave's)
+            if (pend1 >= 0)
+                finish_piece(pend1);
+        }
     }
     wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
 }
 
 // Explicit instantiations (emit the host-side launch stubs).
-#define A8W8_PTILE_INST(BM, BN, WGM, WGN, S)                                                  \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, 0>(Args, int);          \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, 0>(Args, int);           \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, 1>(Args, int);          \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, 1>(Args, int);           \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, false, 2>(Args, int);          \
-    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, true, 2>(Args, int);
+#define A8W8_PTILE_INST1(BM, BN, WGM, WGN, S, SKM)                                             \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, SKM, false, 0>(Args, int);     \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, SKM, true, 0>(Args, int);      \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, SKM, false, 1>(Args, int);     \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, SKM, true, 1>(Args, int);      \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, SKM, false, 2>(Args, int);     \
+    template __global__ void ptile_kernel<BM, BN, WGM, WGN, S, SKM, true, 2>(Args, int);
+#define A8W8_PTILE_INST(BM, BN, WGM, WGN, S) A8W8_PTILE_INST1(BM, BN, WGM, WGN, S, false)
 A8W8_PTILE_INST(256, 256, 2, 4, 2)
 A8W8_PTILE_INST(256, 128, 2, 4, 3)
 A8W8_PTILE_INST(128, 256, 2, 4, 3)
@@ -1492,7 +1655,12 @@ A8W8_PTILE_INST(64, 64, 2, 2, 4)
 A8W8_PTILE_INST(32, 64, 2, 2, 6)
 A8W8_PTILE_INST(32, 32, 2, 2, 4)
 A8W8_PTILE_INST(32, 32, 2, 2, 8)
+A8W8_PTILE_INST1(256, 256, 2, 4, 2, true)
+A8W8_PTILE_INST1(256, 128, 2, 4, 3, true)
+A8W8_PTILE_INST1(128, 256, 2, 4, 3, true)
+A8W8_PTILE_INST1(128, 128, 2, 2, 2, true)
 #undef A8W8_PTILE_INST
+#undef A8W8_PTILE_INST1
 
 // ---------------------------------------------------------------------------
 // One-workgroup-per-tile kernel ("tile").  The same block scaling and LDS
@@ -1864,7 +2032,14 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
 #define PTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_PTILE, BM, BN, WGM * WGN, S, 0, \
                                     tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), 1, \
                                     "ptile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
-                                   FN6(ptile_kernel<BM, BN, WGM, WGN, S), \
+                                   FN6(ptile_kernel<BM, BN, WGM, WGN, S, false), \
+                                   S * ((BM + BN) * 128 + WGM * WGN * 256)}
+// The persistent tile kernel in stream-K mode (see ptile_kernel): the last one
+// or two waves of tiles are cut into equal runs of K blocks, one per workgroup.
+#define SKTILE(BM, BN, WGM, WGN, S, WPC) {{A8W8_KERNEL_SKTILE, BM, BN, WGM * WGN, S, 0, \
+                                    tile_per_cu(S * ((BM + BN) * 128 + WGM * WGN * 256), WGM * WGN, WPC), 1, \
+                                    "sktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_s" #S}, \
+                                   FN6(ptile_kernel<BM, BN, WGM, WGN, S, true), \
                                    S * ((BM + BN) * 128 + WGM * WGN * 256)}
 
 #define TALL(TPW, NT, D, NW) {{A8W8_KERNEL_TALL, 16 * TPW, 16 * NT, NW, D, 0, 0, 1, \
@@ -1900,6 +2075,8 @@ const Entry kEntries[] = {
     SKINNY_SK(2, 5, 4, 2), SKINNY_SK(4, 5, 4, 2), SKINNY_SK(1, 5, 2, 4), SKINNY_SK(2, 4, 8, 2),
     RSKINNY(2, 3, 16, 1), RSKINNY(2, 6, 8, 1), RSKINNY(4, 5, 8, 1), RSKINNY(3, 5, 8, 1), RSKINNY(1, 5, 8, 2),
     RSKINNY(1, 3, 16, 2), RSKINNY(2, 5, 8, 1), RSKINNY(4, 3, 8, 1),
+    SKTILE(256, 256, 2, 4, 2, 8), SKTILE(256, 128, 2, 4, 3, 8), SKTILE(128, 256, 2, 4, 3, 8),
+    SKTILE(128, 128, 2, 2, 2, 8),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -1949,7 +2126,21 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
     if (v.kernel == A8W8_KERNEL_TILE)
         return tiles * v.splits;
     const int64_t slots = (int64_t)(cus > 0 ? cus : 1) * v.per_cu;
+    if (v.kernel == A8W8_KERNEL_SKTILE) {
+        // every slot, unless the whole problem has fewer K blocks than slots
+        const int64_t steps = tiles * (K / 128);
+        return steps < slots ? steps : slots;
+    }
     return tiles < slots ? tiles : slots;
+}
+
+// Stream-K tiles of a stream-K instance on `grid` workgroups (the kernel's own rule).
+static int64_t sk_tiles_of(int64_t tiles, int64_t grid)
+{
+    const int64_t full = tiles / grid, rem = tiles % grid;
+    if (rem == 0)
+        return 0;
+    return full >= 1 ? grid + rem : tiles;
 }
 
 int64_t variant_passes(int id, int64_t K)
@@ -1963,21 +2154,29 @@ int64_t variant_passes(int id, int64_t K)
     return (per_split + per_pass - 1) / per_pass;
 }
 
-int64_t variant_workspace_bytes(int id, int64_t M, int64_t N)
+int64_t variant_workspace_bytes(int id, int64_t M, int64_t N, int64_t K, int cus)
 {
     const Variant &v = kEntries[id].v;
+    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    if (v.kernel == A8W8_KERNEL_SKTILE) {
+        // two partial slots per workgroup, when any tile is cut
+        const int64_t grid = variant_grid(id, M, N, K, cus);
+        return sk_tiles_of(tiles, grid) > 0 ? 2 * grid * v.bm * v.bn * 4 : 0;
+    }
     if (v.splits <= 1)
         return 0;
-    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
     return tiles * v.splits * v.bm * v.bn * 4;
 }
 
-int64_t variant_counters(int id, int64_t M, int64_t N)
+int64_t variant_counters(int id, int64_t M, int64_t N, int64_t K, int cus)
 {
     const Variant &v = kEntries[id].v;
+    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    if (v.kernel == A8W8_KERNEL_SKTILE)
+        return sk_tiles_of(tiles, variant_grid(id, M, N, K, cus));
     if (v.splits <= 1)
         return 0;
-    return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    return tiles;
 }
 
 hipError_t set_kernel_attributes()

@@ -65,6 +65,11 @@ REPLACE_MARGIN = 0.02
 ROW_FIELDS = ("kernel", "bm", "bn", "waves", "kblocks", "splits", "name")
 
 
+def cuts_k(v: dict) -> bool:
+    """Whether the instance cuts K across workgroups (split K or stream-K): it needs a workspace."""
+    return v["splits"] > 1 or v["kernel_name"] == "sktile"
+
+
 def _instance(v: dict) -> dict:
     return {"kernel": v["kernel_name"], "bm": v["bm"], "bn": v["bn"], "waves": v["waves"],
             "kblocks": v["kblocks"], "splits": v["splits"], "name": v["name"]}
@@ -74,13 +79,13 @@ def pick_row(M: int, medians: dict, by_name: dict) -> dict:
     """Table row for key M from per-instance median times (us) keyed by instance name."""
     names = sorted(medians, key=lambda n: (medians[n], n))
     best = names[0]
-    unsplit = [n for n in names if by_name[n]["splits"] == 1]
-    if by_name[best]["splits"] > 1 and unsplit and medians[unsplit[0]] <= (1 + SPLIT_PREFERENCE) * medians[best]:
+    unsplit = [n for n in names if not cuts_k(by_name[n])]
+    if cuts_k(by_name[best]) and unsplit and medians[unsplit[0]] <= (1 + SPLIT_PREFERENCE) * medians[best]:
         best = unsplit[0]
     row = {"key_m": M, **_instance(by_name[best]), "us": round(medians[best], 3)}
     others = [medians[n] for n in names if n != best]
     row["margin"] = round(min(others) / medians[best] - 1, 4) if others else None
-    if by_name[best]["splits"] > 1:
+    if cuts_k(by_name[best]):
         row["unsplit"] = {**_instance(by_name[unsplit[0]]), "us": round(medians[unsplit[0]], 3)}
     row["candidates"] = {n: round(medians[n], 3) for n in names}
     return row
@@ -262,8 +267,8 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
                 keep = {"key_m": M, **_instance(by_name[pn]), "us": round(med[pn], 3)}
                 others = [t for n, t in med.items() if n != pn]
                 keep["margin"] = round(min(others) / med[pn] - 1, 4) if others else None
-                if by_name[pn]["splits"] > 1:
-                    u = min((n for n in med if by_name[n]["splits"] == 1), key=lambda n: (med[n], n))
+                if cuts_k(by_name[pn]):
+                    u = min((n for n in med if not cuts_k(by_name[n])), key=lambda n: (med[n], n))
                     keep["unsplit"] = {**_instance(by_name[u]), "us": round(med[u], 3)}
                 keep["candidates"] = row["candidates"]
                 row = keep
@@ -299,7 +304,7 @@ def parse_instance(name: str) -> dict:
         d, nw, _ = m.groups()
         return {"name": name, "kernel_name": "pskinny", "bm": 16, "bn": 16, "waves": int(nw), "kblocks": int(d),
                 "splits": 1}
-    m = re.fullmatch(r"(p?tile)_(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)(?:_k(\d+))?", name)
+    m = re.fullmatch(r"(p?tile|sktile)_(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)(?:_k(\d+))?", name)
     if m:
         kern, bm, bn, wm, wn, st, sk = m.groups()
         return {"name": name, "kernel_name": kern, "bm": int(bm), "bn": int(bn), "waves": int(wm) * int(wn),

@@ -82,7 +82,8 @@ enum {
     A8W8_KERNEL_PTILE = 3,   /* fp8-MFMA output tiles, persistent workgroups, LDS ring        */
     A8W8_KERNEL_PSKINNY = 4, /* M <= 16, tall W: about one workgroup per CU walks 16-row tiles */
     A8W8_KERNEL_TALL = 5,    /* N <= 32: streams A once, K split over the waves of a workgroup */
-    A8W8_KERNEL_RSKINNY = 6  /* M <= 16: about one workgroup per CU, each an equal run of W rows  */
+    A8W8_KERNEL_RSKINNY = 6, /* M <= 16: about one workgroup per CU, each an equal run of W rows  */
+    A8W8_KERNEL_SKTILE = 7   /* persistent tiles, last waves cut into equal K runs (stream-K)     */
 };
 
 /*

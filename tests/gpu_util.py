@@ -30,7 +30,7 @@ def shared_workspace():
     """One split-K workspace for the forced-instance calls of a test session (calls run in
     stream order on the current stream)."""
     if not _WS:
-        _WS.append(g.Workspace(128 << 20))
+        _WS.append(g.Workspace((128 << 20) + (1 << 20)))
     return _WS[0]
 
 

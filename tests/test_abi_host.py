@@ -123,7 +123,7 @@ def test_run_variant_rejects_persistent_skinny_beyond_its_k():
 
 def test_variant_shapes_are_launchable():
     for v in g.variants():
-        if v["kernel_name"] in ("tile", "ptile"):
+        if v["kernel_name"] in ("tile", "ptile", "sktile"):
             assert v["bm"] % 32 == 0 and v["bn"] % 32 == 0 and v["bn"] // 2 <= 128
             assert 128 % (v["bn"] // 2) == 0, v          # a wave's columns stay in one weight block
             assert 2 * (v["bm"] + v["bn"]) * 128 <= 160 * 1024

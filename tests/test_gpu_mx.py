@@ -62,7 +62,7 @@ def _shape_for(v, cus):
     per_cu = g.gemm_a8w8_describe_variant(v["variant"], 1 << 24, 1 << 16, 640)["grid"] // 256
     N = 3 * v["bn"] + 40
     tiles_n = (N + v["bn"] - 1) // v["bn"]
-    tiles_m = (2 * cus * max(per_cu, 1) + tiles_n - 1) // tiles_n + 1 if k == "ptile" else 3
+    tiles_m = (2 * cus * max(per_cu, 1) + tiles_n - 1) // tiles_n + 1 if k in ("ptile", "sktile") else 3
     return tiles_m * v["bm"] - v["bm"] // 2 - 3, N
 
 
@@ -140,7 +140,7 @@ def test_batched_ragged_every_kernel_family():
             continue
         seen.add(v["kernel_name"])
         M, N = _shape_for(v, cus)
-        if v["kernel_name"] == "ptile":
+        if v["kernel_name"] in ("ptile", "sktile"):
             M = min(M, 3 * v["bm"] + 7)
         K = 384
         A, a, W, w = _batched_operands(3, M, N, K, seed=vid)
@@ -151,7 +151,7 @@ def test_batched_ragged_every_kernel_family():
         rows = _rows(M)
         for i in range(3):
             assert_parity(yh[i][rows], oracle.gemm_mx(A[i], a[i], W[i], w[i], rows=rows), f"{v['name']} batch {i}")
-    assert seen == {"skinny", "pskinny", "tall", "tile", "ptile", "rskinny"}
+    assert seen == {"skinny", "pskinny", "tall", "tile", "ptile", "rskinny", "sktile"}
 
 
 def test_integer_case_bitwise():

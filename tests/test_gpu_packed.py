@@ -55,7 +55,7 @@ def _shape_for(v, cus):
     per_cu = g.gemm_a8w8_describe_variant(v["variant"], 1 << 24, 1 << 16, 640)["grid"] // 256
     N = 3 * v["bn"] + 40
     tiles_n = (N + v["bn"] - 1) // v["bn"]
-    tiles_m = (2 * cus * max(per_cu, 1) + tiles_n - 1) // tiles_n + 1 if k == "ptile" else 3
+    tiles_m = (2 * cus * max(per_cu, 1) + tiles_n - 1) // tiles_n + 1 if k in ("ptile", "sktile") else 3
     return tiles_m * v["bm"] - v["bm"] // 2 - 3, N
 
 

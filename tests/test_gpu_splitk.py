@@ -162,7 +162,8 @@ def test_split_batched_mx(kernel):
 
 
 def _tuned_split_rows():
-    """(shape entry, row) for every row of the tuned tables whose instance splits K."""
+    """(shape entry, row) for every row of the tuned tables whose instance cuts K across
+    workgroups (split K or stream-K)."""
     import json
     import os
     path = os.path.join(os.path.dirname(g.__file__), "tuned_table.json")
@@ -170,7 +171,7 @@ def _tuned_split_rows():
         table = json.load(f)
     out = []
     for sh in table["shapes"]:
-        rows = [r for r in sh["rows"] if int(r.get("splits", 1)) > 1]
+        rows = [r for r in sh["rows"] if int(r.get("splits", 1)) > 1 or r["kernel"] == "sktile"]
         if rows:
             out.append((sh, rows))
     return out
@@ -220,7 +221,7 @@ def test_every_tuned_split_plan_graph_equals_eager(entry):
         A, a = inputgen.make_activations(Mmax, K, seed=40)
         W, w = inputgen.make_weights(N, K, seed=50)
     dA, da, dW, dw = _dev(A, a, W, w)
-    ws = _ws(max(64 << 20, b * (40 << 20)))
+    ws = _ws(max((128 << 20) + (1 << 20), b * (40 << 20)))
     say(f"tuned split rows {kind} N={N} K={K} batch={b}: {len(rows)} keys, M up to {Mmax}")
     for r in rows:
         M = int(r["key_m"])
@@ -228,7 +229,7 @@ def test_every_tuned_split_plan_graph_equals_eager(entry):
         am = (da[:, :M] if b > 1 else da[:M]).contiguous()
         plan = g.gemm_a8w8_ex_plan(M, N, K, scale_kind=kind, batch=b, workspace_bytes=ws.nbytes)
         assert plan["name"] == r["name"] and plan["splits"] == int(r["splits"]), (M, plan["name"], r["name"])
-        assert 0 < plan["workspace"] <= ws.nbytes
+        assert plan["workspace"] <= ws.nbytes
         out = torch.empty(lead + (M, N), dtype=torch.bfloat16, device=DEV)
         eager = _replay_matches_eager(
             lambda: g.gemm_a8w8_ex(Am, am, dW, dw, scale_kind=kind, workspace=ws, out=out), out,
