@@ -39,9 +39,10 @@
  * reduced in a fixed order, so results are bitwise reproducible.
  *
  * Split K across workgroups.  For shapes with few output tiles the fastest
- * plan can split K over several workgroups per tile, which meet in a split-K
- * workspace: device memory the CALLER owns and passes through gemm_a8w8_ex
- * (see a8w8_gemm_desc).  The plain entries (gemm_a8w8_blockscale and the
+ * plan can split K over several workgroups per tile (split-K), or cut the
+ * last waves of tiles into equal runs of K blocks, one per workgroup
+ * (stream-K); the pieces of a tile meet in a workspace: device memory the
+ * CALLER owns and passes through gemm_a8w8_ex (see a8w8_gemm_desc).  The plain entries (gemm_a8w8_blockscale and the
  * other fixed-signature ones) bring no workspace: they always run the fastest
  * plan that splits no K across workgroups (gemm_a8w8_blockscale_plan reports
  * it), which needs nothing beyond the operands.
@@ -101,9 +102,10 @@ typedef struct {
     int64_t grid;       /* workgroups launched for this shape (tile: persistent, at most  */
                         /* a few per CU, each looping over its share of the output tiles) */
     int64_t key_m;      /* selector table key this M maps to (M <= key_m <= 1.25 M), or M */
-    int32_t splits;     /* tile, skinny: workgroups per output tile, each taking 1/splits of K (1: none) */
+    int32_t splits;     /* tile, skinny: workgroups per output tile, each taking 1/splits of K (1: none; stream-K: 1) */
     int32_t reserved;
-    int64_t workspace;  /* bytes of split-K workspace this launch uses (0: none)     */
+    int64_t workspace;  /* bytes of split-K / stream-K workspace this launch uses (0: none);
+                           stream-K: depends on cu_count (two partial tiles per workgroup) */
 } a8w8_plan;
 
 /*
@@ -306,22 +308,23 @@ int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64
  *                leading batch dimension; 1 for plain 2-D operands)
  *   scale_kind   A8W8_SCALE_BLOCK, A8W8_SCALE_MX or A8W8_SCALE_ROWWISE
  *   variant      -1: the selector's plan; else a compiled instance (tuning, tests)
- *   workspace    NULL, or split-K workspace: caller-owned device memory,
+ *   workspace    NULL, or a split-K / stream-K workspace: caller-owned device memory,
  *                256-byte aligned, of workspace_bytes bytes, zero-filled once
  *                by gemm_a8w8_workspace_init before its first use.  Its first
  *                A8W8_WORKSPACE_COUNTER_BYTES hold the per-tile counters of a
- *                split call (the same area for every call), the rest the
- *                fp32 partial tiles.  Every call leaves the counters zero
+ *                split or stream-K call (the same area for every call), the
+ *                rest the fp32 partial tiles.  Every call leaves the counters zero
  *                again, so one workspace serves any number of calls, of any
  *                shapes, IN STREAM ORDER; calls (or graph replays) that may
  *                overlap in time need workspaces of their own.  The library
  *                keeps no pointer to it.
  *
- * Plan rule (variant = -1): the table row's fastest instance if its split-K
+ * Plan rule (variant = -1): the table row's fastest instance if its
  * workspace (gemm_a8w8_ex_plan with workspace_bytes large: plan.workspace)
- * fits in workspace_bytes, else the row's fastest instance that splits no K
- * across workgroups.  A forced split instance without enough workspace
- * returns A8W8_ERR_WORKSPACE before anything is enqueued.
+ * fits in workspace_bytes, else the row's fastest instance that cuts no K
+ * across workgroups.  A forced split or stream-K instance without enough
+ * workspace for this device returns A8W8_ERR_WORKSPACE before anything is
+ * enqueued.
  */
 #define A8W8_WORKSPACE_COUNTER_BYTES 65536
 
