@@ -1206,7 +1206,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     // with B(r) = r * S / grid, so every workgroup does the same number of
     // blocks; a tile cut between runs is finished by the fixed-order fixup
     // after the K loop.  The other tiles go round-robin as below.
+    //
+    // With at most half as many tiles as workgroups the host launches
+    // grid = S x T (S >= 2) and every tile is cut at the same S - 1 points
+    // ("aligned"): workgroup rank takes piece j = rank / T of tile rank % T,
+    // blocks [j KB / S, (j + 1) KB / S).  The workgroups that run together then
+    // work at the same K position, so the tiles that share A rows or W rows
+    // read the same slice of them at the same time, as whole tiles do.
     int dp_tiles = T, sk_tiles = 0;
+    const bool aligned = SKM && 2 * T <= grid;
+    const int S_al = aligned ? grid / T : 1;
     if constexpr (SKM) {
         const int full = T / grid, rem = T - full * grid;
         if (rem != 0) {
@@ -1216,10 +1225,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
     }
     // stream-K steps (the host keeps S_sk >= grid; sk_tiles < 2 grid, so S_sk fits 31 bits)
     const int64_t S_sk = (int64_t)sk_tiles * KB;
-    const int64_t sk_lo = (int64_t)rank * S_sk / grid, sk_hi = (int64_t)(rank + 1) * S_sk / grid;
+    int64_t sk_lo = (int64_t)rank * S_sk / grid, sk_hi = (int64_t)(rank + 1) * S_sk / grid;
+    const int al_tile = rank % T, al_piece = rank / T;
+    if (aligned) {
+        sk_lo = (int64_t)al_tile * KB + (int64_t)al_piece * KB / S_al;
+        sk_hi = (int64_t)al_tile * KB + (int64_t)(al_piece + 1) * KB / S_al;
+    }
     if (rank >= T && S_sk == 0)
         return;
-    const int ntiles = rank < dp_tiles ? (dp_tiles - 1 - rank) / grid + 1 : 0;   // whole tiles of this workgroup
+    const int ntiles = rank < dp_tiles && !aligned ? (dp_tiles - 1 - rank) / grid + 1 : 0;   // whole tiles
     int G = 1;
     while (4 * G * G <= (grid >> 3) && G < tiles_m)   // about sqrt(grid / 8) tile rows per group
         G *= 2;
@@ -1545,12 +1559,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
         const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(p.ws + (size_t)blockIdx.y * 2 * grid * TILE_F,
                                                         (uint32_t)(2 * grid) * (uint32_t)TILE_F * 4u);
         const int lane_off = (wave * WAVE_F + lane * 4) * 4;              // bytes, + ((t TN + u) 64 * 4) * 4
+        // Pieces of tile tp: the runs r_lo..r_hi (aligned: ranks tp, tp + T, ...,
+        // one piece each), in the order they are summed.
         auto sk_range = [&](int tp, int &r_lo, int &r_hi) __attribute__((always_inline)) {
+            if (aligned) {
+                r_lo = 0;
+                r_hi = S_al - 1;
+                return;
+            }
             const int64_t x0 = (int64_t)tp * KB;
             r_lo = (int)min((int64_t)grid - 1, ((x0 + 1) * grid - 1) / S_sk);
             r_hi = (int)min((int64_t)grid - 1, ((x0 + KB) * grid - 1) / S_sk);
         };
+        auto piece_rank = [&](int tp, int j) __attribute__((always_inline)) { return aligned ? tp + j * T : j; };
         auto slot_of = [&](int r, int tp) __attribute__((always_inline)) {
+            if (aligned)
+                return 2 * r;
             return 2 * r + ((int64_t)r * S_sk / grid >= (int64_t)tp * KB ? 0 : 1);
         };
         auto write_partial = [&](int tp) __attribute__((always_inline)) {
@@ -1574,7 +1598,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
             if (!sk_last)
                 return;
             // Every other piece was counted after its stores completed.
-            for (int r = r_lo; r <= r_hi; ++r) {
+            for (int j = r_lo; j <= r_hi; ++j) {
+                const int r = piece_rank(tp, j);
                 const int soff = slot_of(r, tp) * TILE_F * 4;
 #pragma unroll
                 for (int t = 0; t < TM; ++t)
@@ -1583,7 +1608,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void ptile_kernel(Args p, int vec_s
                         const v4f x = __builtin_bit_cast(
                             v4f, __builtin_amdgcn_raw_buffer_load_b128(pres, lane_off + (t * TN + u) * 1024, soff,
                                                                        16 /* sc1 */));
-                        if (r == r_lo) {
+                        if (j == r_lo) {
                             acc[t][u] = x;
                         } else {
                             acc[t][u][0] += x[0];
@@ -1903,22 +1928,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
     wait_vmcnt<0>();                      // no copy into LDS may outlive the workgroup
 
     if (S > 1) {
-        // Partial tile of split s: [tile][s][wave][t][u][component][lane] fp32 in this
-        // batch's workspace, so each dword store covers 256 contiguous bytes.  The
-        // partials are written and read with device-scope (agent) accesses, which
-        // are coherent across the XCDs' L2s by themselves: no cache-wide writeback
-        // or invalidate, which would cost every other tile its cached operands.
+        // Partial tile of split s: [tile][s][wave][t][u][lane][4] fp32 in this batch's
+        // workspace, written and read with 16-byte device-coherent (sc1) accesses,
+        // which are coherent across the XCDs' L2s by themselves: no cache-wide
+        // writeback or invalidate, which would cost every other tile its cached
+        // operands.  Each instruction moves 1 KB contiguous per wave.
         constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 256;
         const size_t tile_g = (size_t)blockIdx.y * tiles_m * tiles_n + tile_lin;
-        float *part = p.ws + tile_g * S * TILE_F + wave * WAVE_F + lane;
+        const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(p.ws + tile_g * S * TILE_F, (uint32_t)S * TILE_F * 4u);
+        const int lane_off = (wave * WAVE_F + lane * 4) * 4;              // bytes, + (t TN + u) * 1024
 #pragma unroll
         for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    __hip_atomic_store(part + (size_t)split * TILE_F + ((t * TN + u) * 4 + c) * 64, acc[t][u][c],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[t][u]), pres,
+                                                       lane_off + (t * TN + u) * 1024, split * TILE_F * 4,
+                                                       16 /* sc1 */);
         __shared__ int last;
         wait_vmcnt<0>();                                     // this wave's partial stores are complete
         __syncthreads();                                     // ... and every wave's
@@ -1927,24 +1952,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void tile_kernel(Args p, int vec_st
         __syncthreads();
         if (!last)
             return;
-        // The last split: every other split counted itself after its stores completed.
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int u = 0; u < TN; ++u)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[t][u][c] = __hip_atomic_load(part + ((t * TN + u) * 4 + c) * 64, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        for (int s2 = 1; s2 < S; ++s2) {
+        // The last split: every other split counted itself after its stores
+        // completed.  Sum in split order 0, 1, ... (its own partial included).
+        for (int s2 = 0; s2 < S; ++s2) {
 #pragma unroll
             for (int t = 0; t < TM; ++t)
 #pragma unroll
-                for (int u = 0; u < TN; ++u)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        acc[t][u][c] += __hip_atomic_load(part + (size_t)s2 * TILE_F + ((t * TN + u) * 4 + c) * 64,
-                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int u = 0; u < TN; ++u) {
+                    const v4f x = __builtin_bit_cast(
+                        v4f, __builtin_amdgcn_raw_buffer_load_b128(pres, lane_off + (t * TN + u) * 1024,
+                                                                   s2 * TILE_F * 4, 16 /* sc1 */));
+                    if (s2 == 0) {
+                        acc[t][u] = x;
+                    } else {
+                        acc[t][u][0] += x[0];
+                        acc[t][u][1] += x[1];
+                        acc[t][u][2] += x[2];
+                        acc[t][u][3] += x[3];
+                    }
+                }
         }
         if (threadIdx.x == 0)
             __hip_atomic_store(p.cnt + tile_g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2127,8 +2153,16 @@ int64_t variant_grid(int id, int64_t M, int64_t N, int64_t K, int cus)
         return tiles * v.splits;
     const int64_t slots = (int64_t)(cus > 0 ? cus : 1) * v.per_cu;
     if (v.kernel == A8W8_KERNEL_SKTILE) {
-        // every slot, unless the whole problem has fewer K blocks than slots
-        const int64_t steps = tiles * (K / 128);
+        // At most half as many tiles as slots: S = slots / tiles aligned pieces per
+        // tile (at most one per K block), one workgroup each.  Otherwise every
+        // slot, unless the whole problem has fewer K blocks than slots.
+        const int64_t KB = K / 128;
+        if (2 * tiles <= slots) {
+            const int64_t S = slots / tiles < KB ? slots / tiles : KB;
+            if (S >= 2)
+                return S * tiles;
+        }
+        const int64_t steps = tiles * KB;
         return steps < slots ? steps : slots;
     }
     return tiles < slots ? tiles : slots;

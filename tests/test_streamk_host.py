@@ -17,6 +17,15 @@ import pytest
 import fp8_block_scaled_a8w8_amd as g
 
 
+def host_grid(T, KB, slots):
+    """The library's grid for a stream-K instance (T tiles, KB blocks each, `slots` workgroup slots)."""
+    if 2 * T <= slots:
+        S = min(slots // T, KB)
+        if S >= 2:
+            return S * T
+    return min(slots, T * KB)
+
+
 def split_work(T, G):
     full, rem = divmod(T, G)
     if rem == 0:
@@ -27,18 +36,25 @@ def split_work(T, G):
 
 def schedule(T, KB, G):
     """Per workgroup rank: list of (tile, kb) steps, plus the fixup facts of each cut piece."""
+    aligned = 2 * T <= G
+    S_al = G // T if aligned else 1
     dp, sk = split_work(T, G)
     S = sk * KB
     assert S == 0 or S >= G, "the host keeps a stream-K grid no larger than the stream"
     B = lambda r: r * S // G
     work = {}
-    pieces = {}          # stream-K tile -> list of (rank, first kb, count, slot)
+    pieces = {}          # stream-K tile -> list of (rank, first kb, count, slot, summed ranks in order)
     for rank in range(G):
         steps = []
-        ntiles = (dp - 1 - rank) // G + 1 if rank < dp else 0
+        ntiles = (dp - 1 - rank) // G + 1 if rank < dp and not aligned else 0
         for i in range(ntiles):
             steps += [(rank + i * G, kb) for kb in range(KB)]
-        for s in range(B(rank), B(rank + 1)):
+        if aligned:
+            t, j = rank % T, rank // T
+            lo, hi = t * KB + j * KB // S_al, t * KB + (j + 1) * KB // S_al
+        else:
+            lo, hi = B(rank), B(rank + 1)
+        for s in range(lo, hi):
             steps.append((dp + s // KB, s % KB))
         work[rank] = steps
         # segments of this rank's stream-K run
@@ -48,22 +64,28 @@ def schedule(T, KB, G):
             n = min(KB - kb0, len(steps) - v)
             if not (kb0 == 0 and n == KB):
                 tp = L - dp
-                x0 = tp * KB
-                r_lo = min(G - 1, ((x0 + 1) * G - 1) // S)
-                r_hi = min(G - 1, ((x0 + KB) * G - 1) // S)
-                slot = 2 * rank + (0 if B(rank) >= x0 else 1)
-                pieces.setdefault(tp, []).append((rank, kb0, n, slot, r_lo, r_hi))
+                if aligned:
+                    order = [tp + j * T for j in range(S_al)]
+                    slot = 2 * rank
+                else:
+                    x0 = tp * KB
+                    r_lo = min(G - 1, ((x0 + 1) * G - 1) // S)
+                    r_hi = min(G - 1, ((x0 + KB) * G - 1) // S)
+                    order = list(range(r_lo, r_hi + 1))
+                    slot = 2 * rank + (0 if B(rank) >= x0 else 1)
+                pieces.setdefault(tp, []).append((rank, kb0, n, slot, tuple(order)))
             v += n
     return dp, sk, work, pieces
 
 
-CASES = [(T, KB, G) for T in (1, 7, 56, 168, 255, 256, 257, 300, 448, 511, 512, 513, 1344, 1792)
-         for KB in (1, 2, 3, 40, 48) for G in (8, 64, 256, 512) if T * KB >= min(G, T * KB)]
+CASES = [(T, KB, slots) for T in (1, 7, 56, 100, 128, 129, 168, 255, 256, 257, 300, 448, 511, 512, 513, 1344, 1792)
+         for KB in (1, 2, 3, 40, 48) for slots in (8, 64, 256, 512)]
 
 
-@pytest.mark.parametrize("T,KB,G", CASES)
-def test_every_block_once_and_fixup_pieces_consistent(T, KB, G):
-    G = min(G, T * KB)                     # the host's grid rule: never more workgroups than blocks
+@pytest.mark.parametrize("T,KB,slots", CASES)
+def test_every_block_once_and_fixup_pieces_consistent(T, KB, slots):
+    G = host_grid(T, KB, slots)
+    assert 1 <= G <= max(slots, 1)
     dp, sk, work, pieces = schedule(T, KB, G)
     seen = {}
     for rank, steps in work.items():
@@ -73,17 +95,21 @@ def test_every_block_once_and_fixup_pieces_consistent(T, KB, G):
     assert len(seen) == T * KB
     # balanced: stream-K runs differ by at most one block
     if sk:
-        lens = [len(w) - ((dp - 1 - r) // G + 1 if r < dp else 0) * KB for r, w in work.items()]
-        assert max(lens) - min(lens) <= 1
+        lens = [len(w) - ((dp - 1 - r) // G + 1 if r < dp and 2 * T > G else 0) * KB for r, w in work.items()]
+        assert max(lens) - min(lens) <= 1, (min(lens), max(lens))
+        assert min(lens) >= 1
     used_slots = set()
     for tp, ps in pieces.items():
         assert 0 <= tp < sk
-        ranks = sorted(p[0] for p in ps)
-        r_lo, r_hi = ps[0][4], ps[0][5]
-        assert all(p[4] == r_lo and p[5] == r_hi for p in ps)
-        assert ranks == list(range(r_lo, r_hi + 1)), (tp, ranks, r_lo, r_hi)
-        assert sum(p[2] for p in ps) == KB                     # the pieces cover the tile's K once
-        for rank, kb0, n, slot, _, _ in ps:
+        order = ps[0][4]
+        assert all(p[4] == order for p in ps)
+        assert sorted(p[0] for p in ps) == sorted(order), (tp, ps)        # the pieces are exactly the summed ranks
+        assert sum(p[2] for p in ps) == KB                               # the pieces cover the tile's K once
+        # summed in K order: each piece starts where the previous one ends
+        by_rank = {p[0]: p for p in ps}
+        starts = [by_rank[r][1] for r in order]
+        assert starts == sorted(starts) and starts[0] == 0
+        for rank, kb0, n, slot, _ in ps:
             assert 0 <= slot < 2 * G
             assert slot // 2 == rank
             assert (rank, slot) not in used_slots
@@ -91,7 +117,7 @@ def test_every_block_once_and_fixup_pieces_consistent(T, KB, G):
     # a rank holds at most two pieces, in different slots
     per_rank = {}
     for ps in pieces.values():
-        for rank, _, _, slot, _, _ in ps:
+        for rank, _, _, slot, _ in ps:
             per_rank.setdefault(rank, []).append(slot)
     assert all(len(v) <= 2 and len(set(v)) == len(v) for v in per_rank.values())
 
@@ -113,7 +139,7 @@ def test_stream_k_instances_exist_and_plan_their_workspace():
             # never more than the problem's K blocks
             per_cu = 2 if (v["bm"], v["bn"]) == (128, 128) else 1
             G = plan["grid"]
-            assert G == min(cus * per_cu, T * (K // 128)), (v["name"], G)
+            assert G == host_grid(T, K // 128, cus * per_cu), (v["name"], G)
             dp, sk = split_work(T, G)
             want = 0 if sk == 0 else 65536 + 2 * G * v["bm"] * v["bn"] * 4
             assert plan["workspace"] == want, (v["name"], M, N, K, plan["workspace"], want)
