@@ -112,5 +112,5 @@ def test_every_lds_dma_copy_is_padded_after_its_m0_write(native_build):
         n += 1
         prev2, prev1 = lines[i - 2].strip(), lines[i - 1].strip()
         assert prev1 == "s_nop 4", (i, prev2, prev1, ln)
-        assert re.match(r"s_mov_b32 m0, s\d+$", prev2), (i, prev2, prev1, ln)
+        assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", prev2), (i, prev2, prev1, ln)
     assert n > 1000, f"only {n} LDS-DMA copies found"
