@@ -1680,6 +1680,9 @@ A8W8_PTILE_INST(64, 64, 2, 2, 4)
 A8W8_PTILE_INST(32, 64, 2, 2, 6)
 A8W8_PTILE_INST(32, 32, 2, 2, 4)
 A8W8_PTILE_INST(32, 32, 2, 2, 8)
+A8W8_PTILE_INST(128, 128, 2, 4, 4)
+A8W8_PTILE_INST(128, 128, 2, 4, 2)
+A8W8_PTILE_INST(128, 128, 4, 2, 3)
 A8W8_PTILE_INST1(256, 256, 2, 4, 2, true)
 A8W8_PTILE_INST1(256, 128, 2, 4, 3, true)
 A8W8_PTILE_INST1(128, 256, 2, 4, 3, true)
@@ -2103,6 +2106,8 @@ const Entry kEntries[] = {
     RSKINNY(1, 3, 16, 2), RSKINNY(2, 5, 8, 1), RSKINNY(4, 3, 8, 1),
     SKTILE(256, 256, 2, 4, 2, 8), SKTILE(256, 128, 2, 4, 3, 8), SKTILE(128, 256, 2, 4, 3, 8),
     SKTILE(128, 128, 2, 2, 2, 8),
+    // 128 x 128 tiles with 8 waves (two per SIMD), for shapes with few tiles
+    PTILE(128, 128, 2, 4, 4, 8), PTILE(128, 128, 2, 4, 2, 16), PTILE(128, 128, 4, 2, 3, 8),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 

@@ -395,7 +395,11 @@ def test_plain_entry_never_splits_and_ex_follows_the_table(N, K):
         assert p["splits"] == 1 and p["workspace"] == 0 and p["name"] == u["name"], (M, p["name"], u["name"])
         e = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=BIG_WS)
         assert e["name"] == r["name"] and e["key_m"] == key, (M, e["name"], r["name"])
-        assert (e["workspace"] > 0) == (int(r.get("splits", 1)) > 1)
+        # a split row always needs its workspace; a stream-K row needs one when it cuts a tile at this M
+        if int(r.get("splits", 1)) > 1:
+            assert e["workspace"] > 0
+        if e["workspace"] > 0:
+            assert gst.cuts_k(r), (M, r["name"])
         if e["workspace"] > 0:
             assert g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=e["workspace"] - 1)["name"] == u["name"]
 
@@ -484,3 +488,13 @@ def test_ceilings_library_builds_and_checks_arguments():
     for args in ((16, 1000, 16, 8, 8), (16, 1024, None, 8, 8), (None, 1024, 16, 8, 8), (16, 1024, 16, 0, 8),
                  (16, 1024, 16, 8, 4), (16, 0, 16, 8, 16)):
         assert fn(*args, None) != 0, args
+
+
+def test_instance_parameters_identify_instances():
+    """The selector table names an instance by (kernel, bm, bn, waves, kblocks, splits): no two
+    compiled instances may share that key."""
+    keys = {}
+    for v in g.variants():
+        k = (v["kernel"], v["bm"], v["bn"], v["waves"], v["kblocks"], v["splits"])
+        assert k not in keys, (v["name"], keys.get(k))
+        keys[k] = v["name"]
