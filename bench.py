@@ -64,7 +64,7 @@ def recorded_traffic():
     or None when the kernel source changed since the counters were taken."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", "skinny_decode_qkv_traffic.md")
+    prof = os.path.join(ROOT, "profiles", "skinny_rskinny_decode_qkv_N14336_K5120_traffic.md")
     src = os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "csrc", "a8w8_kernels.hip")
     try:
         text = open(prof).read()
