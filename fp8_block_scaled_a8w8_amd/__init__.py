@@ -53,6 +53,8 @@ EXPORTED = (
     "gemm_a8w8_status_string",
     "gemm_a8w8_table_hash",
     "a8w8_quantize_1x128",
+    "gemm_a8w8_blockscale_fused_quant",
+    "gemm_a8w8_blockscale_fused_quant_plan",
     "a8w8_prepack_weights",
     "gemm_a8w8_blockscale_packed",
     "gemm_a8w8_blockscale_packed_run_variant",
@@ -162,6 +164,10 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_workspace_init.argtypes = [vp, i64, vp]
         L.gemm_a8w8_blockscale_noalloc.restype = ctypes.c_int
         L.gemm_a8w8_blockscale_noalloc.argtypes = [vp] * 5 + [i64] * 3 + [vp]
+        L.gemm_a8w8_blockscale_fused_quant.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_fused_quant.argtypes = [vp] * 4 + [i64] * 3 + [i32, i32, vp]
+        L.gemm_a8w8_blockscale_fused_quant_plan.restype = ctypes.c_int
+        L.gemm_a8w8_blockscale_fused_quant_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan)]
         _lib = L
     return _lib
 
@@ -393,6 +399,48 @@ def quantize_1x128(X: torch.Tensor, out: torch.Tensor | None = None, scale_out: 
     if rc != A8W8_OK:
         raise A8W8Error(rc, "a8w8_quantize_1x128")
     return out, scale_out
+
+
+def gemm_a8w8_blockscale_fused_quant(X: torch.Tensor, W: torch.Tensor, w_scale: torch.Tensor,
+                                     out: torch.Tensor | None = None, *, packed_n: int | None = None,
+                                     variant: int | None = None, stream=None) -> torch.Tensor:
+    """Decode (M <= 16): bf16 X [M,K] quantised per 1x128 group inside the GEMM kernel, times the
+    block-scaled W; bitwise equal to quantize_1x128 then gemm_a8w8_blockscale_run_variant with the
+    instance gemm_a8w8_blockscale_fused_quant_plan reports.  ``packed_n``: W is in the packed
+    layout (prepack_weights) for N = packed_n rows."""
+    if X.dtype != torch.bfloat16 or X.dim() != 2:
+        raise ValueError("X must be a contiguous bfloat16 [M,K] GPU tensor")
+    if W.dtype not in (torch.float8_e4m3fn, torch.uint8) or W.dim() != 2:
+        raise TypeError("W must be a 2-D float8_e4m3fn (or raw uint8) tensor")
+    if w_scale.dtype != torch.float32:
+        raise TypeError("w_scale must be float32")
+    Wv = W if packed_n is None else _packed_view(W, packed_n)
+    M, K = X.shape
+    N, K2 = Wv.shape
+    if K2 != K or K % 128:
+        raise ValueError(f"X is [M,{K}] and W is [N,{K2}]: K must agree and be a multiple of 128")
+    if tuple(w_scale.shape) != ((N + 127) // 128, K // 128):
+        raise ValueError(f"w_scale must be [{(N + 127) // 128},{K // 128}], got {tuple(w_scale.shape)}")
+    _check_device((("X", X), ("W", W), ("w_scale", w_scale)), X.device)
+    out = _out(out, (M, N), X.device)
+    rc = lib().gemm_a8w8_blockscale_fused_quant(X.data_ptr(), W.data_ptr(), w_scale.data_ptr(), out.data_ptr(),
+                                                M, N, K, 0 if packed_n is None else 1,
+                                                -1 if variant is None else int(variant), _stream_handle(stream))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_blockscale_fused_quant")
+    return out
+
+
+def gemm_a8w8_blockscale_fused_quant_plan(M: int, N: int, K: int, cu_count: int = 0,
+                                          variant: int | None = None) -> dict:
+    p = Plan()
+    rc = lib().gemm_a8w8_blockscale_fused_quant_plan(M, N, K, cu_count, -1 if variant is None else int(variant),
+                                                     ctypes.byref(p))
+    if rc != A8W8_OK:
+        raise A8W8Error(rc, "gemm_a8w8_blockscale_fused_quant_plan")
+    d = p.as_dict()
+    d["name"] = gemm_a8w8_variant_name(d["variant"])
+    return d
 
 
 def packed_rows(N: int) -> int:

@@ -507,6 +507,48 @@ Operands from_desc(const a8w8_gemm_desc &d)
     return {d.A, d.a_scale, d.W, d.w_scale, d.Y, d.batch, d.w_packed, d.scale_kind, d.workspace, d.workspace_bytes};
 }
 
+// The instance the fused-quantisation entry runs: a forced one must be a
+// row-range skinny instance that takes the shape; otherwise, of those that
+// take it, the one with the fewest passes over K, then the most waves, then
+// the most 16-row tiles per workgroup (measured on out_proj, qkv and down_proj
+// at M = 1..16: within 3% of the fastest fused instance).  -1: none.
+int fused_variant(int32_t variant, int64_t M, int64_t N, int64_t K, int cus)
+{
+    if (variant >= 0)
+        return a8w8::variant_fuses_quant(variant) && variant_accepts(variant, M, N, K, cus) ? variant : -1;
+    int best = -1;
+    int64_t best_key = 0;
+    for (int i = 0; i < a8w8::num_variants(); ++i) {
+        if (!a8w8::variant_fuses_quant(i) || !variant_accepts(i, M, N, K, cus))
+            continue;
+        const Variant &v = a8w8::variant(i);
+        const int64_t key = -std::min<int64_t>(a8w8::variant_passes(i, K), 99) * 1000000 + v.waves * 1000 + v.bn;
+        if (best < 0 || key > best_key) {
+            best = i;
+            best_key = key;
+        }
+    }
+    return best;
+}
+
+int fused_check(const void *X, const void *W, const float *w_scale, const void *Y, int64_t M, int64_t N, int64_t K,
+                int32_t w_packed)
+{
+    int rc = check_shape(M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M > 16 || w_packed < 0 || w_packed > 1)
+        return A8W8_ERR_SHAPE;
+    if (M == 0)
+        return A8W8_OK;
+    if (!X || !W || !w_scale || !Y)
+        return A8W8_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(X) & 15) || (reinterpret_cast<uintptr_t>(W) & 15) ||
+        (reinterpret_cast<uintptr_t>(w_scale) & 3) || (reinterpret_cast<uintptr_t>(Y) & 1))
+        return A8W8_ERR_ALIGN;
+    return A8W8_OK;
+}
+
 __global__ void workspace_clear_kernel(uint4 *p, int64_t n16)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
@@ -757,6 +799,60 @@ const char *gemm_a8w8_status_string(int status)
 }
 
 uint64_t gemm_a8w8_table_hash(void) { return a8w8_table::kTableHash; }
+
+int gemm_a8w8_blockscale_fused_quant(const void *X, const void *W, const float *w_scale, void *Y, int64_t M,
+                                     int64_t N, int64_t K, int32_t w_packed, int32_t variant, void *stream)
+{
+    if (variant >= a8w8::num_variants())
+        return A8W8_ERR_PLAN;
+    int rc = fused_check(X, W, w_scale, Y, M, N, K, w_packed);
+    if (rc != A8W8_OK || M == 0)
+        return rc;
+    if (variant >= 0 && (!a8w8::variant_fuses_quant(variant) || !variant_accepts(variant, M, N, K, 0)))
+        return A8W8_ERR_PLAN;
+    int cus = 0;
+    rc = device_ready(&cus);
+    if (rc != A8W8_OK)
+        return rc;
+    const int id = fused_variant(variant, M, N, K, cus);
+    if (id < 0)
+        return A8W8_ERR_PLAN;
+    Args a;
+    std::memset(&a, 0, sizeof(a));
+    a.A = static_cast<const uint8_t *>(X);
+    a.W = static_cast<const uint8_t *>(W);
+    a.w_scale = w_scale;
+    a.Y = static_cast<uint16_t *>(Y);
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.wpk = w_packed;
+    a.sm = 0;
+    a.splits = 1;
+    if (a8w8::launch_quant_fused(id, a, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return A8W8_ERR_HIP;
+    return A8W8_OK;
+}
+
+int gemm_a8w8_blockscale_fused_quant_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, int32_t variant,
+                                          a8w8_plan *out)
+{
+    if (!out)
+        return A8W8_ERR_NULL;
+    if (variant >= a8w8::num_variants())
+        return A8W8_ERR_PLAN;
+    int rc = check_shape(M, N, K);
+    if (rc != A8W8_OK)
+        return rc;
+    if (M > 16)
+        return A8W8_ERR_SHAPE;
+    const int cus = cu_count > 0 ? cu_count : 256;
+    const int id = fused_variant(variant, M > 0 ? M : 1, N, K, cus);
+    if (id < 0)
+        return A8W8_ERR_PLAN;
+    fill_plan(id, M, N, K, 1, cus, M, 0, out);
+    return A8W8_OK;
+}
 
 int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64_t K, void *stream)
 {

@@ -58,6 +58,11 @@ int64_t variant_passes(int id, int64_t K);
 // every workgroup's run of rows fits the instance's tiles on a device with `cus` CUs.
 int64_t rskinny_grid(int id, int64_t N, int cus, bool packed);
 bool rskinny_rows_fit(int id, int64_t N, int cus);
+// Row-range skinny instances also come with fused-quantisation kernels: A is
+// then bf16 [M, K] (a.A; a.a_scale unused) quantised per 1 x 128 group inside
+// the kernel, block scales only (a.sm == 0), one problem.
+bool variant_fuses_quant(int id);
+hipError_t launch_quant_fused(int id, const Args &a, int cus, hipStream_t stream);
 // Raise the dynamic-LDS limit of the instances that need more than 64 KB
 // (once per device, with that device current).
 hipError_t set_kernel_attributes();

@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include "a8w8_internal.h"
+#include "a8w8_quant_math.h"
 #include "gemm_a8w8_blockscale.h"
 
 namespace a8w8 {
@@ -44,6 +45,7 @@ namespace kern {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // Read-only global data read through the constant address space: wave-uniform
@@ -641,6 +643,26 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 // DPP fix (packed: two contiguous kilobytes), one activation fragment per
 // block feeding T MFMAs, and the wave partials summed through LDS in wave
 // order (bitwise reproducible), rounded once to bf16.
+//
+// Fused quantisation (QX, block scales only): A is bf16 [M, K] and the kernel
+// quantises it per 1 x 128 group itself, with the arithmetic of the
+// standalone quantisation kernel, so the codes and scales are the ones that
+// kernel writes, bit for bit, and the result equals quantise-then-GEMM with
+// the same instance bitwise.  Every workgroup quantises all of A (each wave
+// its own blocks), so the work per block is spread over the wave to scale
+// with M: the block's MQ rows (MQ = 1, 2, 4, 8 or 16, the first power of two
+// >= M) take 64 / MQ lanes each, 2 MQ values per lane; the lanes of a row
+// combine their amax with a butterfly, and each lane forms the group scale
+// and its codes.  MQ = 16: the lane's values are exactly those its MFMA
+// operand holds (row l % 16, K 16g..16g+15 and 64+16g..64+16g+15 of the
+// block, g = l / 16), so the codes go straight into the operand and the scale
+// is the lane's own row scale.  MQ < 16: the codes and scales go through the
+// wave's own LDS slot ([block][row][128] bytes) and come back in operand
+// order; lanes of rows >= MQ take zero codes.  MQ = 16 takes the LDS route
+// too where the pass's codes would not fit in registers beside its weights.
+// A pass's activations are loaded before its weights and quantised as soon
+// as they arrive; at MQ = 16 their registers let only the first QE blocks'
+// weights go out with them.
 // Rows [r0, r1) of workgroup b of G: RG-row units split as evenly as integers allow.
 template <bool PK>
 __device__ __forceinline__ void rsk_rows(int b, int G, int N, int &r0, int &r1)
@@ -651,16 +673,44 @@ __device__ __forceinline__ void rsk_rows(int b, int G, int N, int &r0, int &r1)
     r1 = min(N, RG * (int)((int64_t)(b + 1) * units / G));
 }
 
-template <int T, int D, int NW, bool PK, int SM>
+// The amax of a 1 x 128 group over the lanes that hold it: MQ = 16, lanes l,
+// l^16, l^32, l^48 (the MFMA operand layout); otherwise 64 / MQ consecutive lanes.
+template <int MQ>
+__device__ __forceinline__ float group_amax(float m)
+{
+    if constexpr (MQ == 16) {
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+    } else {
+#pragma unroll
+        for (int mask = 32 / MQ; mask >= 1; mask >>= 1)
+            m = fmaxf(m, __shfl_xor(m, mask));
+    }
+    return m;
+}
+
+// QX: bf16 activations quantised in the kernel, MQ rows per block, the first
+// QE blocks' weights issued with the activations (see issue).
+template <int T, int D, int NW, bool PK, int SM, bool QX = false, int QE = D, int MQ = 16>
 __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
 {
+    static_assert(!QX || SM == SM_BLOCK, "fused quantisation makes 1 x 128 fp32 block scales");
+    static_assert(QE >= 1 && QE <= D, "at least one block of weights goes out with the activations");
+    static_assert(MQ == 1 || MQ == 2 || MQ == 4 || MQ == 8 || MQ == 16, "rows per block: a power of two");
+    constexpr int LR = 64 / MQ, XW = MQ;                        // QX: lanes per row, bf16 words per lane
+    // Codes through LDS: MQ < 16, and at MQ = 16 where the pass's codes would
+    // not fit in registers beside its weights (t4_d5: 205 VGPRs, spilled).
+    constexpr bool QLDS = QX && (MQ < 16 || 8 * T * D + 9 * D > 200);
     select_batch(p);
     constexpr bool MX = SM == SM_MX, PER_BLOCK_SCALES = SM != SM_ROWWISE;
+    constexpr bool STAGE_AS = PER_BLOCK_SCALES && !QX;     // a_scale read from memory
     constexpr int SH = wscale_shift<SM>();
     constexpr int AS32 = (16 * D + 63) / 64;                  // a_scale words per lane per pass
     static_assert(T <= NW, "wave t sums and stores tile t");
     __shared__ float s_as[NW][16 * D];                         // this wave's a_scale [m][block of the pass]
     __shared__ v4f red[NW][T][64];
+    __shared__ __align__(16) uint8_t q_lds[QLDS ? NW * D * MQ * 128 : 16];   // [wave][block][row][128]
+    __shared__ float s_lds[QLDS ? NW * D * MQ : 1];                          // [wave][block][row]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int M = p.M, N = p.N, K = p.K, KB = K >> 7;
@@ -670,9 +720,9 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
     const uint32_t lcol = (uint32_t)(g + 4 * (r16 >> 3)) * 16;
     constexpr uint32_t OOB = 0x7ffff000u;                     // beyond any buffer: loads return zeros
     const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(p.W, w_rows<PK>(p) * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)K * (QX ? 2u : 1u));
     const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.W, 0u);   // zero records: every load returns zeros
-    const __amdgpu_buffer_rsrc_t sares = buffer_rsrc(p.a_scale, PER_BLOCK_SCALES ? (uint32_t)(M * KB) * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t sares = buffer_rsrc(p.a_scale, STAGE_AS ? (uint32_t)(M * KB) * 4u : 0u);
     const int NB = (N + (1 << SH) - 1) >> SH;
     const int sb0 = min(r0, N - 1) >> SH;
     // Block scale: the run's rows lie in weight-scale rows sb0 and sb0 + 1 (scalar loads).
@@ -702,6 +752,12 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
         const int m = 8 * h + lrow;
         aoff[h] = m < M ? (uint32_t)m * (uint32_t)K + lcol : OOB;
     }
+    // QX, MQ = 16: bf16 row r16, bytes 32 g (+16) and 128 + 32 g (+16) of each block;
+    // MQ < 16: row qrow = l / LR, bytes 4 MQ qcol (qcol = l % LR) onward.
+    const int qrow = MQ == 16 ? r16 : lane / LR, qcol = MQ == 16 ? g : lane % LR;
+    const uint32_t xoff = qrow < M ? (uint32_t)qrow * (uint32_t)K * 2u +
+                                         (MQ == 16 ? 32u * (uint32_t)g : 4u * MQ * (uint32_t)qcol)
+                                   : OOB;
     // Block scale: output rows n = r0 + 16 t + 4 g + i take scale row sb0 or sb0 + 1.
     bool second[T][4];
 #pragma unroll
@@ -722,15 +778,68 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
         acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     v4i ar[D][2];
+    uint32_t xw[QX ? D : 1][XW];
     v4i wr[D][T][2];
     float asv[AS32];
     float mxw[D][T];
-    // Issue every load of the pass starting at block kb_begin: first this wave's
+    v8i afq[QX && !QLDS ? D : 1];
+    float saq[QX && !QLDS ? D : 1];
+    // The weight loads of block kb_begin + j (blocks past K read through the
+    // zero-record descriptor: no traffic).
+    auto issue_w = [&](int kb_begin, int j) __attribute__((always_inline)) {
+        const int kb = kb_begin + j;
+        const bool live = kb < KB;
+        const int koff = (live ? kb : 0) * 128;
+        const __amdgpu_buffer_rsrc_t rw = live ? wres : none;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int so = PK ? (int)packed_block((uint32_t)((r0 >> 4) + t), (uint32_t)(live ? kb : 0),
+                                                  (uint32_t)KB) : koff;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[t][h], so, 2 /* nt */);
+            if constexpr (MX)
+                mxw[j][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          live ? swres : none, (int)mxoff[t], (live ? kb : 0) * 4, 0));
+        }
+    };
+    // The activation loads of block kb_begin + j (QX: this lane's XW bf16 words).
+    auto issue_a = [&](int kb_begin, int j) __attribute__((always_inline)) {
+        const int kb = kb_begin + j;
+        const bool live = kb < KB;
+        const int koff = (live ? kb : 0) * 128;
+        const __amdgpu_buffer_rsrc_t ra = live ? ares : none;
+        if constexpr (QX) {
+            if constexpr (MQ >= 4) {
+#pragma unroll
+                for (int c = 0; c < XW / 4; ++c) {
+                    const uint32_t at = MQ == 16 ? 16u * (c & 1) + 128u * (c >> 1) : 16u * c;
+                    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(xoff + at), 2 * koff, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xw[j][4 * c + i] = (uint32_t)v[i];
+                }
+            } else if constexpr (MQ == 2) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, (int)xoff, 2 * koff, 0);
+                xw[j][0] = v[0];
+                xw[j][1] = v[1];
+            } else {
+                xw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(ra, (int)xoff, 2 * koff, 0);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff[h], koff, 0);
+        }
+    };
+    // Issue the loads of the pass starting at block kb_begin: first this wave's
     // activation scales (one word per lane: rows m < M, blocks of the pass, in
-    // consecutive words of each row), then the weights and activations; blocks
-    // past K read through the zero-record descriptor (no traffic).
+    // consecutive words of each row), then per block the weights and the
+    // activations.  QX: the pass's bf16 activations first, then the
+    // weights of its first QE blocks only (the rest follow once the
+    // activations are quantised and their registers free).
     auto issue = [&](int kb_begin) {
-        if constexpr (PER_BLOCK_SCALES) {
+        if constexpr (STAGE_AS) {
 #pragma unroll
             for (int u = 0; u < AS32; ++u) {
                 const int i = lane + 64 * u, m = i / D, j = i - m * D;
@@ -739,31 +848,62 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
                                                        sares, ok ? (m * KB + kb_begin + j) * 4 : (int)OOB, 0, 0));
             }
         }
+        if constexpr (QX) {
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const int kb = kb_begin + j;
-            const bool live = kb < KB;
-            const int koff = (live ? kb : 0) * 128;
-            const __amdgpu_buffer_rsrc_t rw = live ? wres : none, ra = live ? ares : none;
+            for (int j = 0; j < D; ++j)
+                issue_a(kb_begin, j);
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int so = PK ? (int)packed_block((uint32_t)((r0 >> 4) + t), (uint32_t)(live ? kb : 0),
-                                                      (uint32_t)KB) : koff;
+            for (int j = 0; j < QE; ++j)
+                issue_w(kb_begin, j);
+        } else {
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[t][h], so, 2 /* nt */);
-                if constexpr (MX)
-                    mxw[j][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                              live ? swres : none, (int)mxoff[t], (live ? kb : 0) * 4, 0));
+            for (int j = 0; j < D; ++j) {
+                issue_w(kb_begin, j);
+                issue_a(kb_begin, j);
             }
+        }
+    };
+    // QX: quantise the pass's activations (into the operand registers, or the
+    // wave's LDS slot), then issue its remaining weights.
+    auto quantise_early = [&](int kb_begin) __attribute__((always_inline)) {
+        if constexpr (QX) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff[h], koff, 0);
+            for (int j = 0; j < D; ++j) {
+                if (kb_begin + j < KB) {
+                    const float m = group_amax<MQ>(bf16_absmax(xw[j]));
+                    uint32_t c[(XW + 1) / 2];
+                    const float sq = quant_bf16(xw[j], m, c);
+                    if constexpr (!QLDS) {
+                        afq[j] = (v8i){(int)c[0], (int)c[1], (int)c[2], (int)c[3],
+                                       (int)c[4], (int)c[5], (int)c[6], (int)c[7]};
+                        saq[j] = sq;
+                    } else {
+                        uint8_t *q = q_lds + ((wave * D + j) * MQ + qrow) * 128 + (MQ == 16 ? 16 : 2 * MQ) * qcol;
+                        if constexpr (MQ == 16) {
+                            *reinterpret_cast<v4i *>(q) = (v4i){(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+                            *reinterpret_cast<v4i *>(q + 64) = (v4i){(int)c[4], (int)c[5], (int)c[6], (int)c[7]};
+                        } else if constexpr (MQ == 8)
+                            *reinterpret_cast<v4i *>(q) = (v4i){(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+                        else if constexpr (MQ == 4)
+                            *reinterpret_cast<v2u *>(q) = (v2u){c[0], c[1]};
+                        else if constexpr (MQ == 2)
+                            *reinterpret_cast<uint32_t *>(q) = c[0];
+                        else
+                            *reinterpret_cast<uint16_t *>(q) = (uint16_t)c[0];
+                        if (qcol == 0)
+                            s_lds[(wave * D + j) * MQ + qrow] = sq;
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = QE; j < D; ++j)
+                issue_w(kb_begin, j);
         }
     };
     // Multiply the pass starting at kb_begin.
     auto consume = [&](int kb_begin) {
-        if constexpr (PER_BLOCK_SCALES) {
+        if constexpr (STAGE_AS) {
             // this wave's scales into its own LDS slot (read back by other lanes of the wave)
 #pragma unroll
             for (int u = 0; u < AS32; ++u)
@@ -776,8 +916,23 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
         for (int j = 0; j < D; ++j) {
             const int kb = kb_begin + j;
             if (kb < KB) {
-                const v8i af = fix_row_layout(ar[j][0], ar[j][1]);
-                const float sa = PER_BLOCK_SCALES ? s_as[wave][min(r16, M - 1) * D + j] : 0.f;
+                v8i af;
+                float sa = 0.f;
+                if constexpr (QX && !QLDS) {
+                    af = afq[j];
+                    sa = saq[j];
+                } else if constexpr (QLDS) {
+                    // rows >= MQ: zero codes (and scale)
+                    const int row = r16 < MQ ? r16 : 0;
+                    const uint8_t *q = q_lds + ((wave * D + j) * MQ + row) * 128 + 16 * g;
+                    const v4i lo = *reinterpret_cast<const v4i *>(q), hi = *reinterpret_cast<const v4i *>(q + 64);
+                    af = r16 < MQ ? cat(lo, hi) : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+                    sa = r16 < MQ ? s_lds[(wave * D + j) * MQ + row] : 0.f;
+                } else {
+                    af = fix_row_layout(ar[j][0], ar[j][1]);
+                    if constexpr (PER_BLOCK_SCALES)
+                        sa = s_as[wave][min(r16, M - 1) * D + j];
+                }
                 float sc0 = 0.f, sc1 = 0.f;
                 if constexpr (SM == SM_BLOCK) {
                     sc0 = sa * wsp0[kb];
@@ -797,13 +952,17 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
                 }
             }
         }
-        if constexpr (PER_BLOCK_SCALES)
+        if constexpr (STAGE_AS)
             __builtin_amdgcn_wave_barrier();       // the slot is rewritten by the next pass
     };
 
     for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
         issue(kb_begin);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (QX) {
+            quantise_early(kb_begin);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         consume(kb_begin);
     }
 
@@ -2030,6 +2189,8 @@ struct Entry {
     Variant v;
     const void *fn[6];
     int lds_bytes;
+    // Row-range skinny instances: the fused-quantisation kernels [log2 MQ][packed W].
+    const void *fq[5][2];
 };
 
 #define FN_ONE(PKV, SMV, ...) reinterpret_cast<const void *>(&__VA_ARGS__, PKV, SMV>)
@@ -2076,9 +2237,22 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
                               FN6(tall_kernel<TPW, NT, D, NW), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
                            FN6(pskinny_kernel<D, NW, P), 0}
+// Fused quantisation, MQ = 16: the weight blocks issued with the bf16
+// activations, as many as keep that moment's registers (16 D activation + 8 T QE
+// weight VGPRs) within those held once the activations are codes (9 D + 8 T D).
+// MQ < 16 holds at most 8 activation VGPRs per block: every block goes out.
+constexpr int rsk_qe(int T, int D, int MQ)
+{
+    return MQ < 16 ? D : D - (7 * D + 8 * T - 1) / (8 * T) > 1 ? D - (7 * D + 8 * T - 1) / (8 * T) : 1;
+}
+#define FQ(T, D, NW, PK, MQ) \
+    reinterpret_cast<const void *>(&rskinny_kernel<T, D, NW, PK, SM_BLOCK, true, rsk_qe(T, D, MQ), MQ>)
+#define FQ2(T, D, NW, MQ) {FQ(T, D, NW, false, MQ), FQ(T, D, NW, true, MQ)}
 // Row-range skinny: T tiles per workgroup at most, about G = WPC workgroups per CU.
 #define RSKINNY(T, D, NW, WPC) {{A8W8_KERNEL_RSKINNY, 16, 16 * T, NW, D, 16, WPC, 1, \
-                                 "rskinny_t" #T "_d" #D "_w" #NW "_g" #WPC}, FN6(rskinny_kernel<T, D, NW), 0}
+                                 "rskinny_t" #T "_d" #D "_w" #NW "_g" #WPC}, FN6(rskinny_kernel<T, D, NW), 0, \
+                                {FQ2(T, D, NW, 1), FQ2(T, D, NW, 2), FQ2(T, D, NW, 4), FQ2(T, D, NW, 8), \
+                                 FQ2(T, D, NW, 16)}}
 
 const Entry kEntries[] = {
     SKINNY(1, 5, 8), SKINNY(2, 5, 8), SKINNY(4, 5, 8), SKINNY(1, 6, 8), SKINNY(2, 6, 8),
@@ -2231,6 +2405,22 @@ hipError_t set_kernel_attributes()
         }
     }
     return hipSuccess;
+}
+
+bool variant_fuses_quant(int id) { return id >= 0 && id < kNumEntries && kEntries[id].fq[0][0] != nullptr; }
+
+hipError_t launch_quant_fused(int id, const Args &a, int cus, hipStream_t stream)
+{
+    if (!variant_fuses_quant(id) || a.sm != 0 || !rskinny_rows_fit(id, a.N, cus))
+        return hipErrorInvalidConfiguration;
+    const int mq = a.M <= 1 ? 0 : a.M <= 2 ? 1 : a.M <= 4 ? 2 : a.M <= 8 ? 3 : 4;
+    const Entry &e = kEntries[id];
+    const int64_t grid = rskinny_grid(id, a.N, cus, a.wpk != 0);
+    int vec = ((reinterpret_cast<uintptr_t>(a.Y) & 7) == 0 && (a.N & 3) == 0) ? 1 : 0;
+    Args args = a;
+    void *params[] = {&args, &vec};
+    return hipLaunchKernel(e.fq[mq][a.wpk ? 1 : 0], dim3((unsigned)grid, 1u), dim3(e.v.waves * 64), params, 0,
+                           stream);
 }
 
 hipError_t launch_variant(int id, const Args &a, int batch, int cus, hipStream_t stream)

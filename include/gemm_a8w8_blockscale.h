@@ -298,6 +298,47 @@ uint64_t gemm_a8w8_table_hash(void);
 int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64_t K, void *stream);
 
 /*
+ * Quantise-and-multiply in one kernel, for decode (M <= 16): X bf16 [M, K] is
+ * quantised per 1x128 group inside the GEMM kernel exactly as
+ * a8w8_quantize_1x128 does it, then multiplied by the block-scaled W:
+ *
+ *   Y = gemm_a8w8_blockscale(quantize_1x128(X), W, w_scale)
+ *
+ * bitwise equal to those two calls in sequence when the GEMM runs the
+ * instance this entry's plan reports (gemm_a8w8_blockscale_run_variant with
+ * plan.variant).  The activation quantisation otherwise runs as a kernel of
+ * its own before every decode GEMM (the "CK int8 GEMM ... gfx90a" page's
+ * decode kernel table, section 3, lists the quantising kernel beside the
+ * GEMM); fusing it saves that launch and the codes' round trip through memory.
+ * The kernels are the row-range skinny ones (A8W8_KERNEL_RSKINNY); each
+ * wave quantises the blocks it multiplies, its lanes spread over the M rows.
+ *
+ * Buffers (device memory, row-major, caller-owned):
+ *   X        bf16 (uint16 bit patterns) [M, K]   16-byte aligned, finite values
+ *   W        uint8 e4m3fn [N, K]                 16-byte aligned (w_packed = 1:
+ *                                                a8w8_prepack_weights layout)
+ *   w_scale  float32 [ceil(N/128), K/128]        4-byte aligned
+ *   Y        bf16 [M, N]                         2-byte aligned; overwritten
+ *   variant  -1: the plan below; else a row-range skinny instance (tuning, tests)
+ * Plan (variant = -1; no tuned table): of the row-range skinny instances that
+ * take (M, N, K), the one with the fewest passes over K, then the most waves,
+ * then the most 16-row tiles per workgroup.  0 <= M <= 16 (A8W8_ERR_SHAPE
+ * otherwise; M == 0 is a no-op); A8W8_ERR_PLAN when no row-range skinny
+ * instance takes (N, K) (they cover N up to 64 rows per CU, e.g. not
+ * N = 34816 on 256 CUs) or a forced instance is not one.  Same threading and
+ * error rules as gemm_a8w8_blockscale: one kernel enqueued, no allocation, no
+ * memset.  The work of quantising grows with M (every workgroup quantises
+ * all of X): on MI355X the fused call is ~19% faster than the two calls at
+ * M = 1 on a 5120 x 6144 weight and about 3% slower at M = 16.
+ */
+int gemm_a8w8_blockscale_fused_quant(const void *X, const void *W, const float *w_scale, void *Y,
+                                     int64_t M, int64_t N, int64_t K, int32_t w_packed, int32_t variant,
+                                     void *stream);
+/* The plan gemm_a8w8_blockscale_fused_quant launches (host only; cu_count 0 = 256). */
+int gemm_a8w8_blockscale_fused_quant_plan(int64_t M, int64_t N, int64_t K, int32_t cu_count, int32_t variant,
+                                          a8w8_plan *out);
+
+/*
  * One call of any scale kind and weight layout, with an optional caller-owned
  * split-K workspace and an optional forced instance.  The plain entries above
  * are this call with workspace = NULL, workspace_bytes = 0, variant = -1.
