@@ -176,7 +176,7 @@ def read_ceiling_block(torch, dev, nbytes, R, replays, us_decode):
             "decode_frac_of_ceiling": round(us / us_decode, 4)}
 
 
-def decode_shape_block(torch, g, inputgen, oracle, dev, N, K, Ms, replays, seed_w=11):
+def decode_shape_block(torch, g, inputgen, oracle, dev, N, K, Ms, replays, seed_w=11, with_fused=True):
     """One decode shape with cold weights (>= 2 GiB of rotated copies): parity gate on the first
     and last copy for every M (all 16 rows against the oracle), then, per M, one HIP graph of R
     calls timed with HIP events; returns per-M us/call and HBM fractions and their mean."""
@@ -201,6 +201,8 @@ def decode_shape_block(torch, g, inputgen, oracle, dev, N, K, Ms, replays, seed_
         per_m[str(M)] = {"us_per_call": round(us, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                          "plan": g.gemm_a8w8_blockscale_plan(M, N, K)["name"]}
         del gm
+    fused = fused_quant_block(torch, g, inputgen, dev, copies, dw, N, K, [m for m in (1, 2, 4, 8, 16) if m in Ms],
+                              replays) if with_fused else {}
     del copies
     torch.cuda.empty_cache()
     us_mean = sum(v["us_per_call"] for v in per_m.values()) / len(per_m)
@@ -208,7 +210,46 @@ def decode_shape_block(torch, g, inputgen, oracle, dev, N, K, Ms, replays, seed_
     return {"us_per_call_mean": round(us_mean, 3),
             "hbm_frac": round(bytes_mean / (us_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_call_mean": round(bytes_mean), "weight_copies": R,
-            "rotate_bytes": R * (W0.nbytes + w_s.nbytes), "parity_worst_rel_l2": round(worst, 6), "per_m": per_m}
+            "rotate_bytes": R * (W0.nbytes + w_s.nbytes), "parity_worst_rel_l2": round(worst, 6), "per_m": per_m,
+            "fused_quantisation": fused}
+
+
+def fused_quant_block(torch, g, inputgen, dev, copies, dw, N, K, Ms, replays):
+    """Decode from bf16 activations: a8w8_quantize_1x128 then gemm_a8w8_blockscale (two kernels)
+    against gemm_a8w8_blockscale_fused_quant (one), per M, each timed as one HIP graph of calls
+    over the rotated weight copies.  Parity gate: the fused result equals the quantise-then-GEMM
+    result with the fused plan's instance bit for bit (first and last copy, every M)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        g.gemm_a8w8_blockscale_fused_quant_plan(1, N, K, cu_count=cus)
+    except g.A8W8Error:
+        return {}
+    X = inputgen.normal_bf16(16, K, 1.0, seed=77).to(torch.bfloat16).to(dev)
+    R = len(copies)
+    out = {}
+    for M in Ms:
+        Xm = X[:M]
+        plan = g.gemm_a8w8_blockscale_fused_quant_plan(M, N, K, cu_count=cus)
+        q, s = g.quantize_1x128(Xm)
+        for r in (0, R - 1):
+            y = g.gemm_a8w8_blockscale_fused_quant(Xm, copies[r], dw)
+            two = g.gemm_a8w8_blockscale_run_variant(plan["variant"], q, s, copies[r], dw)
+            if not torch.equal(y.view(torch.int16), two.view(torch.int16)):
+                raise SystemExit(f"parity gate failed (fused quantisation N={N} K={K} M={M} copy {r})")
+        outM = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        g2 = time_graph(torch, [(lambda r=r: (g.quantize_1x128(Xm, out=q, scale_out=s),
+                                              g.gemm_a8w8_blockscale(q, s, copies[r], dw, out=outM)))
+                                for r in range(R)], 0, 2)
+        us2 = timed_replays(torch, g2, replays) * 1000.0 / R
+        del g2
+        g1 = time_graph(torch, [(lambda r=r: g.gemm_a8w8_blockscale_fused_quant(Xm, copies[r], dw, out=outM))
+                                for r in range(R)], 0, 2)
+        us1 = timed_replays(torch, g1, replays) * 1000.0 / R
+        del g1
+        out[str(M)] = {"fused_us_per_call": round(us1, 3), "quantize_then_gemm_us_per_call": round(us2, 3),
+                       "fused_gain": round(us2 / us1 - 1.0, 4), "fused_plan": plan["name"],
+                       "gemm_plan": g.gemm_a8w8_blockscale_plan(M, N, K)["name"]}
+    return out
 
 
 def mfma_ceiling_block(torch, dev, W_bytes_dev, replays):
@@ -487,6 +528,8 @@ def main():
                     help="N:K of the decode workload (default: the qkv shape 14336:5120)")
     ap.add_argument("--decode-ms", default="1,2,4,8,16", help="M values the decode workload cycles through")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX-scaled and row-wise points")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the bf16-activation legs (quantise then GEMM, and the fused entry)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the run, copy 256 MiB device-to-device three times (traffic calibration)")
     args = ap.parse_args()
@@ -624,6 +667,11 @@ def main():
     del pcopies
     log("prepacked:", json.dumps(packed))
 
+    # the same workload from bf16 activations: quantise then GEMM, against the fused entry
+    fused = {} if args.no_fused else fused_quant_block(torch, g, inputgen, dev, copies, dw, N, K, Ms,
+                                                       max(5, args.steps // 5))
+    log("fused quantisation:", json.dumps(fused))
+
     # ------------------------------------------------------------ prefill (compute-bound)
     prefill = {} if args.no_prefill else prefill_block(torch, g, inputgen, oracle, dev, PREFILL_POINTS)
     log("prefill:", json.dumps(prefill))
@@ -633,7 +681,8 @@ def main():
     if not args.no_decode_shapes:
         for name, (Nd, Kd) in DECODE_SHAPES.items():
             decode_shapes[f"{name}_N{Nd}_K{Kd}"] = decode_shape_block(torch, g, inputgen, oracle, dev, Nd, Kd,
-                                                                     list(range(1, 17)), max(5, args.steps // 5))
+                                                                     list(range(1, 17)), max(5, args.steps // 5),
+                                                                     with_fused=not args.no_fused)
             log(f"decode {name}:", json.dumps(decode_shapes[f"{name}_N{Nd}_K{Kd}"]))
 
     # ------------------------------------------------------------ sustained MFMA ceiling
@@ -689,6 +738,7 @@ def main():
         "mixed_m_graph": mixed,
         "read_ceiling": ceiling,
         "prepacked_weights": packed,
+        "fused_quantisation": fused,
         "prefill": prefill,
         "decode_shapes": decode_shapes,
         "mfma_ceiling": mfma_ceiling,

@@ -192,7 +192,37 @@ int64_t workspace_need(int id, int64_t M, int64_t N, int64_t K, int64_t batch, i
     return kCounterBytes + batch * a8w8::variant_workspace_bytes(id, M, N, K, cus);
 }
 
-// Plan for shapes with no tuned table.  Up to M = 16: the skinny instance
+// Ranking of the row-range skinny instances that take a shape: the fewest
+// passes over K, then the most waves, then the most 16-row tiles per
+// workgroup, then the fewest K blocks per pass.  Measured on the seven untuned
+// decode shapes of 20 MiB and more among ten (N x K from 4608 x 5120 to
+// 16384 x 2048, M = 1, 8, 16), the instance it ranks first is within 7% of the
+// fastest row-range instance (within 2% on all but one of the 21 points).
+// Returns -1 when none takes (M, N, K).
+int best_rskinny(int64_t M, int64_t N, int64_t K, int cus, bool need_fused)
+{
+    int best = -1;
+    int64_t best_key = 0;
+    for (int i = 0; i < a8w8::num_variants(); ++i) {
+        const Variant &v = a8w8::variant(i);
+        if (v.kernel != A8W8_KERNEL_RSKINNY || (need_fused && !a8w8::variant_fuses_quant(i)) ||
+            !variant_accepts(i, M, N, K, cus))
+            continue;
+        const int64_t key = -std::min<int64_t>(a8w8::variant_passes(i, K), 99) * 100000000 +
+                            (int64_t)v.waves * 100000 + (int64_t)v.bn * 100 - v.waves * v.kblocks;
+        if (best < 0 || key > best_key) {
+            best = i;
+            best_key = key;
+        }
+    }
+    return best;
+}
+
+// Plan for shapes with no tuned table.  Up to M = 16: for weights of 20 MiB
+// and more (fp32 block or row-wise scales), the row-range skinny instance ranked first above (measured 2-41%
+// less time than the skinny rule below on those seven shapes: 5120 x 17408 at
+// M = 16 in 23.9 against 40.2 us; on the three smaller ones, 15-17 MB, the
+// skinny rule took up to 15% less time at M = 1); below, the skinny instance
 // with the widest row group that still yields at least ~200 workgroups (wider
 // groups share each activation fragment across more weight tiles), covering
 // K in the fewest passes with the most blocks per pass (8 waves x 6 blocks
@@ -204,8 +234,15 @@ int64_t workspace_need(int id, int64_t M, int64_t N, int64_t K, int64_t batch, i
 // at least two workgroups, else the smallest, with K split (given a
 // workspace) when even that leaves compute units idle.  Returns the plan with
 // split K allowed in *split and the one without in *unsplit.
-void heuristic_variants(int64_t M, int64_t N, int64_t K, int cus, int *split, int *unsplit)
+void heuristic_variants(int64_t M, int64_t N, int64_t K, int cus, int mx, int *split, int *unsplit)
 {
+    if (M <= 16 && !mx && N * K >= ((int64_t)20 << 20)) {
+        const int r = best_rskinny(M, N, K, cus, false);
+        if (r >= 0) {
+            *split = *unsplit = r;
+            return;
+        }
+    }
     if (M <= 16 && skinny_fits(N, K)) {
         int best = -1;
         int64_t best_key = 0;
@@ -309,7 +346,7 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t 
         break;
     }
     int split = -1, unsplit = -1;
-    heuristic_variants(M, N, K, cus, &split, &unsplit);
+    heuristic_variants(M, N, K, cus, mx, &split, &unsplit);
     return {workspace_need(split, M, N, K, batch, cus) <= ws_bytes ? split : unsplit, M, 1};
 }
 
@@ -508,27 +545,14 @@ Operands from_desc(const a8w8_gemm_desc &d)
 }
 
 // The instance the fused-quantisation entry runs: a forced one must be a
-// row-range skinny instance that takes the shape; otherwise, of those that
-// take it, the one with the fewest passes over K, then the most waves, then
-// the most 16-row tiles per workgroup (measured on out_proj, qkv and down_proj
-// at M = 1..16: within 3% of the fastest fused instance).  -1: none.
+// row-range skinny instance that takes the shape; otherwise the one
+// best_rskinny ranks first (on out_proj, qkv and down_proj at M = 1..16 within
+// 3% of the fastest fused instance).  -1: none.
 int fused_variant(int32_t variant, int64_t M, int64_t N, int64_t K, int cus)
 {
     if (variant >= 0)
         return a8w8::variant_fuses_quant(variant) && variant_accepts(variant, M, N, K, cus) ? variant : -1;
-    int best = -1;
-    int64_t best_key = 0;
-    for (int i = 0; i < a8w8::num_variants(); ++i) {
-        if (!a8w8::variant_fuses_quant(i) || !variant_accepts(i, M, N, K, cus))
-            continue;
-        const Variant &v = a8w8::variant(i);
-        const int64_t key = -std::min<int64_t>(a8w8::variant_passes(i, K), 99) * 1000000 + v.waves * 1000 + v.bn;
-        if (best < 0 || key > best_key) {
-            best = i;
-            best_key = key;
-        }
-    }
-    return best;
+    return best_rskinny(M, N, K, cus, true);
 }
 
 int fused_check(const void *X, const void *W, const float *w_scale, const void *Y, int64_t M, int64_t N, int64_t K,

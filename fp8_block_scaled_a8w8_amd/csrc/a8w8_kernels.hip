@@ -661,8 +661,8 @@ __global__ __launch_bounds__(NW * 64) void pskinny_kernel(Args p, int vec_store)
 // order; lanes of rows >= MQ take zero codes.  MQ = 16 takes the LDS route
 // too where the pass's codes would not fit in registers beside its weights.
 // A pass's activations are loaded before its weights and quantised as soon
-// as they arrive; at MQ = 16 their registers let only the first QE blocks'
-// weights go out with them.
+// as they arrive, while the weights stream; where the registers do not hold
+// both, only the first QE blocks' weights go out with the activations.
 // Rows [r0, r1) of workgroup b of G: RG-row units split as evenly as integers allow.
 template <bool PK>
 __device__ __forceinline__ void rsk_rows(int b, int G, int N, int &r0, int &r1)
@@ -673,20 +673,76 @@ __device__ __forceinline__ void rsk_rows(int b, int G, int N, int &r0, int &r1)
     r1 = min(N, RG * (int)((int64_t)(b + 1) * units / G));
 }
 
-// The amax of a 1 x 128 group over the lanes that hold it: MQ = 16, lanes l,
-// l^16, l^32, l^48 (the MFMA operand layout); otherwise 64 / MQ consecutive lanes.
-template <int MQ>
-__device__ __forceinline__ float group_amax(float m)
+// One step of a max-butterfly over lanes: each lane takes the larger of its
+// value and that of lane l ^ MASK.  Within a row of 16 lanes the partner comes
+// through DPP: quad_perm for 1 and 2, then the half-row mirror for 4 and the
+// row mirror for 8 (lane i of 8 reads lane 7 - i, of 16 lane 15 - i), which
+// give the same maxima as l ^ 4 and l ^ 8 once the smaller steps are done, as
+// every lane of a 4- or 8-lane group then holds one value.  16 and 32 cross
+// rows: ds_bpermute.
+template <int MASK>
+__device__ __forceinline__ float amax_step(float m)
 {
+    const int v = __float_as_int(m);
+    int o;
+    if constexpr (MASK == 1)
+        o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    else if constexpr (MASK == 2)
+        o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    else if constexpr (MASK == 4)
+        o = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    else if constexpr (MASK == 8)
+        o = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);   // row_mirror
+    else
+        o = __shfl_xor(v, MASK);
+    return fmaxf(m, __int_as_float(o));
+}
+
+// The amax of each of D 1 x 128 groups over the lanes that hold it: MQ = 16,
+// lanes l, l^16, l^32, l^48 (the MFMA operand layout); otherwise 64 / MQ
+// consecutive lanes, reduced smallest step first (the mirrors need that).
+// Each step runs over all D groups before the next, so their exchanges overlap.
+template <int MQ, int D>
+__device__ __forceinline__ void group_amax(float (&m)[D])
+{
+    constexpr int LR = 64 / MQ;
     if constexpr (MQ == 16) {
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            m[j] = amax_step<16>(m[j]);
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            m[j] = amax_step<32>(m[j]);
     } else {
 #pragma unroll
-        for (int mask = 32 / MQ; mask >= 1; mask >>= 1)
-            m = fmaxf(m, __shfl_xor(m, mask));
+        for (int j = 0; j < D; ++j)
+            m[j] = amax_step<1>(m[j]);
+        if constexpr (LR > 2) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                m[j] = amax_step<2>(m[j]);
+        }
+        if constexpr (LR > 4) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                m[j] = amax_step<4>(m[j]);
+        }
+        if constexpr (LR > 8) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                m[j] = amax_step<8>(m[j]);
+        }
+        if constexpr (LR > 16) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                m[j] = amax_step<16>(m[j]);
+        }
+        if constexpr (LR > 32) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                m[j] = amax_step<32>(m[j]);
+        }
     }
-    return m;
 }
 
 // QX: bf16 activations quantised in the kernel, MQ rows per block, the first
@@ -856,10 +912,29 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
             for (int j = 0; j < QE; ++j)
                 issue_w(kb_begin, j);
         } else {
+            // (written out rather than through issue_w / issue_a: with those the
+            // scheduler moved block 0's loads behind the others, so that the first
+            // MFMA waited for nearly the whole pass -- 9% slower on qkv at M = 8)
 #pragma unroll
             for (int j = 0; j < D; ++j) {
-                issue_w(kb_begin, j);
-                issue_a(kb_begin, j);
+                const int kb = kb_begin + j;
+                const bool live = kb < KB;
+                const int koff = (live ? kb : 0) * 128;
+                const __amdgpu_buffer_rsrc_t rw = live ? wres : none, ra = live ? ares : none;
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int so = PK ? (int)packed_block((uint32_t)((r0 >> 4) + t), (uint32_t)(live ? kb : 0),
+                                                          (uint32_t)KB) : koff;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        wr[j][t][h] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[t][h], so, 2 /* nt */);
+                    if constexpr (MX)
+                        mxw[j][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                  live ? swres : none, (int)mxoff[t], (live ? kb : 0) * 4, 0));
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    ar[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff[h], koff, 0);
             }
         }
     };
@@ -867,12 +942,16 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
     // wave's LDS slot), then issue its remaining weights.
     auto quantise_early = [&](int kb_begin) __attribute__((always_inline)) {
         if constexpr (QX) {
+            float am[D];
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                am[j] = bf16_absmax(xw[j]);
+            group_amax<MQ>(am);
 #pragma unroll
             for (int j = 0; j < D; ++j) {
                 if (kb_begin + j < KB) {
-                    const float m = group_amax<MQ>(bf16_absmax(xw[j]));
                     uint32_t c[(XW + 1) / 2];
-                    const float sq = quant_bf16(xw[j], m, c);
+                    const float sq = quant_bf16(xw[j], am[j], c);
                     if constexpr (!QLDS) {
                         afq[j] = (v8i){(int)c[0], (int)c[1], (int)c[2], (int)c[3],
                                        (int)c[4], (int)c[5], (int)c[6], (int)c[7]};
@@ -2237,16 +2316,22 @@ constexpr int tile_per_cu(int lds_bytes, int waves, int wpc)
                               FN6(tall_kernel<TPW, NT, D, NW), 0}
 #define PSKINNY(D, NW, P) {{A8W8_KERNEL_PSKINNY, 16, 16, NW, D, 16, 1, 1, "pskinny_d" #D "_w" #NW "_p" #P}, \
                            FN6(pskinny_kernel<D, NW, P), 0}
-// Fused quantisation, MQ = 16: the weight blocks issued with the bf16
-// activations, as many as keep that moment's registers (16 D activation + 8 T QE
-// weight VGPRs) within those held once the activations are codes (9 D + 8 T D).
-// MQ < 16 holds at most 8 activation VGPRs per block: every block goes out.
-constexpr int rsk_qe(int T, int D, int MQ)
+// Fused quantisation: the weight blocks issued with the bf16 activations, all
+// of them where the registers allow, else as many as fit (at least one); the
+// rest follow once the activations are codes.  A wave of an NW-wave workgroup
+// has 2048 / NW VGPRs; the activations take 16 D (MQ = 16) or MQ D of them,
+// each weight block 8 T, and addresses, accumulators, codes and temporaries
+// about 48 + 8 D (MQ = 16) or 40 + 4 D (as the compiler allocated them).
+constexpr int rsk_qe_fit(int T, int D, int NW, int MQ)
 {
-    return MQ < 16 ? D : D - (7 * D + 8 * T - 1) / (8 * T) > 1 ? D - (7 * D + 8 * T - 1) / (8 * T) : 1;
+    return (2048 / NW - (MQ == 16 ? 16 * D + 48 + 8 * D : MQ * D + 40 + 4 * D)) / (8 * T);
+}
+constexpr int rsk_qe(int T, int D, int NW, int MQ)
+{
+    return rsk_qe_fit(T, D, NW, MQ) >= D ? D : rsk_qe_fit(T, D, NW, MQ) >= 1 ? rsk_qe_fit(T, D, NW, MQ) : 1;
 }
 #define FQ(T, D, NW, PK, MQ) \
-    reinterpret_cast<const void *>(&rskinny_kernel<T, D, NW, PK, SM_BLOCK, true, rsk_qe(T, D, MQ), MQ>)
+    reinterpret_cast<const void *>(&rskinny_kernel<T, D, NW, PK, SM_BLOCK, true, rsk_qe(T, D, NW, MQ), MQ>)
 #define FQ2(T, D, NW, MQ) {FQ(T, D, NW, false, MQ), FQ(T, D, NW, true, MQ)}
 // Row-range skinny: T tiles per workgroup at most, about G = WPC workgroups per CU.
 #define RSKINNY(T, D, NW, WPC) {{A8W8_KERNEL_RSKINNY, 16, 16 * T, NW, D, 16, WPC, 1, \

@@ -327,9 +327,11 @@ int a8w8_quantize_1x128(const void *X, void *A, float *a_scale, int64_t M, int64
  * instance takes (N, K) (they cover N up to 64 rows per CU, e.g. not
  * N = 34816 on 256 CUs) or a forced instance is not one.  Same threading and
  * error rules as gemm_a8w8_blockscale: one kernel enqueued, no allocation, no
- * memset.  The work of quantising grows with M (every workgroup quantises
- * all of X): on MI355X the fused call is ~19% faster than the two calls at
- * M = 1 on a 5120 x 6144 weight and about 3% slower at M = 16.
+ * memset.  Every workgroup quantises all of X, so that work grows with M:
+ * measured on MI355X against the two calls (both in HIP graphs, cold weights),
+ * the fused call takes 18-23% less time at M = 1..4 on a 5120 x 6144 weight
+ * and 3-5% less on 14336 x 5120 (M = 1..8), but up to 19% more at M = 16;
+ * above M = 8, quantise-then-GEMM is generally the faster path.
  */
 int gemm_a8w8_blockscale_fused_quant(const void *X, const void *W, const float *w_scale, void *Y,
                                      int64_t M, int64_t N, int64_t K, int32_t w_packed, int32_t variant,

@@ -206,6 +206,25 @@ def test_heuristic_skinny_rule():
     assert p["fallback"] == 1 and p["splits"] == 1 and p["kernel_name"] == "skinny"
 
 
+def test_heuristic_row_range_rule_for_large_weights():
+    # Up to M = 16 on an unregistered (N, K) with at least 20 MiB of weights: the
+    # row-range skinny instance with the fewest passes over K, then the most waves,
+    # then the widest, then the shortest pass; below 20 MiB the skinny rule.
+    cases = {(8, 6144, 4096): "rskinny_t2_d3_w16_g1", (1, 5120, 17408): "rskinny_t2_d3_w16_g1",
+             (16, 12288, 4096): "rskinny_t4_d5_w8_g1", (1, 16384, 2048): "rskinny_t4_d3_w8_g1",
+             (8, 10240, 3072): "rskinny_t4_d3_w8_g1", (16, 4608, 5120): "rskinny_t2_d3_w16_g1"}
+    for (M, N, K), name in cases.items():
+        p = g.gemm_a8w8_blockscale_plan(M, N, K, cu_count=256)
+        assert p["fallback"] == 1 and p["name"] == name, (M, N, K, p)
+        assert g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=BIG_WS, cu_count=256)["name"] == name
+    for M, N, K in ((1, 4096, 4096), (16, 7168, 2048), (8, 2048, 8192)):
+        assert g.gemm_a8w8_blockscale_plan(M, N, K, cu_count=256)["kernel_name"] == "skinny", (M, N, K)
+    # rows beyond the largest row-range instance (64 per CU): the skinny rule
+    assert g.gemm_a8w8_blockscale_plan(4, 20480, 2048, cu_count=256)["kernel_name"] == "skinny"
+    # MX scales keep the skinny rule
+    assert g.gemm_a8w8_mxscale_plan(8, 6144, 4096, cu_count=256)["kernel_name"] != "rskinny"
+
+
 def test_unregistered_shape_falls_back_not_fails():
     p = g.gemm_a8w8_blockscale_plan(3, 1000, 384)
     assert p["fallback"] == 1 and p["kernel_name"] == "skinny"

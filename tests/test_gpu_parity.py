@@ -267,6 +267,22 @@ def test_heuristic_skinny_plans(M, N, K):
         assert np.array_equal(y_bits(g.gemm_a8w8_blockscale(dA, da, dW, dw)), first)
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 6144, 4096), (1, 12288, 4096), (16, 16384, 2048), (13, 4608, 5120)])
+def test_heuristic_row_range_plans(M, N, K):
+    # Unregistered shapes with >= 20 MiB of weights at M <= 16: the heuristic's row-range
+    # plan, full output against the oracle and bitwise repeatable.
+    plan = g.gemm_a8w8_blockscale_plan(M, N, K)
+    assert plan["fallback"] == 1 and plan["kernel_name"] == "rskinny"
+    A, a_s = inputgen.make_activations(M, K, seed=M + N)
+    W, w_s = inputgen.make_weights(N, K, seed=K)
+    dA, da, dW, dw = to_dev(A, a_s, W, w_s)
+    say(f"heuristic {plan['name']} M={M} N={N} K={K}")
+    y = g.gemm_a8w8_blockscale(dA, da, dW, dw)
+    first = y_bits(y).copy()
+    assert_parity(y_host(y), oracle.gemm(A, a_s, W, w_s), f"heuristic {plan['name']}")
+    assert np.array_equal(y_bits(g.gemm_a8w8_blockscale(dA, da, dW, dw)), first)
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 5120, 6144), (300, 1000, 1024)])
 def test_doubling_activation_scales_doubles_output(M, N, K):
     A, a_s, W, w_s = _inputs(M, N, K)
