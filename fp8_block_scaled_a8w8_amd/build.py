@@ -13,6 +13,9 @@ SOURCES = [os.path.join(HERE, "csrc", f) for f in ("a8w8_api.hip", "a8w8_kernels
 # a library of their own.
 CEILINGS_LIB = os.path.join(HERE, "libceilings.so")
 CEILINGS_SRC = [os.path.join(HERE, "csrc", f) for f in ("read_ceiling.hip", "mfma_ceiling.hip")]
+# Diagnostics: the same library with the row-range kernel's per-wave timeline stamps
+# compiled in (timeline.py loads it); never loaded by the product path.
+TIMELINE_LIB = os.path.join(HERE, "libgemm_a8w8_timeline.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -61,5 +64,20 @@ def build_ceilings(verbose: bool = False) -> str:
     return CEILINGS_LIB
 
 
+def build_timeline(verbose: bool = False) -> str:
+    """Compile the timeline build (-DA8W8_TIMELINE) into TIMELINE_LIB."""
+    tmp = TIMELINE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-DA8W8_TIMELINE", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(HERE, "csrc"), "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd))
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, TIMELINE_LIB)
+    return TIMELINE_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build_timeline(verbose=True) if "--timeline" in sys.argv[1:] else build(verbose=True))

@@ -40,6 +40,18 @@
 #include "a8w8_quant_math.h"
 #include "gemm_a8w8_blockscale.h"
 
+// Timeline build (-DA8W8_TIMELINE, a separate library that diagnostics load):
+// the row-range skinny kernel stamps the 100 MHz real-time counter at five
+// points of every wave -- entry, first pass issued, last data consumed, after
+// the reduction barrier, after its store -- and its hardware id, into the
+// call's workspace ([workgroup][wave][6] 64-bit words from ws on) when one is
+// given.  The product library compiles none of it.
+#ifdef A8W8_TIMELINE
+#define A8W8_TL(...) __VA_ARGS__
+#else
+#define A8W8_TL(...)
+#endif
+
 namespace a8w8 {
 namespace kern {
 
@@ -1035,21 +1047,25 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
             __builtin_amdgcn_wave_barrier();       // the slot is rewritten by the next pass
     };
 
+    A8W8_TL(uint64_t tl[5] = {__builtin_amdgcn_s_memrealtime(), 0, 0, 0, 0};)
     for (int kb_begin = wave * D; kb_begin < KB; kb_begin += NW * D) {
         issue(kb_begin);
         __builtin_amdgcn_sched_barrier(0);
+        A8W8_TL(if (tl[1] == 0) tl[1] = __builtin_amdgcn_s_memrealtime();)
         if constexpr (QX) {
             quantise_early(kb_begin);
             __builtin_amdgcn_sched_barrier(0);
         }
         consume(kb_begin);
     }
+    A8W8_TL(__builtin_amdgcn_s_waitcnt(0); tl[2] = __builtin_amdgcn_s_memrealtime();)
 
     // Wave t sums tile t over the waves in wave order and stores it.
 #pragma unroll
     for (int t = 0; t < T; ++t)
         red[wave][t][lane] = acc[t];
     __syncthreads();
+    A8W8_TL(tl[3] = __builtin_amdgcn_s_memrealtime();)
     if (wave < T) {
         v4f v = red[0][wave][lane];
 #pragma unroll
@@ -1064,6 +1080,13 @@ __global__ __launch_bounds__(NW * 64) void rskinny_kernel(Args p, int vec_store)
         if (r16 < M && n < r1)
             store4(p.Y, (int64_t)r16 * N, n, N, vec_store != 0, rowwise_apply<SM>(v, rs));
     }
+    A8W8_TL(__builtin_amdgcn_s_waitcnt(0); tl[4] = __builtin_amdgcn_s_memrealtime();
+            if (p.ws != nullptr && lane == 0) {
+                uint64_t *rec = reinterpret_cast<uint64_t *>(p.ws) + ((int)blockIdx.x * NW + wave) * 6;
+                for (int i = 0; i < 5; ++i)
+                    rec[i] = tl[i];
+                rec[5] = __smid();
+            })
 }
 
 // ---------------------------------------------------------------------------
