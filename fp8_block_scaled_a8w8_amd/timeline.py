@@ -7,7 +7,9 @@ call's workspace.  For each decode shape it captures one HIP graph of R calls ov
 rotated weight copies (cold weights, as the benchmark), replays it, reads the stamps of the
 graph's last call, and prints per-workgroup phase percentiles beside the graph's time per call:
 the difference between the two is the time a call spends outside its waves (dispatch, the
-kernel-boundary fences).
+kernel-boundary fences).  Two reference rows follow: the graph time per call of a near-empty
+kernel (256 workgroups reading 4 KB each: the floor a graph node costs) and of the streaming-read
+ceiling kernel at qkv's byte count.
 
     python -m fp8_block_scaled_a8w8_amd.timeline [--reps 3]
 """
@@ -23,7 +25,7 @@ import torch
 
 import inputgen
 from fp8_block_scaled_a8w8_amd import SCALE_KINDS, GemmDesc, gemm_a8w8_ex_plan, variants
-from fp8_block_scaled_a8w8_amd.build import TIMELINE_LIB
+from fp8_block_scaled_a8w8_amd.build import CEILINGS_LIB, TIMELINE_LIB
 
 SHAPES = [(5120, 6144, 1, "rskinny_t2_d3_w16_g1"), (5120, 6144, 16, "rskinny_t2_d3_w16_g1"),
           (14336, 5120, 1, "rskinny_t4_d5_w8_g1"), (14336, 5120, 8, "rskinny_t4_d5_w8_g1"),
@@ -110,6 +112,52 @@ def main() -> None:
               f"{p(ph['end'], 50):.2f} / {ph['end'].max():.2f} |", flush=True)
         del graph, copies
         torch.cuda.empty_cache()
+    floor_and_read(dev, args.reps)
+
+
+def _graph_us(dev, launch, R, reps):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(R):
+            launch(r, s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        for r in range(R):
+            launch(r, s)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / R
+
+
+def floor_and_read(dev, reps):
+    C = ctypes.CDLL(CEILINGS_LIB)
+    C.a8w8_read_ceiling_launch.restype = ctypes.c_int
+    C.a8w8_read_ceiling_launch.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_void_p]
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    small = torch.ones(256 * 4096, dtype=torch.uint8, device=dev)
+
+    def tiny(r, s):
+        assert C.a8w8_read_ceiling_launch(small.data_ptr(), small.numel(), sink.data_ptr(), 256, 16,
+                                          s.cuda_stream) == 0
+    us = _graph_us(dev, tiny, 64, reps)
+    print(f"| graph floor: near-empty kernel | - | read_kernel, 256 WGs x 4 KB | {us:.2f} | | | | | | | |")
+    nbytes = 14336 * 5120
+    R = math.ceil(2 * 2**30 / nbytes)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+
+    def read(r, s):
+        assert C.a8w8_read_ceiling_launch(bufs[r].data_ptr(), nbytes, sink.data_ptr(), 4096, 8,
+                                          s.cuda_stream) == 0
+    us = _graph_us(dev, read, R, reps)
+    print(f"| read ceiling at 14336×5120 bytes | - | read_kernel, 4096 WGs | {us:.2f} | | | | | | | |")
 
 
 if __name__ == "__main__":
