@@ -491,7 +491,10 @@ int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
         return A8W8_OK;
     if (variant >= 0 && !variant_accepts(variant, M, N, K, 0))
         return A8W8_ERR_PLAN;
-    if (variant >= 0 && workspace_need(variant, M, N, K, o.batch, 0) > o.ws_bytes)
+    // A forced split instance's need is known here; a stream-K instance's depends on the
+    // device's CU count (it may cut no tile at all) and is checked once that is known.
+    if (variant >= 0 && a8w8::variant(variant).kernel != A8W8_KERNEL_SKTILE &&
+        workspace_need(variant, M, N, K, o.batch, 0) > o.ws_bytes)
         return A8W8_ERR_WORKSPACE;
     rc = check_pointers(o.A, o.a_scale, o.W, o.w_scale, o.Y);
     if (rc != A8W8_OK)

@@ -2,7 +2,8 @@
 
 For every registered (N, K) and every key M -- each M from 1 to 16, then a
 grid whose consecutive keys satisfy key_{i+1} = floor(1.125 * (key_i + 1)) up
-to 8192 (the selector allows 1.25) -- every compiled kernel instance that
+to 8192 (the selector allows 1.25), plus the multiples of 128 up to 2048 and
+of 256 up to 4096 -- every compiled kernel instance that
 accepts M is timed, and the
 fastest one becomes the table row for that key.  A request M is later served
 by the smallest key >= M, so no M runs an instance tuned for more than 1.25 M.
@@ -57,6 +58,11 @@ MX_EXTRA_KEYS = (48, 768)
 # best instance can change sharply inside one 1.25x interval of the mid-M band
 # (tile-count quantisation), so the finer grid serves every M with a row tuned closer to it.
 KEY_RATIO = 1.125
+# Keys at the tile multiples of the mid-M band as well (every 128 up to 2048, every 256 up to
+# 4096): a key's row is measured at the top of its interval, where the large tiles may need
+# one more row of tiles than just below a multiple of their height -- M = 512 ran the row
+# measured at 574, whose 256 x 256 tiles took 81 us where 128 x 256 takes 56 us at M <= 512.
+TILE_KEYS = tuple(range(256, 2049, 128)) + tuple(range(2304, 4097, 256))
 
 # An unsplit instance within this fraction of the fastest wins the row; a new pick must beat the
 # production row by more than this in both re-measurements.
@@ -215,7 +221,7 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
     import inputgen
     dev = "cuda:0"
     prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
-    grid = key_grid(extra=MX_EXTRA_KEYS if mx else ())
+    grid = key_grid(extra=MX_EXTRA_KEYS if mx else TILE_KEYS)
     done = {k: v for k, v in done.items() if not (k.startswith(f"{prefix}{N}:{K}:") and
                                                    int(k.rsplit(":", 1)[1]) in retune)}
     if all(f"{prefix}{N}:{K}:{M}" in done for M in grid):

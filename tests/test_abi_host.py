@@ -401,8 +401,10 @@ def test_plans_report_splits():
 
 @pytest.mark.parametrize("N,K", REGISTERED)
 def test_plain_entry_never_splits_and_ex_follows_the_table(N, K):
-    """The plain entry's plan never needs a workspace; gemm_a8w8_ex with room for it runs the
-    row's instance, with less room the row's unsplit instance (the one the plain entry runs)."""
+    """The plain entry's plan never needs a workspace: it runs the row's instance when that needs
+    none at this M (a stream-K row whose grid cuts no tile), else the row's unsplit instance;
+    gemm_a8w8_ex with room for the workspace runs the row's instance, with less room the unsplit
+    one."""
     rows = {int(r["key_m"]): r for s in gst.load()["shapes"]
             if (int(s["n"]), int(s["k"])) == (N, K) and not s.get("mx") for r in s["rows"]}
     keys = sorted(rows)
@@ -411,8 +413,9 @@ def test_plain_entry_never_splits_and_ex_follows_the_table(N, K):
         r = rows[key]
         u = gst.unsplit_of(r)
         p = g.gemm_a8w8_blockscale_plan(M, N, K)
-        assert p["splits"] == 1 and p["workspace"] == 0 and p["name"] == u["name"], (M, p["name"], u["name"])
         e = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=BIG_WS)
+        want = r["name"] if e["workspace"] == 0 else u["name"]
+        assert p["splits"] == 1 and p["workspace"] == 0 and p["name"] == want, (M, p["name"], want)
         assert e["name"] == r["name"] and e["key_m"] == key, (M, e["name"], r["name"])
         # a split row always needs its workspace; a stream-K row needs one when it cuts a tile at this M
         if int(r.get("splits", 1)) > 1:

@@ -205,7 +205,7 @@ def test_every_tuned_split_plan_graph_equals_eager(entry):
     """Every split row of the tuned tables at its key M: the plan gemm_a8w8_ex reports is the split
     instance of the row and is what runs (bitwise equal to forcing it); a graph captured on a
     fresh stream replays bitwise equal to eager; the plain entry (no workspace) runs the row's
-    unsplit instance, captured or not."""
+    unsplit instance (its own where that needs no workspace at M), captured or not."""
     sh, rows = _tuned_split_rows()[entry]
     N, K, mx, b = int(sh["n"]), int(sh["k"]), bool(sh.get("mx")), int(sh.get("batch", 1))
     kind = "mx" if mx else "block"
@@ -236,9 +236,11 @@ def test_every_tuned_split_plan_graph_equals_eager(entry):
             f"{kind} N={N} K={K} M={M} {r['name']}")
         forced = g.gemm_a8w8_ex(Am, am, dW, dw, scale_kind=kind, variant=plan["variant"], workspace=ws)
         assert np.array_equal(y_bits(forced), eager), f"M={M}: the reported plan is not what ran"
-        # the plain entry: the row's unsplit instance, no workspace, graph == eager
+        # the plain entry: no workspace, graph == eager; it runs the row's unsplit instance, or the
+        # row's own instance where that cuts nothing at this M (a stream-K grid with whole waves)
         uplan = g.gemm_a8w8_blockscale_plan(M, N, K) if not mx else g.gemm_a8w8_mxscale_plan(M, N, K)
-        assert uplan["name"] == r["unsplit"]["name"] and uplan["splits"] == 1 and uplan["workspace"] == 0
+        want = r["name"] if plan["workspace"] == 0 else r["unsplit"]["name"]
+        assert uplan["name"] == want and uplan["splits"] == 1 and uplan["workspace"] == 0, (M, uplan["name"], want)
         plain = (lambda: g.gemm_a8w8_blockscale(Am, am, dW, dw, out=out)) if not mx else \
             ((lambda: g.batched_gemm_a8w8_mxscale(Am, am, dW, dw, out=out)) if b > 1 else
              (lambda: g.gemm_a8w8_mxscale(Am, am, dW, dw, out=out)))
