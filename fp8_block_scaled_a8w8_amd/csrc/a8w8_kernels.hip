@@ -2390,6 +2390,11 @@ const Entry kEntries[] = {
     SKTILE(128, 128, 2, 2, 2, 8),
     // 128 x 128 tiles with 8 waves (two per SIMD), for shapes with few tiles
     PTILE(128, 128, 2, 4, 4, 8), PTILE(128, 128, 2, 4, 2, 16), PTILE(128, 128, 4, 2, 3, 8),
+    // K split three ways: mid-M shapes whose tiles number about a third of the CUs
+    // (5120 x 6144 at M = 256: 80 tiles of 128 x 128).  (Six- and sixteen-way splits were
+    // tuned too and won no key.)
+    TILE_SK(128, 128, 2, 2, 4, 3), TILE_SK(128, 64, 2, 2, 3, 3), TILE_SK(64, 128, 2, 2, 3, 3),
+    TILE_SK(64, 64, 2, 2, 3, 3), TILE_SK(128, 256, 2, 4, 3, 3),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
