@@ -399,13 +399,13 @@ int gemm_a8w8_workspace_init(void *workspace, int64_t bytes, void *stream);
  * Allocation-free entry: for callers that cannot allocate device memory
  * (code under HIP-graph capture, tight serving loops, harnesses that forbid
  * hipMalloc) yet want the split-K plans, which need a workspace.  Same
- * arguments and result as gemm_a8w8_blockscale, but it runs the table row's
- * fastest plan (what gemm_a8w8_ex runs with an unlimited workspace) and takes
- * that plan's split-K workspace from a static device array of
- * A8W8_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until the
- * process ends.  A plan that needs more than that returns A8W8_ERR_WORKSPACE
- * before anything is enqueued (gemm_a8w8_ex_plan with workspace_bytes =
- * INT64_MAX reports the need as plan.workspace).  It allocates nothing, issues
+ * arguments and result as gemm_a8w8_blockscale, but it runs the plan
+ * gemm_a8w8_ex runs with a workspace of A8W8_NOALLOC_SCRATCH_BYTES -- the
+ * table row's fastest plan when its split-K / stream-K workspace fits that
+ * size, else the row's fastest plan that cuts no K (gemm_a8w8_ex_plan with
+ * that workspace_bytes reports it) -- and takes the workspace from a static
+ * device array of that size per GPU, which the library holds until the
+ * process ends.  It allocates nothing, issues
  * no memset and does not synchronise.  Every call on a GPU shares that GPU's
  * array: calls that overlap in time on one GPU (other streams, concurrent
  * graph replays) race and give wrong results; calls in stream order are safe.
