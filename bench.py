@@ -282,6 +282,70 @@ def mfma_ceiling_block(torch, dev, W_bytes_dev, replays):
                       f"v_mfma_f32_16x16x128_f8f6f4 per wave, fp8 weight bytes as operands"}
 
 
+def cu_capacity_block(torch, dev):
+    """What one CU moves per clock through the data paths of the tile kernels
+    (fp8_block_scaled_a8w8_amd/csrc/cu_capacity.hip): 16-byte LDS reads, 16-byte vector loads into
+    registers and 16-byte direct-to-LDS copies, the last two from a 2 MB buffer (L2-resident) and a
+    64 MB one (beyond L2, inside the 256 MB MALL).  One workgroup of 16 waves per CU; each times its
+    own loop with the shader clock (s_memtime) and the 100 MHz real-time counter, so the figure is
+    bytes per clock of the clock the part ran at, which is reported too.  Median over workgroups."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_block_scaled_a8w8_amd", "libceilings.so"))
+    fn = lib.a8w8_cu_capacity_launch
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    nb = lib.a8w8_cu_capacity_bytes
+    nb.argtypes = [ctypes.c_int]
+    nb.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(2 * cus, dtype=torch.int64, device=dev)
+    res = {}
+    for name, which, size, iters in (("lds_read", 0, 0, 4000), ("vmem_load_L2", 1, 2 << 20, 1000),
+                                     ("vmem_load_MALL", 1, 64 << 20, 1000), ("lds_dma_L2", 2, 2 << 20, 1000),
+                                     ("lds_dma_MALL", 2, 64 << 20, 1000)):
+        src = torch.full((max(size, 16),), 7, dtype=torch.uint8, device=dev)
+        rows = []
+        for _ in range(3):                      # the first launch warms the caches and the clock
+            rc = fn(which, src.data_ptr(), size, out.data_ptr(), cus, iters, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"cu_capacity launch failed ({rc})")
+            torch.cuda.synchronize()
+            rows.append(out.view(cus, 2).cpu().numpy().astype(np.float64))
+        cyc, ticks = rows[-1][:, 0], rows[-1][:, 1]
+        bpc = nb(iters) / cyc
+        res[name] = {"B_per_clk_per_CU": round(float(np.median(bpc)), 1),
+                     "B_per_clk_per_CU_p10_p90": [round(float(np.percentile(bpc, 10)), 1),
+                                                  round(float(np.percentile(bpc, 90)), 1)],
+                     "GB_s_per_CU": round(float(np.median(nb(iters) / (ticks * 10.0))), 1),
+                     "clock_GHz": round(float(np.median(cyc / (ticks * 10.0))), 3)}
+        del src
+    res["config"] = (f"{cus} workgroups x 16 waves (96 KB LDS each: one per CU), 8 16-byte operations per lane "
+                     "per step, contiguous kilobyte per instruction")
+    return res
+
+
+def vendor_fp8_us(torch, a, w, reps=20):
+    """Context, not part of this library: the vendor GEMM library's plain fp8 GEMM (per-tensor unit
+    scales, no block scaling; torch._scaled_mm) on the same fp8 operand bytes, HIP events around
+    `reps` back-to-back calls after three warm-up calls.  Returns us per call, or an error string."""
+    try:
+        one = torch.ones((), dtype=torch.float32, device=a.device)
+        a8, w8 = a.view(torch.float8_e4m3fn), w.view(torch.float8_e4m3fn)
+        for _ in range(3):
+            torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1000.0 / reps
+    except Exception as e:                      # reported, not fatal: this is context only
+        return f"{type(e).__name__}: {str(e)[:160]}"
+
+
 def quantize_bytes(M: int, K: int) -> int:
     """Algorithmic bytes of the activation quantisation: bf16 in, e4m3fn codes and fp32 scales out."""
     return 2 * M * K + M * K + 4 * M * (K // 128)
@@ -467,6 +531,11 @@ def prefill_block(torch, g, inputgen, oracle, dev, points):
             out_res[f"M{Mp}_N{Np}_K{Kp}"] = {"us_per_call": round(ms * 1000, 2), "TFLOP_s": round(tf, 1),
                                              "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4), "plan": plan["name"],
                                              "parity_rows": len(rows), "parity_rel_l2": round(rel, 6)}
+            # context: the vendor library's unscaled fp8 GEMM on the same operand bytes, right after
+            vus = vendor_fp8_us(torch, dA8[:Mp], dWp)
+            out_res[f"M{Mp}_N{Np}_K{Kp}"]["vendor_unscaled_fp8_context"] = (
+                {"us_per_call": round(vus, 2), "TFLOP_s": round(flops(Mp, Np, Kp) / (vus * 1e-6) / 1e12, 1)}
+                if isinstance(vus, float) else {"error": vus})
             log(f"prefill M={Mp} N={Np}: {out_res[f'M{Mp}_N{Np}_K{Kp}']}")
             del gp, out
         del dWp
@@ -692,6 +761,10 @@ def main():
         for v in prefill.values():
             v["frac_of_mfma_ceiling"] = round(v["TFLOP_s"] / mfma_ceiling["TFLOP_s"], 4)
 
+    # ------------------------------------------------------------ per-CU data-path capacities
+    capacity = cu_capacity_block(torch, dev)
+    log("cu capacity:", json.dumps(capacity))
+
     # ------------------------------------------------------------ activation quantisation
     quant = quantize_block(torch, g, inputgen, oracle, dev, max(5, args.steps // 10))
     log("quantize:", json.dumps(quant))
@@ -742,6 +815,7 @@ def main():
         "prefill": prefill,
         "decode_shapes": decode_shapes,
         "mfma_ceiling": mfma_ceiling,
+        "cu_capacity": capacity,
         "quantize": quant,
         "mx": mx,
         "rowwise": rowwise,

@@ -12,7 +12,7 @@ SOURCES = [os.path.join(HERE, "csrc", f) for f in ("a8w8_api.hip", "a8w8_kernels
 # The benchmark's measured ceilings (streaming read, sustained fp8 MFMA): measurement aids,
 # a library of their own.
 CEILINGS_LIB = os.path.join(HERE, "libceilings.so")
-CEILINGS_SRC = [os.path.join(HERE, "csrc", f) for f in ("read_ceiling.hip", "mfma_ceiling.hip")]
+CEILINGS_SRC = [os.path.join(HERE, "csrc", f) for f in ("read_ceiling.hip", "mfma_ceiling.hip", "cu_capacity.hip")]
 # Diagnostics: the same library with the row-range kernel's per-wave timeline stamps
 # compiled in (timeline.py loads it); never loaded by the product path.
 TIMELINE_LIB = os.path.join(HERE, "libgemm_a8w8_timeline.so")

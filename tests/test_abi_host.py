@@ -510,6 +510,18 @@ def test_ceilings_library_builds_and_checks_arguments():
     for args in ((16, 1000, 16, 8, 8), (16, 1024, None, 8, 8), (None, 1024, 16, 8, 8), (16, 1024, 16, 0, 8),
                  (16, 1024, 16, 8, 4), (16, 0, 16, 8, 16)):
         assert fn(*args, None) != 0, args
+    cap = lib.a8w8_cu_capacity_launch
+    cap.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                    ctypes.c_void_p]
+    cap.restype = ctypes.c_int
+    for args in ((3, 16, 1 << 20, 16, 8, 8), (0, None, 0, None, 8, 8), (1, None, 1 << 20, 16, 8, 8),
+                 (1, 16, 3 << 20, 16, 8, 8), (2, 16, 1 << 12, 16, 8, 8), (2, 16, 1 << 29, 16, 8, 8),
+                 (1, 16, 1 << 20, 16, 0, 8), (0, None, 0, 16, 8, 0)):
+        assert cap(*args, None) != 0, args
+    nb = lib.a8w8_cu_capacity_bytes
+    nb.argtypes = [ctypes.c_int]
+    nb.restype = ctypes.c_double
+    assert nb(10) == 16 * 64 * 16 * 8 * 10
 
 
 def test_instance_parameters_identify_instances():

@@ -101,8 +101,7 @@ def test_host_api_under_sanitizers(native_build):
 DMA = re.compile(r"^\s*(buffer_load_dword\w*\s.*\blds\b|global_load_lds_dword\w*\s)")
 
 
-def test_every_lds_dma_copy_is_padded_after_its_m0_write(native_build):
-    path = os.path.join(native_build, "a8w8_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")
+def _check_dma_padding(path, at_least):
     with open(path) as f:
         lines = [ln for ln in f.read().splitlines() if ln.strip() and not ln.strip().startswith(";")]
     n = 0
@@ -113,4 +112,22 @@ def test_every_lds_dma_copy_is_padded_after_its_m0_write(native_build):
         prev2, prev1 = lines[i - 2].strip(), lines[i - 1].strip()
         assert prev1 == "s_nop 4", (i, prev2, prev1, ln)
         assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", prev2), (i, prev2, prev1, ln)
-    assert n > 1000, f"only {n} LDS-DMA copies found"
+    assert n >= at_least, f"only {n} LDS-DMA copies found"
+
+
+def test_every_lds_dma_copy_is_padded_after_its_m0_write(native_build):
+    _check_dma_padding(os.path.join(native_build, "a8w8_kernels-hip-amdgcn-amd-amdhsa-gfx950.s"), 1000)
+
+
+def test_capacity_probe_copies_are_padded(tmp_path):
+    """The per-CU capacity probe (a measurement aid the benchmark runs) uses the same copy form."""
+    try:
+        hipcc = build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    flags = [f for f in build.HIPCC_FLAGS if f != "-shared"]
+    cmd = [hipcc, *flags, "-save-temps", "-c", os.path.join(build.HERE, "csrc", "cu_capacity.hip"),
+           "-o", str(tmp_path / "cu_capacity.o")]
+    res = subprocess.run(cmd, cwd=tmp_path, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    _check_dma_padding(str(tmp_path / "cu_capacity-hip-amdgcn-amd-amdhsa-gfx950.s"), 8)
