@@ -711,9 +711,10 @@ def main():
 
     # the same workload with the weights prepacked offline (a8w8_prepack_weights)
     pcopies = [g.prepack_weights(c) for c in copies]
-    for r in (0, R - 1):                                  # bitwise the same as the row-major call
+    for r in (0, R - 1):            # bitwise the same as the row-major run of the packed plan's instance
         for M in Ms:
-            y_row = g.gemm_a8w8_blockscale(dA[:M], da[:M], copies[r], dw)
+            y_row = g.gemm_a8w8_blockscale_run_variant(g.gemm_a8w8_ex_plan(M, N, K, packed=True)["variant"],
+                                                       dA[:M], da[:M], copies[r], dw)
             y_pk = g.gemm_a8w8_blockscale_packed(dA[:M], da[:M], pcopies[r], dw, N)
             if not torch.equal(y_row.view(torch.int16), y_pk.view(torch.int16)):
                 raise SystemExit(f"parity gate failed (packed weights, copy {r}, M={M})")
@@ -731,8 +732,9 @@ def main():
     packed = {"us_per_call": round(us_pk, 3),
               "hbm_frac": round(bytes_mean / (us_pk * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
               "per_m": per_m_pk,
-              "note": "same workload and plans, weights prepacked offline into the kernels' fragment order; "
-                      "outputs bitwise equal to the row-major call"}
+              "plans": {str(M): g.gemm_a8w8_ex_plan(M, N, K, packed=True)["name"] for M in Ms},
+              "note": "same workload, weights prepacked offline into the kernels' fragment order, plans from "
+                      "the packed decode table; outputs bitwise equal to the row-major run of the same instance"}
     del pcopies
     log("prepacked:", json.dumps(packed))
 

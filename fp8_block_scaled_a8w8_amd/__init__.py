@@ -361,10 +361,11 @@ def gemm_a8w8_ex(A, a_scale, W, w_scale, *, scale_kind: str = "block", packed_n:
 
 
 def gemm_a8w8_ex_plan(M: int, N: int, K: int, *, scale_kind: str = "block", batch: int = 1,
-                      variant: int | None = None, workspace_bytes: int = 0, cu_count: int = 0) -> dict:
+                      variant: int | None = None, workspace_bytes: int = 0, cu_count: int = 0,
+                      packed: bool = False) -> dict:
     """The plan gemm_a8w8_ex launches for this shape with `workspace_bytes` of workspace
-    (host only); plan["workspace"] is the workspace it uses."""
-    d = GemmDesc(None, None, None, None, None, batch, M, N, K, SCALE_KINDS[scale_kind], 0,
+    (host only; packed: weights in the packed layout); plan["workspace"] is the workspace it uses."""
+    d = GemmDesc(None, None, None, None, None, batch, M, N, K, SCALE_KINDS[scale_kind], 1 if packed else 0,
                  -1 if variant is None else int(variant), 0, None, int(workspace_bytes))
     p = Plan()
     rc = lib().gemm_a8w8_ex_plan(ctypes.byref(d), cu_count, ctypes.byref(p))

@@ -18,7 +18,7 @@ CEILINGS_SRC = [os.path.join(HERE, "csrc", f) for f in ("read_ceiling.hip", "mfm
 TIMELINE_LIB = os.path.join(HERE, "libgemm_a8w8_timeline.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-parallel-jobs=4",
     "-Wall", "-Wno-unused-result",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

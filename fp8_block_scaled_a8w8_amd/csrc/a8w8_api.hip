@@ -316,15 +316,25 @@ struct Choice {
     int fallback;
 };
 
-// The instance serving (M, N, K): the fastest one of the table row (or of the
-// heuristic), or -- when the call brings less workspace than that instance
-// needs for `batch` problems -- the fastest one that splits no K.
-Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t batch, int64_t ws_bytes)
+// Table forms (the generated table's `form` field): fp32 block scales with
+// row-major weights, MX, fp32 block scales with prepacked weights, row-wise.
+// The packed and row-wise tables are decode tables (keys 1..16).
+constexpr int FORM_BLOCK = 0, FORM_MX = 1, FORM_PACKED = 2, FORM_ROWWISE = 3;
+
+int call_form(int sm, int wpk)
+{
+    return sm == 1 ? FORM_MX : sm == 2 ? FORM_ROWWISE : wpk ? FORM_PACKED : FORM_BLOCK;
+}
+
+// The row of the (N, K) table of `form` that serves M, if the table has one:
+// its fastest instance, or -- when the call brings less workspace than that
+// instance needs for `batch` problems -- the fastest one that splits no K.
+Choice table_variant(int64_t M, int64_t N, int64_t K, int cus, int form, int64_t batch, int64_t ws_bytes)
 {
     using namespace a8w8_table;
     for (int t = 0; t < kNumShapes; ++t) {
         const ShapeTable &s = kShapes[t];
-        if (s.n != N || s.k != K || s.mx != mx)
+        if (s.n != N || s.k != K || s.form != form)
             continue;
         // smallest key >= M (binary search over the ascending keys)
         int lo = 0, hi = s.count;
@@ -345,8 +355,23 @@ Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int mx, int64_t 
         }
         break;
     }
+    return {-1, M, 1};
+}
+
+// The instance serving (M, N, K) for a call of `form`: the row of that form's
+// table, else (packed and row-wise calls above their decode tables, or without
+// one) the row of the block-scale table -- the MX table for MX calls -- else the
+// heuristic plan (fallback = 1).
+Choice select_variant(int64_t M, int64_t N, int64_t K, int cus, int form, int64_t batch, int64_t ws_bytes)
+{
+    Choice c = table_variant(M, N, K, cus, form, batch, ws_bytes);
+    const int base = form == FORM_MX ? FORM_MX : FORM_BLOCK;
+    if (c.variant < 0 && form != base)
+        c = table_variant(M, N, K, cus, base, batch, ws_bytes);
+    if (c.variant >= 0)
+        return c;
     int split = -1, unsplit = -1;
-    heuristic_variants(M, N, K, cus, mx, &split, &unsplit);
+    heuristic_variants(M, N, K, cus, form == FORM_MX ? 1 : 0, &split, &unsplit);
     return {workspace_need(split, M, N, K, batch, cus) <= ws_bytes ? split : unsplit, M, 1};
 }
 
@@ -507,9 +532,9 @@ int gemm_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
         return A8W8_ERR_PLAN;
     int id = variant;
     if (id < 0) {
-        // Row-wise calls use the block-scale tables: same kernels and loads, less
-        // scale work per block.
-        const Choice c = select_variant(M, N, K, cus, o.sm == 1 ? 1 : 0, o.batch, o.ws_bytes);
+        // Packed and row-wise calls take their own decode tables where tuned and
+        // the block-scale table otherwise: the same kernels serve every form.
+        const Choice c = select_variant(M, N, K, cus, call_form(o.sm, o.wpk), o.batch, o.ws_bytes);
         log_plan(M, N, K, c.variant, c.key_m, c.fallback);
         id = c.variant;
     }
@@ -537,7 +562,7 @@ int plan_impl(int32_t variant, const Operands &o, int64_t M, int64_t N, int64_t 
         fill_plan(variant, M, N, K, batch, cus, M, 0, out);
         return A8W8_OK;
     }
-    const Choice c = select_variant(Mp, N, K, cus, o.sm == 1 ? 1 : 0, batch, o.ws_bytes);
+    const Choice c = select_variant(Mp, N, K, cus, call_form(o.sm, o.wpk), batch, o.ws_bytes);
     fill_plan(c.variant, M, N, K, batch, cus, c.key_m, c.fallback, out);
     return A8W8_OK;
 }
@@ -706,7 +731,7 @@ int gemm_a8w8_blockscale_noalloc(const void *A, const float *a_scale, const void
         return rc;
     // The table's fastest plan when its workspace fits the array, else the
     // fastest one that cuts no K (the selector's rule for a call's workspace).
-    const Choice c = select_variant(M, N, K, cus, 0, 1, (int64_t)A8W8_NOALLOC_SCRATCH_BYTES);
+    const Choice c = select_variant(M, N, K, cus, FORM_BLOCK, 1, (int64_t)A8W8_NOALLOC_SCRATCH_BYTES);
     if (workspace_need(c.variant, M, N, K, 1, cus) > (int64_t)A8W8_NOALLOC_SCRATCH_BYTES)
         return A8W8_ERR_WORKSPACE;
     // Set-up, once per device with that device current: the device address of

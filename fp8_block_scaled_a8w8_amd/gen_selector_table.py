@@ -10,6 +10,10 @@ kernel instance the tuner picked for each key:
 A shape tuned for the MX-scaled variant carries ``"mx": true`` (and the
 batch count it was timed with, ``"batch"``); the selector matches a call's
 variant against it, so block-scale and MX tables for one (N, K) coexist.
+A shape tuned for fp32 block scales with prepacked weights carries
+``"form": "packed"``, one tuned for row-wise scales ``"form": "rowwise"``.
+These two are decode tables (keys 1..16): a call of that form and M <= 16
+takes its row, every other M the block-scale table's.
 
 A row whose instance cuts K across workgroups (split K, "splits" > 1, or a
 stream-K "sktile" instance) also names, under "unsplit", the fastest instance
@@ -19,8 +23,8 @@ one) run that instance, so every key has a plan that needs no workspace.
 A request M is served by the row with the smallest key_m >= M.  The checks
 below make that safe: keys strictly ascending, every key <= 1.25 x the
 smallest M it serves (exact keys for M <= 16), the skinny kernel only for
-keys <= 16, the last key at least 8192, and an unsplit instance for every
-key.
+keys <= 16, the last key at least 8192 (exactly 16 for the packed and
+row-wise decode tables), and an unsplit instance for every key.
 
 Usage: python -m fp8_block_scaled_a8w8_amd.gen_selector_table [--check]
 """
@@ -36,6 +40,18 @@ HEADER = os.path.join(HERE, "csrc", "a8w8_selector_table.h")
 KERNELS = {"skinny": 1, "tile": 2, "ptile": 3, "pskinny": 4, "tall": 5, "rskinny": 6, "sktile": 7}
 MAX_KEY_RATIO = 1.25
 M_COVERED = 8192
+# Table forms: the selector's code for each (0: fp32 block scales, row-major weights).
+FORMS = {"block": 0, "mx": 1, "packed": 2, "rowwise": 3}
+DECODE_FORMS = ("packed", "rowwise")     # tables of M <= 16 only
+
+
+def form_of(sh: dict) -> str:
+    if sh.get("mx"):
+        return "mx"
+    f = sh.get("form", "block")
+    if f not in FORMS or f == "mx":
+        raise ValueError(f"unknown table form {f!r}")
+    return f
 
 
 def load(path: str = TABLE_JSON) -> dict:
@@ -48,9 +64,10 @@ def load(path: str = TABLE_JSON) -> dict:
 def validate(table: dict) -> None:
     seen = set()
     for sh in table["shapes"]:
-        key = (int(sh["n"]), int(sh["k"]), bool(sh.get("mx", False)))
+        form = form_of(sh)
+        key = (int(sh["n"]), int(sh["k"]), form)
         if key in seen:
-            raise ValueError(f"duplicate (N,K,mx) {key}")
+            raise ValueError(f"duplicate (N,K,form) {key}")
         seen.add(key)
         rows = sh["rows"]
         if not rows:
@@ -75,8 +92,9 @@ def validate(table: dict) -> None:
             if u["kernel"] in ("skinny", "pskinny", "rskinny") and km > 16:
                 raise ValueError(f"{key}: skinny kernel for key {km} > 16")
             prev = km
-        if prev < M_COVERED:
-            raise ValueError(f"{key}: table stops at M={prev} < {M_COVERED}")
+        covered = 16 if form in DECODE_FORMS else M_COVERED
+        if prev < covered or (form in DECODE_FORMS and prev > 16):
+            raise ValueError(f"{key}: table stops at M={prev}, needs {covered}")
 
 
 def cuts_k(row: dict) -> bool:
@@ -102,7 +120,7 @@ def fnv1a64(data: bytes) -> int:
 
 
 def _order(sh: dict):
-    return (bool(sh.get("mx", False)), int(sh["n"]), int(sh["k"]))
+    return (FORMS[form_of(sh)], int(sh["n"]), int(sh["k"]))
 
 
 def canonical(table: dict) -> bytes:
@@ -110,8 +128,8 @@ def canonical(table: dict) -> bytes:
     for sh in sorted(table["shapes"], key=_order):
         for r in sh["rows"]:
             row = [sh["n"], sh["k"], r["key_m"], r["kernel"], r["bm"], r["bn"], r["waves"], r.get("kblocks", 1)]
-            if sh.get("mx"):
-                row.append("mx")
+            if form_of(sh) != "block":
+                row.append(form_of(sh))
             if cuts_k(r):
                 if int(r.get("splits", 1)) > 1:
                     row.append(f"k{int(r['splits'])}")
@@ -132,7 +150,7 @@ def render(table: dict) -> str:
     out.append("")
     out.append("struct ShapeTable {")
     out.append("    int64_t n, k;")
-    out.append("    int32_t mx;   // 1: tuned for the MX-scaled variant")
+    out.append("    int32_t form;   // 0 fp32 block scales, 1 MX, 2 block scales + packed weights, 3 row-wise")
     out.append("    int count;")
     out.append("    const int64_t *key_m;")
     out.append("    const int32_t *kernel, *bm, *bn, *waves, *kblocks, *splits;   // fastest instance")
@@ -162,7 +180,7 @@ def render(table: dict) -> str:
     if shapes:
         out.append("static const ShapeTable kShapes[] = {")
         for i, sh in enumerate(shapes):
-            out.append(f"    {{{int(sh['n'])}, {int(sh['k'])}, {1 if sh.get('mx') else 0}, {len(sh['rows'])}, "
+            out.append(f"    {{{int(sh['n'])}, {int(sh['k'])}, {FORMS[form_of(sh)]}, {len(sh['rows'])}, "
                        f"s{i}_key, s{i}_kernel, "
                        f"s{i}_bm, s{i}_bn, s{i}_waves, s{i}_kblocks, s{i}_splits, "
                        f"s{i}_u_kernel, s{i}_u_bm, s{i}_u_bn, s{i}_u_waves, s{i}_u_kblocks}},")

@@ -9,7 +9,7 @@ fastest one becomes the table row for that key.  A request M is later served
 by the smallest key >= M, so no M runs an instance tuned for more than 1.25 M.
 
 Timing follows the cold-weight method: each call reads its own copy of W
-(copies totalling >= --rotate-gib, default 1 GiB, four times the 256 MB MALL,
+(copies totalling >= --rotate-gib, default 2 GiB, eight times the 256 MB MALL,
 at most --max-copies of them; copies are sign-flipped versions of one seeded
 W), R calls are captured in
 one HIP graph, the graph is replayed, and the per-call time is the median of
@@ -25,7 +25,14 @@ operands; --batch b times the batched form with b problems per call), and
 the shapes are stored with "mx": true -- by default the page's MX shapes,
 the dense (N, K) pairs and the batched b = 8, N = 1024, K = 4096 one.
 
+With --form packed (fp32 block scales, weights prepacked by
+a8w8_prepack_weights) or --form rowwise (per-row fp32 scales) the decode keys
+M = 1..16 of that form are tuned, by default on the three decode shapes, and
+stored with "form": "packed" / "rowwise"; calls of that form with M > 16 take
+the block-scale table.
+
 Usage: python -m fp8_block_scaled_a8w8_amd.tune [--shapes N:K,...] [--rounds 3] [--mx [--batch b]]
+                                                [--form packed|rowwise]
 """
 from __future__ import annotations
 
@@ -48,6 +55,11 @@ REGISTERED = [(5120, 6144), (14336, 5120), (16384, 5120), (34816, 5120), (256, 6
 # MX-scaled shapes of the gfx1250 BF16 and MX32 tuned-rows page (ROCm/aiter #7247,
 # Technical Details): dense (N, K) pairs, and the batched one as N:K:batch.
 REGISTERED_MX = ["1792:5120", "4608:5120", "5120:2304", "5120:8192", "32768:1280", "1024:4096:8"]
+
+
+# Decode shapes whose packed-weight and row-wise forms get decode tables of their own.
+REGISTERED_DECODE = ["14336:5120", "5120:6144", "34816:5120"]
+FORM_PREFIX = {"packed": "pk:", "rowwise": "rw:"}
 
 
 # The M values the MX page times (M = 16, 48, 768) get exact keys in the MX tables.
@@ -104,7 +116,7 @@ def key_grid(limit: int = 8192, extra=()) -> list[int]:
     return sorted(set(keys) | set(extra))
 
 
-def candidates(M: int, N: int, K: int) -> list[dict]:
+def candidates(M: int, N: int, K: int, packed: bool = False) -> list[dict]:
     out = []
     for v in variants():
         if v["kernel_name"] == "skinny":
@@ -122,7 +134,7 @@ def candidates(M: int, N: int, K: int) -> list[dict]:
             # the instance must take the shape: each workgroup's run of rows within its tiles
             if M <= 16:
                 try:
-                    gemm_a8w8_ex_plan(M, N, K, variant=v["variant"])
+                    gemm_a8w8_ex_plan(M, N, K, variant=v["variant"], packed=packed)
                     out.append(v)
                 except A8W8Error:
                     pass
@@ -183,10 +195,14 @@ def time_graph(g, reps: int) -> float:
     return t0.elapsed_time(t1) / reps
 
 
-def _operands(N: int, K: int, mx: bool, batch: int):
+def _operands(N: int, K: int, mx: bool, batch: int, form: str | None = None):
     """Seeded operands on the device: activations for M up to 8192, one weight copy, scales."""
     import inputgen
     dev = "cuda:0"
+    if form == "rowwise":
+        A, a_s = inputgen.make_rowwise_activations(8192, K, seed=0)
+        W0, w_s = inputgen.make_rowwise_weights(N, K, seed=1)
+        return [torch.from_numpy(x).to(dev) for x in (A, a_s)], W0, torch.from_numpy(w_s).to(dev)
     if not mx:
         A, a_s = inputgen.make_activations(8192, K, seed=0)
         W0, w_s = inputgen.make_weights(N, K, seed=1)
@@ -217,20 +233,23 @@ def _measure(cands, make_calls, R: int, rounds: int) -> dict:
 
 def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
                mx: bool = False, batch: int = 1, results_path: str = RESULTS, max_copies: int = 256,
-               production: dict | None = None, retune=()) -> list[dict]:
+               production: dict | None = None, retune=(), form: str | None = None) -> list[dict]:
     import inputgen
+    from . import prepack_weights
     dev = "cuda:0"
-    prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else ""
-    grid = key_grid(extra=MX_EXTRA_KEYS if mx else TILE_KEYS)
+    prefix = ("mx" + (str(batch) if batch > 1 else "") + ":") if mx else FORM_PREFIX.get(form, "")
+    grid = key_grid(limit=16) if form else key_grid(extra=MX_EXTRA_KEYS if mx else TILE_KEYS)
     done = {k: v for k, v in done.items() if not (k.startswith(f"{prefix}{N}:{K}:") and
                                                    int(k.rsplit(":", 1)[1]) in retune)}
     if all(f"{prefix}{N}:{K}:{M}" in done for M in grid):
         return [row_from_log(done[f"{prefix}{N}:{K}:{M}"]) for M in grid]   # all measured: no GPU needed
-    (dA, da), W0, dw = _operands(N, K, mx, batch)
+    (dA, da), W0, dw = _operands(N, K, mx, batch, form)
     R = max(2, math.ceil(rotate_gib * 2**30 / (W0.nbytes + dw.numel() * dw.element_size())))
     R = min(R, max_copies)          # tiny weights: bounded graphs (the activations dominate the traffic there)
     copies = [torch.from_numpy(W0).to(dev)] + \
         [torch.from_numpy(inputgen.sign_flip_copy(W0, seed=1000 + r)).to(dev) for r in range(1, R)]
+    if form == "packed":
+        copies = [prepack_weights(c) for c in copies]
     ws = Workspace(batch * (128 << 20) + (1 << 20))
     by_name = {v["name"]: v for v in variants()}
     prod_rows = {int(r["key_m"]): r for r in (production or {}).get("rows", [])}
@@ -240,7 +259,7 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
         if key in done:
             rows.append(row_from_log(done[key]))
             continue
-        cands = candidates(M, N, K)
+        cands = candidates(M, N, K, packed=form == "packed")
         if mx:
             lead = (batch,) if batch > 1 else ()
             Am = (dA[:, :M] if batch > 1 else dA[:M]).contiguous()
@@ -251,9 +270,11 @@ def tune_shape(N: int, K: int, rounds: int, rotate_gib: float, done: dict, log,
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
         def make_calls(v):
-            kind = "mx" if mx else "block"
-            return [(lambda r=r, vid=v["variant"]: gemm_a8w8_ex(Am, am, copies[r], dw, scale_kind=kind, variant=vid,
-                                                                workspace=ws, out=out)) for r in range(R)]
+            kind = "mx" if mx else "rowwise" if form == "rowwise" else "block"
+            pn = N if form == "packed" else None
+            return [(lambda r=r, vid=v["variant"]: gemm_a8w8_ex(Am, am, copies[r], dw, scale_kind=kind, packed_n=pn,
+                                                                variant=vid, workspace=ws, out=out))
+                    for r in range(R)]
 
         med = _measure(cands, make_calls, R, rounds)
         row = pick_row(M, med, by_name)
@@ -351,7 +372,7 @@ def rebuild(results_path: str = RESULTS) -> dict:
     out = []
     for sh in table["shapes"]:
         b = int(sh.get("batch", 1))
-        prefix = ("mx" + (str(b) if b > 1 else "") + ":") if sh.get("mx") else ""
+        prefix = ("mx" + (str(b) if b > 1 else "") + ":") if sh.get("mx") else FORM_PREFIX.get(sh.get("form"), "")
         rows = []
         for r in sh["rows"]:
             rec = done.get(f"{prefix}{sh['n']}:{sh['k']}:{r['key_m']}")
@@ -366,6 +387,8 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--shapes", default=None, help="N:K[,N:K...] (MX: N:K[:batch])")
     ap.add_argument("--mx", action="store_true", help="tune the MX-scaled variant")
+    ap.add_argument("--form", choices=sorted(FORM_PREFIX), default=None,
+                    help="tune the decode keys of the packed-weight or row-wise form")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--rotate-gib", type=float, default=2.0)
     ap.add_argument("--max-copies", type=int, default=256, help="at most this many weight copies per graph")
@@ -400,8 +423,11 @@ def main(argv=None) -> int:
         lo, _, hi = part.partition("-")
         retune.update(range(int(lo), int(hi or lo) + 1))
     table = gst.load()
-    shapes = {(int(s["n"]), int(s["k"]), bool(s.get("mx", False))): s for s in table["shapes"]}
-    default = REGISTERED_MX if args.mx else [f"{n}:{k}" for n, k in REGISTERED]
+    if args.mx and args.form:
+        ap.error("--mx and --form are exclusive")
+    shapes = {(int(s["n"]), int(s["k"]), gst.form_of(s)): s for s in table["shapes"]}
+    form = "mx" if args.mx else args.form or "block"
+    default = REGISTERED_MX if args.mx else REGISTERED_DECODE if args.form else [f"{n}:{k}" for n, k in REGISTERED]
     for item in (args.shapes.split(",") if args.shapes else default):
         f = [int(x) for x in item.split(":")]
         N, K = f[0], f[1]
@@ -409,12 +435,15 @@ def main(argv=None) -> int:
         t = time.time()
         rows = tune_shape(N, K, args.rounds, args.rotate_gib, done, log, mx=args.mx, batch=batch,
                           results_path=args.results, max_copies=args.max_copies,
-                          production=shapes.get((N, K, args.mx)), retune=retune)
+                          production=shapes.get((N, K, form)) or (shapes.get((N, K, "block")) if args.form else None),
+                          retune=retune, form=args.form)
         entry = {"n": N, "k": K, "rows": [table_row(r) for r in rows]}
         if args.mx:
             entry = {"n": N, "k": K, "mx": True, "batch": batch, "rows": entry["rows"]}
-        shapes[(N, K, args.mx)] = entry
-        log(f"tuned {'MX ' if args.mx else ''}N={N} K={K} batch={batch} in {time.time() - t:.1f}s")
+        elif args.form:
+            entry = {"n": N, "k": K, "form": args.form, "rows": entry["rows"]}
+        shapes[(N, K, form)] = entry
+        log(f"tuned {form} N={N} K={K} batch={batch} in {time.time() - t:.1f}s")
         table = {"shapes": sorted(shapes.values(), key=gst._order)}
         gst.validate(table)
         with open(gst.TABLE_JSON, "w") as f:

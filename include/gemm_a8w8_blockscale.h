@@ -162,9 +162,13 @@ int gemm_a8w8_blockscale_run_variant(int32_t variant,
  *
  * a8w8_prepack_weights enqueues the conversion (W and Wp device memory,
  * 16-byte aligned, not overlapping; K % 128 == 0).  gemm_a8w8_blockscale_packed
- * computes exactly what gemm_a8w8_blockscale computes from the same W (the
- * same kernels and instances, bitwise identical Y) reading Wp instead; N is
- * the real row count.  Same contract otherwise.
+ * computes what gemm_a8w8_blockscale computes from the same W, reading Wp
+ * instead; N is the real row count.  Every instance gives bitwise the same Y
+ * on Wp as on W (_run_variant); the packed entry's plan comes from its own
+ * decode table where one is tuned (M <= 16 on the tuned decode shapes: the
+ * contiguous loads favour other instances there) and from the block-scale
+ * table otherwise (gemm_a8w8_ex_plan with w_packed = 1 reports it).  Same
+ * contract otherwise.
  */
 int a8w8_prepack_weights(const void *W, void *Wp, int64_t N, int64_t K, void *stream);
 int gemm_a8w8_blockscale_packed(const void *A, const float *a_scale,
@@ -243,8 +247,10 @@ int gemm_a8w8_mxscale_run_variant(int32_t variant, const void *A, const void *a_
  * once, in that order, before the round to nearest even.  Buffers as for
  * gemm_a8w8_blockscale except a_scale float32 [M] and w_scale float32 [N]
  * (4-byte aligned).  The _packed form reads a8w8_prepack_weights output.  Same
- * kernels and selection tables as the block-scale entries, same threading and
- * error rules; bitwise reproducible.
+ * kernels as the block-scale entries; plans from the row-wise decode tables
+ * (M <= 16 on the tuned decode shapes, either weight layout) and the
+ * block-scale tables otherwise; same threading and error rules; bitwise
+ * reproducible.
  */
 int gemm_a8w8_rowwise(const void *A, const float *a_scale,
                       const void *W, const float *w_scale,

@@ -165,8 +165,9 @@ def test_table_validation_rejects_bad_tables():
         gst.validate(bad)
 
 
-def _table_shapes(mx=False):
-    return [(int(s["n"]), int(s["k"])) for s in gst.load()["shapes"] if bool(s.get("mx", False)) == mx]
+def _table_shapes(mx=False, form=None):
+    want = form or ("mx" if mx else "block")
+    return [(int(s["n"]), int(s["k"])) for s in gst.load()["shapes"] if gst.form_of(s) == want]
 
 
 @pytest.mark.parametrize("N,K", REGISTERED)
@@ -406,7 +407,7 @@ def test_plain_entry_never_splits_and_ex_follows_the_table(N, K):
     gemm_a8w8_ex with room for the workspace runs the row's instance, with less room the unsplit
     one."""
     rows = {int(r["key_m"]): r for s in gst.load()["shapes"]
-            if (int(s["n"]), int(s["k"])) == (N, K) and not s.get("mx") for r in s["rows"]}
+            if (int(s["n"]), int(s["k"])) == (N, K) and gst.form_of(s) == "block" for r in s["rows"]}
     keys = sorted(rows)
     for M in list(range(1, 200)) + list(range(200, 8193, 37)):
         key = next(k for k in keys if k >= M)
@@ -424,6 +425,45 @@ def test_plain_entry_never_splits_and_ex_follows_the_table(N, K):
             assert gst.cuts_k(r), (M, r["name"])
         if e["workspace"] > 0:
             assert g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=e["workspace"] - 1)["name"] == u["name"]
+
+
+@pytest.mark.parametrize("form", ["packed", "rowwise"])
+def test_decode_form_tables_serve_m_up_to_16_and_block_table_above(form):
+    """Packed-weight and row-wise calls take their own decode table (exact keys 1..16) where one
+    is tuned, and the block-scale table's plan for every other M."""
+    shapes = _table_shapes(form=form)
+    if not shapes:
+        pytest.skip(f"no {form} tables")
+    kind = "rowwise" if form == "rowwise" else "block"
+    packed = form == "packed"
+    for N, K in shapes:
+        rows = {int(r["key_m"]): r for s in gst.load()["shapes"]
+                if (int(s["n"]), int(s["k"])) == (N, K) and gst.form_of(s) == form for r in s["rows"]}
+        assert sorted(rows) == list(range(1, 17))
+        for M in range(1, 17):
+            e = g.gemm_a8w8_ex_plan(M, N, K, scale_kind=kind, packed=packed, workspace_bytes=BIG_WS)
+            assert e["fallback"] == 0 and e["key_m"] == M and e["name"] == rows[M]["name"], (N, K, M, e["name"])
+        for M in list(range(17, 300, 7)) + [1024, 4097, 8192]:
+            e = g.gemm_a8w8_ex_plan(M, N, K, scale_kind=kind, packed=packed, workspace_bytes=BIG_WS)
+            b = g.gemm_a8w8_ex_plan(M, N, K, workspace_bytes=BIG_WS)
+            assert (e["name"], e["key_m"], e["fallback"]) == (b["name"], b["key_m"], 0), (N, K, M)
+    # a row-wise call with packed weights takes the row-wise table; MX calls never take these tables
+    for N, K in shapes:
+        if form == "rowwise":
+            assert g.gemm_a8w8_ex_plan(3, N, K, scale_kind="rowwise", packed=True)["name"] == \
+                g.gemm_a8w8_ex_plan(3, N, K, scale_kind="rowwise")["name"]
+
+
+def test_table_validation_of_decode_forms():
+    rows = [{"key_m": m, "kernel": "skinny", "bm": 16, "bn": 16, "waves": 4} for m in range(1, 17)]
+    gst.validate({"shapes": [{"n": 64, "k": 128, "form": "packed", "rows": rows}]})
+    with pytest.raises(ValueError):                           # a decode table stops at 16
+        gst.validate({"shapes": [{"n": 64, "k": 128, "form": "packed",
+                                  "rows": rows + [{"key_m": 20, "kernel": "tile", "bm": 32, "bn": 32, "waves": 4}]}]})
+    with pytest.raises(ValueError):                           # ... and covers every M up to 16
+        gst.validate({"shapes": [{"n": 64, "k": 128, "form": "rowwise", "rows": rows[:8]}]})
+    with pytest.raises(ValueError):
+        gst.validate({"shapes": [{"n": 64, "k": 128, "form": "other", "rows": rows}]})
 
 
 def _desc(**kw):

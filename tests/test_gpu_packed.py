@@ -1,8 +1,11 @@
 """GPU tests of the packed weight layout (a8w8_prepack_weights, gemm_a8w8_blockscale_packed).
 
-The packed path must compute exactly what the row-major path computes: the
-same kernels and accumulation order, so Y is compared bitwise with the
-row-major call, and against the oracle to the parity bar.  The layout itself
+Every instance must compute on packed weights exactly what it computes on
+row-major weights: the same kernels and accumulation order, so Y is compared
+bitwise with the row-major run of the same instance, and against the oracle
+to the parity bar.  The packed entry's own plan (its decode table on the
+tuned decode shapes, the block-scale table elsewhere) is checked the same
+way.  The layout itself
 is checked byte for byte against a numpy permutation written from its
 definition in include/gemm_a8w8_blockscale.h.
 """
@@ -86,7 +89,10 @@ def test_selector_plan_packed_equals_row_major(N, K, Ms):
     dA, da, dW, dw = to_dev(A, a_s, W, w_s)
     dWp = g.prepack_weights(dW)
     for M in Ms:
-        y_row = g.gemm_a8w8_blockscale(dA[:M], da[:M], dW, dw)
+        plan = g.gemm_a8w8_ex_plan(M, N, K, packed=True)
         y_pk = g.gemm_a8w8_blockscale_packed(dA[:M], da[:M], dWp, dw, N)
-        assert np.array_equal(y_bits(y_pk), y_bits(y_row)), f"M={M} N={N} K={K}"
+        y_row = g.gemm_a8w8_blockscale_run_variant(plan["variant"], dA[:M], da[:M], dW, dw)
+        assert np.array_equal(y_bits(y_pk), y_bits(y_row)), f"M={M} N={N} K={K} {plan['name']}"
+        rows = sorted({0, M // 2, M - 1})
+        assert_parity(y_host(y_pk)[rows], oracle.gemm(A[:M], a_s[:M], W, w_s, rows=rows), f"packed M={M} N={N}")
     say(f"packed selector path N={N} K={K}: {len(Ms)} M values bitwise equal")
