@@ -171,6 +171,8 @@ def _tuned_split_rows():
         table = json.load(f)
     out = []
     for sh in table["shapes"]:
+        if sh.get("form"):          # packed / row-wise decode tables: test_gpu_forms.py
+            continue
         rows = [r for r in sh["rows"] if int(r.get("splits", 1)) > 1 or r["kernel"] == "sktile"]
         if rows:
             out.append((sh, rows))
