@@ -685,31 +685,6 @@ __device__ __forceinline__ void rsk_rows(int b, int G, int N, int &r0, int &r1)
     r1 = min(N, RG * (int)((int64_t)(b + 1) * units / G));
 }
 
-// One step of a max-butterfly over lanes: each lane takes the larger of its
-// value and that of lane l ^ MASK.  Within a row of 16 lanes the partner comes
-// through DPP: quad_perm for 1 and 2, then the half-row mirror for 4 and the
-// row mirror for 8 (lane i of 8 reads lane 7 - i, of 16 lane 15 - i), which
-// give the same maxima as l ^ 4 and l ^ 8 once the smaller steps are done, as
-// every lane of a 4- or 8-lane group then holds one value.  16 and 32 cross
-// rows: ds_bpermute.
-template <int MASK>
-__device__ __forceinline__ float amax_step(float m)
-{
-    const int v = __float_as_int(m);
-    int o;
-    if constexpr (MASK == 1)
-        o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
-    else if constexpr (MASK == 2)
-        o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
-    else if constexpr (MASK == 4)
-        o = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
-    else if constexpr (MASK == 8)
-        o = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);   // row_mirror
-    else
-        o = __shfl_xor(v, MASK);
-    return fmaxf(m, __int_as_float(o));
-}
-
 // The amax of each of D 1 x 128 groups over the lanes that hold it: MQ = 16,
 // lanes l, l^16, l^32, l^48 (the MFMA operand layout); otherwise 64 / MQ
 // consecutive lanes, reduced smallest step first (the mirrors need that).

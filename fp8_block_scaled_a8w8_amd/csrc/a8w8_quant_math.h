@@ -57,6 +57,31 @@ __device__ __forceinline__ uint32_t pack4_ieee(const float *x, float s)
     return e4m3fn_pack4(x[0] / s, x[1] / s, x[2] / s, x[3] / s);
 }
 
+// One step of a max-butterfly over lanes: each lane takes the larger of its
+// value and that of lane l ^ MASK.  Within a row of 16 lanes the partner comes
+// through DPP: quad_perm for 1 and 2, then the half-row mirror for 4 and the
+// row mirror for 8 (lane i of 8 reads lane 7 - i, of 16 lane 15 - i), which
+// give the same maxima as l ^ 4 and l ^ 8 once the smaller steps are done, as
+// every lane of a 4- or 8-lane group then holds one value.  16 and 32 cross
+// rows: ds_bpermute.
+template <int MASK>
+__device__ __forceinline__ float amax_step(float m)
+{
+    const int v = __float_as_int(m);
+    int o;
+    if constexpr (MASK == 1)
+        o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    else if constexpr (MASK == 2)
+        o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    else if constexpr (MASK == 4)
+        o = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    else if constexpr (MASK == 8)
+        o = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);   // row_mirror
+    else
+        o = __shfl_xor(v, MASK);
+    return fmaxf(m, __int_as_float(o));
+}
+
 // Largest |x| over this lane's bf16 values (two per word, any subset of a
 // group): finite bf16 magnitudes order as their low 15 bits read as integers,
 // so the maximum is taken on the bits (no conversions kept live).  Non-finite
