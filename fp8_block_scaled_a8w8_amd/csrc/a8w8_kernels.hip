@@ -2370,6 +2370,9 @@ const Entry kEntries[] = {
     // tuned too and won no key.)
     TILE_SK(128, 128, 2, 2, 4, 3), TILE_SK(128, 64, 2, 2, 3, 3), TILE_SK(64, 128, 2, 2, 3, 3),
     TILE_SK(64, 64, 2, 2, 3, 3), TILE_SK(128, 256, 2, 4, 3, 3),
+    // A two-stage 128 x 128 instance split three ways: 66 KB of LDS, two workgroups per
+    // CU (5120 x 6144 at M = 453..512: 3-4% faster; two- and six-way splits won no key).
+    TILE_SK(128, 128, 2, 2, 2, 3),
 };
 constexpr int kNumEntries = sizeof(kEntries) / sizeof(kEntries[0]);
 
